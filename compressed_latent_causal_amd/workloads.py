@@ -1,0 +1,135 @@
+"""Seeded synthetic workloads for causal GQA attention (no attention arithmetic).
+
+This module only draws random inputs and describes shapes; it is shared by the
+tests, the benchmark and the smoke check, which feed the very same bytes to the
+GPU library and to the CPU oracle.
+
+Generator recipe: a CPU ``torch.Generator`` seeded with ``seed`` draws, in this
+order, q, k, v (then decode lengths) as float32 N(0, 1); bf16 workloads round
+those float32 draws to bf16 (nearest even).  With seed 0 and the tiny shape
+this reproduces the tensors of the PyTorch example on the "Grouped Query
+Attention (GQA)" glossary page (section "Cómo funciona GQA"): ``manual_seed(0)``
+then ``randn`` for q (1,8,16,64), k (1,2,16,64) and v (1,2,16,64).
+
+The named workloads follow the head geometries the pages discuss: Llama 3.1 8B
+(32 query heads, 8 KV heads of dim 128; "Por qué GQA reduce la caché KV"), and
+the compressed-latent CCGQA setting of "Compressed Convolutional Attention"
+("Methodologie"): hidden E = 2048 compressed by C = 4 into a 512-wide latent,
+split into 8 query heads of 64 with 2 shared KV heads.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "prefill" or "decode"
+    dtype: str           # "f32" or "bf16"
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    S: int               # prefill: sequence length; decode: cache capacity S_cap
+    theta: float
+    len_lo: int = 0      # decode: per-sequence lengths uniform in [len_lo, len_hi]
+    len_hi: int = 0
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return {"f32": torch.float32, "bf16": torch.bfloat16}[self.dtype]
+
+
+# Latent geometry of the CCGQA workload: E / C = 512 = Hq * D.
+CCA_HIDDEN = 2048
+CCA_COMPRESSION = 4
+
+WORKLOADS = {
+    "tiny_gqa": Workload("tiny_gqa", "prefill", "f32", 1, 8, 2, 64, 16, 1e4),
+    "llama8b_prefill": Workload("llama8b_prefill", "prefill", "bf16", 4, 32, 8, 128, 4096,
+                                5e5),
+    "gqa_decode": Workload("gqa_decode", "decode", "bf16", 32, 32, 8, 128, 8192, 5e5,
+                           1024, 8192),
+    "ccgqa_prefill": Workload("ccgqa_prefill", "prefill", "bf16", 2, 8, 2, 64, 16384, 1e4),
+    "long_decode": Workload("long_decode", "decode", "bf16", 1, 64, 8, 128, 131072, 5e5,
+                            131072, 131072),
+}
+
+
+def _randn(g: torch.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
+    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    return x if dtype == torch.float32 else x.to(dtype)
+
+
+def make_prefill(w: Workload, seed: int = 0):
+    """q [B,Hq,S,D], k, v [B,Hkv,S,D] on the CPU, dtype of the workload."""
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (w.B, w.Hq, w.S, w.D), w.torch_dtype)
+    k = _randn(g, (w.B, w.Hkv, w.S, w.D), w.torch_dtype)
+    v = _randn(g, (w.B, w.Hkv, w.S, w.D), w.torch_dtype)
+    return q, k, v
+
+
+def make_decode(w: Workload, seed: int = 0, poison_tail: bool = False):
+    """q [B,Hq,D], k/v caches [B,Hkv,S_cap,D], seqlens int32 [B] (CPU).
+
+    Lengths are integers drawn uniformly from [len_lo, len_hi] (both ends
+    included).  The cache is filled to capacity with N(0,1); with poison_tail,
+    every slot at or beyond a sequence's length holds NaN instead, so that a
+    kernel reading past the length shows up in the output.
+    """
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (w.B, w.Hq, w.D), w.torch_dtype)
+    k = _randn(g, (w.B, w.Hkv, w.S, w.D), w.torch_dtype)
+    v = _randn(g, (w.B, w.Hkv, w.S, w.D), w.torch_dtype)
+    if w.len_lo == w.len_hi:
+        lens = torch.full((w.B,), w.len_hi, dtype=torch.int32)
+    else:
+        lens = torch.randint(w.len_lo, w.len_hi + 1, (w.B,), generator=g, dtype=torch.int32)
+    if poison_tail:
+        poison_cache_tail(k, lens)
+        poison_cache_tail(v, lens)
+    return q, k, v, lens
+
+
+def poison_cache_tail(cache: torch.Tensor, lens: torch.Tensor) -> None:
+    """Write NaN into cache[b, :, t, :] for every t >= lens[b] (in place)."""
+    for b in range(cache.shape[0]):
+        n = int(lens[b])
+        if n < cache.shape[2]:
+            cache[b, :, n:, :] = float("nan")
+
+
+def custom(kind: str, dtype: str, B: int, Hq: int, Hkv: int, D: int, S: int,
+           theta: float = 1e4, len_lo: int = 0, len_hi: int = 0) -> Workload:
+    """An ad-hoc workload (tests sweep shapes and edge cases with it)."""
+    return Workload(f"custom_{kind}", kind, dtype, B, Hq, Hkv, D, S, theta, len_lo, len_hi)
+
+
+def to_numpy_bits(t: torch.Tensor):
+    """CPU tensor -> numpy array in the oracle's input convention
+    (float32/float64 as is, bf16 as uint16 bit patterns)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view("uint16")
+    return t.numpy()
+
+
+def from_numpy_bits(a, dtype: torch.dtype) -> torch.Tensor:
+    """Inverse of to_numpy_bits for float32 / bf16."""
+    import numpy as np
+    if dtype == torch.bfloat16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dtype)

@@ -1,0 +1,219 @@
+"""Plain fp64 CPU oracle for causal grouped-query attention with RoPE.
+
+TEST INFRASTRUCTURE ONLY.  The tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may use this package; the library under test
+(``compressed_latent_causal_amd``) never imports it, and this package imports
+nothing from the library.  The arithmetic lives in ``oracle.c`` (plain C, double
+precision, computed row by row from the definition); this module only marshals
+numpy arrays into it.
+
+Inputs are numpy arrays: float64, float32, or uint16 holding raw bf16 bit
+patterns (pass ``dtype="bf16"``).  Outputs are float64 arrays.
+
+Pages cited (by title and section):
+  * "Grouped Query Attention (GQA)" glossary, "Cómo funciona GQA": GQA is
+    unchanged scaled dot-product attention per query head, with consecutive
+    query heads sharing one key/value head; the example is causal.
+  * same page, "Por qué GQA reduce la caché KV": the cache stores keys and
+    values of every earlier token and is read in full per generated token; its
+    size grows with the number of key/value heads.
+  * "Compressed Convolutional Attention" summary, "Methodologie" item 4: RoPE is
+    applied to q and k inside the attention space itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_DT_CODE = {"f64": 0, "f32": 1, "bf16": 2}
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (IEEE semantics, no FMA
+    contraction, OpenMP over output rows)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = [
+            "gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+            "-fopenmp", "-shared", "-fPIC", "-Wall", _SRC, "-o", tmp, "-lm",
+        ]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            # ORACLE_LIB points the pins at a deliberately broken build of
+            # oracle.c (the mutation test); normally the library is built here.
+            path = os.environ.get("ORACLE_LIB") or build()
+            lib = ctypes.CDLL(path)
+            P = ctypes.c_void_p
+            i = ctypes.c_int
+            lib.oracle_rope.argtypes = [P, P, i, i, i, i, i, P, ctypes.c_double]
+            lib.oracle_rope.restype = None
+            lib.oracle_prefill.argtypes = [P, P, P, P, i, i, i, i, i, i,
+                                           ctypes.c_double, P, ctypes.c_int64]
+            lib.oracle_prefill.restype = i
+            lib.oracle_decode.argtypes = [P, P, P, P, i, i, i, i, i, i, P,
+                                          ctypes.c_double]
+            lib.oracle_decode.restype = i
+            lib.oracle_round_bf16.argtypes = [P, P, ctypes.c_size_t]
+            lib.oracle_round_bf16.restype = None
+            lib.oracle_round_f32.argtypes = [P, P, ctypes.c_size_t]
+            lib.oracle_round_f32.restype = None
+            _lib = lib
+    return _lib
+
+
+def _as_input(x: np.ndarray, dtype: str) -> np.ndarray:
+    want = {"f64": np.float64, "f32": np.float32, "bf16": np.uint16}[dtype]
+    x = np.ascontiguousarray(x)
+    if x.dtype != want:
+        raise TypeError(f"oracle input for dtype {dtype} must be {want}, got {x.dtype}")
+    return x
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_of(x: np.ndarray) -> str:
+    return {np.dtype(np.float64): "f64", np.dtype(np.float32): "f32",
+            np.dtype(np.uint16): "bf16"}[x.dtype]
+
+
+# ---------------------------------------------------------------------------
+# rounding to storage types
+# ---------------------------------------------------------------------------
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bf16 (nearest, ties to even); returns uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_round_bf16(_ptr(out), _ptr(x), x.size)
+    return out
+
+
+def round_f32(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.float32)
+    _load().oracle_round_f32(_ptr(out), _ptr(x), x.size)
+    return out
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp64 values to the storage type `dtype` ("f32" or "bf16")."""
+    if dtype == "f32":
+        return round_f32(x)
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f64":
+        return np.ascontiguousarray(x, dtype=np.float64)
+    raise ValueError(dtype)
+
+
+def widen(x: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of an f64/f32/bf16-bits array."""
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# RoPE, prefill, decode
+# ---------------------------------------------------------------------------
+def rope(x: np.ndarray, theta: float, pos_offset=None) -> np.ndarray:
+    """Rotary embedding of x [B, H, S, D]; token s of sequence b at position
+    pos_offset[b] + s.  Returns fp64 [B, H, S, D]."""
+    dt = _dtype_of(x)
+    x = _as_input(x, dt)
+    B, H, S, D = x.shape
+    if D % 2:
+        raise ValueError("RoPE needs an even head dim")
+    off = None
+    if pos_offset is not None:
+        off = np.ascontiguousarray(pos_offset, dtype=np.int32)
+        if off.shape != (B,):
+            raise ValueError("pos_offset must have shape [B]")
+    out = np.empty(x.shape, dtype=np.float64)
+    _load().oracle_rope(_ptr(out), _ptr(x), _DT_CODE[dt], B, H, S, D, _ptr(off),
+                        float(theta))
+    return out
+
+
+def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float | None = None,
+            rows: np.ndarray | None = None) -> np.ndarray:
+    """Causal GQA attention.  q [B,Hq,S,D], k/v [B,Hkv,S,D] of one dtype.
+    rows=None: fp64 [B,Hq,S,D]; else rows are flat indices (b*Hq+h)*S+i and the
+    result is fp64 [len(rows), D]."""
+    dt = _dtype_of(q)
+    q, k, v = (_as_input(t, dt) for t in (q, k, v))
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape or Hq % Hkv:
+        raise ValueError("bad shapes")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if rows is None:
+        out = np.empty((B, Hq, S, D), dtype=np.float64)
+        r_ptr, n = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((rows.size, D), dtype=np.float64)
+        r_ptr, n = _ptr(rows), rows.size
+    rc = _load().oracle_prefill(_ptr(out), _ptr(q), _ptr(k), _ptr(v), _DT_CODE[dt], B,
+                                Hq, Hkv, S, D, float(scale), r_ptr, n)
+    if rc:
+        raise RuntimeError(f"oracle_prefill failed ({rc})")
+    return out
+
+
+def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, seqlens,
+           scale: float | None = None) -> np.ndarray:
+    """One new query token per sequence over a contiguous cache.
+    q [B,Hq,D], caches [B,Hkv,S_cap,D], seqlens int [B].  Returns fp64 [B,Hq,D]."""
+    dt = _dtype_of(q)
+    q, k_cache, v_cache = (_as_input(t, dt) for t in (q, k_cache, v_cache))
+    B, Hq, D = q.shape
+    _, Hkv, S_cap, _ = k_cache.shape
+    if k_cache.shape != (B, Hkv, S_cap, D) or v_cache.shape != k_cache.shape or Hq % Hkv:
+        raise ValueError("bad shapes")
+    lens = np.ascontiguousarray(seqlens, dtype=np.int32)
+    if lens.shape != (B,) or (lens < 0).any() or (lens > S_cap).any():
+        raise ValueError("seqlens must be [B] in [0, S_cap]")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    rc = _load().oracle_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _DT_CODE[dt], B, Hq, Hkv, S_cap, D, _ptr(lens),
+                               float(scale))
+    if rc:
+        raise RuntimeError(f"oracle_decode failed ({rc})")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# KV-cache accounting ("Por qué GQA reduce la caché KV" and the worked example)
+# ---------------------------------------------------------------------------
+def kv_values_per_token(n_kv_heads: int, head_dim: int, n_layers: int = 1) -> int:
+    """Cached scalars per token: one key and one value vector per KV head."""
+    return n_layers * 2 * n_kv_heads * head_dim
+
+
+def kv_cache_bytes(n_kv_heads: int, head_dim: int, n_tokens: int, n_layers: int = 1,
+                   bytes_per_value: int = 2) -> int:
+    return kv_values_per_token(n_kv_heads, head_dim, n_layers) * n_tokens * bytes_per_value

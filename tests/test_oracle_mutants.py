@@ -1,0 +1,61 @@
+"""The oracle's pins must be able to fail (CPU only).
+
+Each case plants one plausible mistake into a copy of oracle/oracle.c, builds
+it into a temporary library and runs the pin suite against it through the
+ORACLE_LIB override; the suite has to fail for every mutant.  Nothing here
+touches the GPU or the library under test.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "dropped_scale": ("w[t] = scale * dot;", "w[t] = dot;"),
+    "rope_sign": ("out[row + 2 * i] = x0 * c - x1 * sn;", "out[row + 2 * i] = x0 * c + x1 * sn;"),
+    "rope_freq_sign": ("pow(theta, -2.0 * i / D)", "pow(theta, 2.0 * i / D)"),
+    "rope_half_split": ("double x1 = load(x, row + 2 * i + 1, dt);",
+                        "double x1 = load(x, row + i + D / 2, dt);"),
+    "rope_ignores_offset": ("double p = (double)(off + s);", "double p = (double)(s);"),
+    "prefill_modulo_groups": ("int j = h / G;\n                size_t q_base",
+                              "int j = h % Hkv;\n                size_t q_base"),
+    "causal_off_by_one": ("i + 1, D,", "i, D,"),
+    "value_from_keys": ("o[d] += w[t] * load(v,", "o[d] += w[t] * load(k,"),
+    "decode_modulo_groups": ("int j = h / G;\n                int n",
+                             "int j = h % Hkv;\n                int n"),
+    "decode_length_short": ("int n = seqlens[b];", "int n = seqlens[b] > 0 ? seqlens[b] - 1 : 0;"),
+    "bf16_truncates": ("double r = rint(ldexp(x, -k));", "double r = trunc(ldexp(x, -k));"),
+    "missing_normalisation": ("o[d] /= l;", "o[d] /= 1.0;"),
+}
+
+
+def _run_mutant(name, tmp):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    mpath = os.path.join(tmp, f"{name}.c")
+    open(mpath, "w").write(src.replace(old, new))
+    lib = os.path.join(tmp, f"lib{name}.so")
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
+                    mpath, "-o", lib, "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB=lib, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return r.returncode
+
+
+def test_every_planted_mistake_fails_a_pin():
+    with tempfile.TemporaryDirectory() as tmp:
+        with cf.ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
+            codes = dict(zip(MUTANTS, ex.map(lambda n: _run_mutant(n, tmp), MUTANTS)))
+    survivors = [n for n, rc in codes.items() if rc == 0]
+    assert not survivors, f"mutants not caught by the pins: {survivors}"
+    # rc 1 = tests failed; anything else would mean the run itself broke
+    assert all(rc == 1 for rc in codes.values()), codes

@@ -1,0 +1,426 @@
+"""Pins of the fp64 CPU oracle to facts outside itself (CPU only).
+
+Each test ties one part of the oracle to something it cannot agree with by
+construction: values printed on the pages (tests/golden, with citations), a
+library routine the GQA page itself uses (torch scaled_dot_product_attention,
+here on the CPU in float64), brute force written independently in pure Python,
+closed forms and invariants.  A plausible slip in the oracle -- a dropped
+scale, a wrong sign in the rotation, a modulo instead of a division in the
+head mapping, a transposed operand, an off-by-one causal bound -- fails at
+least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from compressed_latent_causal_amd import workloads as wl
+
+
+def _sdpa_f64(q, k, v, scale=None):
+    """torch CPU float64 SDPA with is_causal and enable_gqa (inputs are numpy)."""
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+                  for x in (q, k, v))
+    return F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, enable_gqa=True,
+                                          scale=scale).numpy()
+
+
+def _rand(shape, seed, dtype=np.float64):
+    return np.random.default_rng(seed).standard_normal(shape).astype(dtype)
+
+
+# ---------------------------------------------------------------------------
+# Worked example of the GQA glossary page
+# ---------------------------------------------------------------------------
+def _worked_example():
+    w = wl.WORKLOADS["tiny_gqa"]
+    q, k, v = wl.make_prefill(w, seed=0)
+    return w, q.numpy(), k.numpy(), v.numpy()
+
+
+def test_worked_example_inputs_are_the_pages_draws(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "gqa_worked_example.json")))
+    torch.manual_seed(g["seed"])
+    q = torch.randn(*g["q_shape"])
+    k = torch.randn(*g["kv_shape"])
+    v = torch.randn(*g["kv_shape"])
+    _, q2, k2, v2 = _worked_example()
+    assert np.array_equal(q.numpy(), q2)
+    assert np.array_equal(k.numpy(), k2)
+    assert np.array_equal(v.numpy(), v2)
+
+
+def test_worked_example_shape_and_mha_equivalence(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "gqa_worked_example.json")))
+    _, q, k, v = _worked_example()
+    out = oracle.prefill(q, k, v)
+    assert list(out.shape) == g["output_shape"]
+    r = g["repeat_interleave_factor"]
+    k_full = np.repeat(k, r, axis=1)   # numpy repeat along an axis == repeat_interleave
+    v_full = np.repeat(v, r, axis=1)
+    ref = oracle.prefill(q, k_full, v_full)
+    close = bool(np.allclose(out, ref, atol=g["equivalence_atol"], rtol=0))
+    assert close == g["equals_repeat_interleaved_mha"]
+    # Same arithmetic in the same order: the equivalence holds bit for bit.
+    assert np.array_equal(out, ref)
+
+
+def test_worked_example_matches_torch_sdpa():
+    _, q, k, v = _worked_example()
+    out = oracle.prefill(q, k, v)
+    ref = _sdpa_f64(q, k, v)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_cached_values_per_token(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "gqa_worked_example.json")))
+    _, q, k, _ = _worked_example()
+    hkv, d = k.shape[1], k.shape[3]
+    hq = q.shape[1]
+    assert oracle.kv_values_per_token(hkv, d) == g["cached_values_per_token_per_layer_gqa"]
+    assert oracle.kv_values_per_token(hq, d) == g["cached_values_per_token_per_layer_mha"]
+    # the page counts k[0, :, 0].numel() * 2
+    assert k[0, :, 0].size * 2 == g["cached_values_per_token_per_layer_gqa"]
+
+
+def test_llama_kv_cache_bytes(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "kv_cache_llama31_8b.json")))
+    L, hkv, d, bpv = g["layers"], g["kv_heads"], g["head_dim"], g["bytes_per_value"]
+    assert oracle.kv_cache_bytes(hkv, d, 1, L, bpv) == g["bytes_per_token_gqa"]
+    assert oracle.kv_cache_bytes(hkv, d, g["context_tokens"], L, bpv) == \
+        g["cache_bytes_gqa_full_context"]
+    assert oracle.kv_cache_bytes(g["mha_kv_heads"], d, 1, L, bpv) == g["bytes_per_token_mha"]
+    assert oracle.kv_cache_bytes(g["mha_kv_heads"], d, g["context_tokens"], L, bpv) == \
+        g["cache_bytes_mha_full_context"]
+    assert g["mha_kv_heads"] // hkv == g["tokens_held_ratio_gqa_over_mha"]
+
+
+# ---------------------------------------------------------------------------
+# The whole attention definition against torch SDPA (float64, CPU)
+# ---------------------------------------------------------------------------
+GEOMS = [  # B, Hq, Hkv, S, D
+    (2, 8, 2, 33, 64),     # GQA, G = 4 (the worked example's geometry)
+    (1, 4, 1, 17, 128),    # MQA
+    (1, 4, 4, 9, 64),      # MHA
+    (2, 8, 8, 40, 16),
+    (1, 64, 8, 5, 128),    # G = 8
+    (1, 6, 2, 23, 32),     # G = 3
+    (3, 2, 1, 1, 8),       # S = 1
+]
+
+
+@pytest.mark.parametrize("geom", GEOMS)
+def test_prefill_matches_torch_sdpa(geom):
+    B, Hq, Hkv, S, D = geom
+    q = _rand((B, Hq, S, D), 1)
+    k = _rand((B, Hkv, S, D), 2)
+    v = _rand((B, Hkv, S, D), 3)
+    out = oracle.prefill(q, k, v)
+    ref = _sdpa_f64(q, k, v)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("scale", [0.3, 2.0])
+def test_prefill_scale_is_applied(scale):
+    q, k, v = _rand((1, 4, 12, 16), 4), _rand((1, 2, 12, 16), 5), _rand((1, 2, 12, 16), 6)
+    out = oracle.prefill(q, k, v, scale=scale)
+    ref = _sdpa_f64(q, k, v, scale=scale)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_prefill_row_subset_equals_full():
+    B, Hq, Hkv, S, D = 2, 8, 2, 21, 32
+    q, k, v = _rand((B, Hq, S, D), 7), _rand((B, Hkv, S, D), 8), _rand((B, Hkv, S, D), 9)
+    full = oracle.prefill(q, k, v)
+    rows = np.array([0, 5, S - 1, S, 3 * S + 7, B * Hq * S - 1], dtype=np.int64)
+    part = oracle.prefill(q, k, v, rows=rows)
+    assert np.array_equal(part, full.reshape(-1, D)[rows])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_low_precision_inputs_are_widened_exactly(dtype):
+    B, Hq, Hkv, S, D = 1, 4, 2, 19, 64
+    q, k, v = _rand((B, Hq, S, D), 10), _rand((B, Hkv, S, D), 11), _rand((B, Hkv, S, D), 12)
+    if dtype == "f32":
+        lq, lk, lv = (x.astype(np.float32) for x in (q, k, v))
+    else:
+        lq, lk, lv = (oracle.round_bf16(x) for x in (q, k, v))
+    out = oracle.prefill(lq, lk, lv)
+    tw = lambda x: torch.from_numpy(x.astype(np.float32)) if x.dtype == np.float32 else \
+        torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    ref = _sdpa_f64(*(tw(x).double().numpy() for x in (lq, lk, lv)))
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Independent brute force in pure Python (no numpy, no torch)
+# ---------------------------------------------------------------------------
+def _brute(q, k, v, G, scale):
+    B, Hq, S, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    out = [[[[0.0] * D for _ in range(S)] for _ in range(Hq)] for _ in range(B)]
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // G
+            for i in range(S):
+                sc = [scale * sum(q[b][h][i][d] * k[b][kv][t][d] for d in range(D))
+                      for t in range(i + 1)]
+                mx = max(sc)
+                ws = [math.exp(s - mx) for s in sc]
+                tot = sum(ws)
+                for d in range(D):
+                    out[b][h][i][d] = sum(ws[t] * v[b][kv][t][d] for t in range(i + 1)) / tot
+    return out
+
+
+@pytest.mark.parametrize("geom", [(1, 4, 2, 6, 4), (2, 3, 1, 5, 2), (1, 2, 2, 7, 6)])
+def test_prefill_matches_brute_force(geom):
+    B, Hq, Hkv, S, D = geom
+    q, k, v = _rand((B, Hq, S, D), 13), _rand((B, Hkv, S, D), 14), _rand((B, Hkv, S, D), 15)
+    scale = 1 / math.sqrt(D)
+    ref = np.array(_brute(q.tolist(), k.tolist(), v.tolist(), Hq // Hkv, scale))
+    out = oracle.prefill(q, k, v)
+    assert np.max(np.abs(out - ref)) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and invariants
+# ---------------------------------------------------------------------------
+def test_first_row_is_first_value_row():
+    B, Hq, Hkv, S, D = 2, 8, 2, 10, 16
+    q, k, v = _rand((B, Hq, S, D), 16), _rand((B, Hkv, S, D), 17), _rand((B, Hkv, S, D), 18)
+    out = oracle.prefill(q, k, v)
+    for h in range(Hq):
+        assert np.array_equal(out[:, h, 0, :], v[:, h // (Hq // Hkv), 0, :])
+
+
+def test_zero_scale_gives_running_mean_of_values():
+    B, Hq, Hkv, S, D = 1, 4, 2, 13, 8
+    q, k, v = _rand((B, Hq, S, D), 19), _rand((B, Hkv, S, D), 20), _rand((B, Hkv, S, D), 21)
+    out = oracle.prefill(q, k, v, scale=0.0)
+    mean = np.cumsum(v, axis=2) / np.arange(1, S + 1)[None, None, :, None]
+    assert np.max(np.abs(out - np.repeat(mean, Hq // Hkv, axis=1))) < 1e-14
+
+
+def test_causality_future_keys_do_not_matter():
+    B, Hq, Hkv, S, D = 1, 4, 2, 16, 8
+    q, k, v = _rand((B, Hq, S, D), 22), _rand((B, Hkv, S, D), 23), _rand((B, Hkv, S, D), 24)
+    base = oracle.prefill(q, k, v)
+    for i in (0, 5, 14):
+        k2, v2 = k.copy(), v.copy()
+        k2[:, :, i + 1:] = _rand(k2[:, :, i + 1:].shape, 25 + i)
+        v2[:, :, i + 1:] = 1e3
+        out = oracle.prefill(q, k2, v2)
+        assert np.array_equal(out[:, :, :i + 1], base[:, :, :i + 1])
+        assert not np.array_equal(out[:, :, i + 1:], base[:, :, i + 1:])
+
+
+def test_group_mapping_is_contiguous_not_modulo():
+    """Query head h reads KV head h // G; the modulo mapping (tile instead of
+    repeat_interleave) gives different results, so the pin above can see it."""
+    B, Hq, Hkv, S, D = 1, 8, 2, 9, 16
+    q, k, v = _rand((B, Hq, S, D), 26), _rand((B, Hkv, S, D), 27), _rand((B, Hkv, S, D), 28)
+    out = oracle.prefill(q, k, v)
+    tiled = oracle.prefill(q, np.tile(k, (1, Hq // Hkv, 1, 1)), np.tile(v, (1, Hq // Hkv, 1, 1)))
+    inter = oracle.prefill(q, np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1))
+    assert np.array_equal(out, inter)
+    assert not np.allclose(out, tiled)
+
+
+def test_mqa_and_mha_limits():
+    B, Hq, S, D = 1, 4, 11, 16
+    q = _rand((B, Hq, S, D), 29)
+    # MQA: one KV head shared by all query heads
+    k1, v1 = _rand((B, 1, S, D), 30), _rand((B, 1, S, D), 31)
+    mqa = oracle.prefill(q, k1, v1)
+    for h in range(Hq):
+        single = oracle.prefill(q[:, h:h + 1], k1, v1)
+        assert np.array_equal(mqa[:, h:h + 1], single)
+    # MHA: every head its own KV head, heads independent
+    k4, v4 = _rand((B, Hq, S, D), 32), _rand((B, Hq, S, D), 33)
+    mha = oracle.prefill(q, k4, v4)
+    for h in range(Hq):
+        single = oracle.prefill(q[:, h:h + 1], k4[:, h:h + 1], v4[:, h:h + 1])
+        assert np.array_equal(mha[:, h:h + 1], single)
+
+
+# ---------------------------------------------------------------------------
+# Decode
+# ---------------------------------------------------------------------------
+def test_decode_equals_last_prefill_row():
+    B, Hq, Hkv, S, D = 2, 8, 2, 24, 32
+    q, k, v = _rand((B, Hq, S, D), 34), _rand((B, Hkv, S, D), 35), _rand((B, Hkv, S, D), 36)
+    pre = oracle.prefill(q, k, v)
+    # cache with spare capacity whose tail is NaN
+    cap = S + 9
+    kc = np.full((B, Hkv, cap, D), np.nan)
+    vc = np.full((B, Hkv, cap, D), np.nan)
+    kc[:, :, :S], vc[:, :, :S] = k, v
+    for n in (1, 7, S):
+        dec = oracle.decode(np.ascontiguousarray(q[:, :, n - 1]), kc, vc, [n] * B)
+        assert np.array_equal(dec, pre[:, :, n - 1])
+
+
+def test_decode_ragged_lengths_match_sdpa_and_empty_is_zero():
+    B, Hq, Hkv, cap, D = 4, 8, 2, 30, 16
+    q = _rand((B, Hq, D), 37)
+    kc, vc = _rand((B, Hkv, cap, D), 38), _rand((B, Hkv, cap, D), 39)
+    lens = [0, 1, 17, 30]
+    out = oracle.decode(q, kc, vc, lens)
+    assert np.array_equal(out[0], np.zeros((Hq, D)))
+    for b in range(1, B):
+        n = lens[b]
+        # a single query attending to all n keys == last row of causal SDPA whose
+        # earlier queries are arbitrary
+        qq = np.zeros((1, Hq, n, D))
+        qq[0, :, n - 1] = q[b]
+        ref = _sdpa_f64(qq, kc[b:b + 1, :, :n], vc[b:b + 1, :, :n])[0, :, n - 1]
+        assert np.max(np.abs(out[b] - ref)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+def test_rope_position_zero_is_identity():
+    x = _rand((2, 3, 1, 64), 40)
+    assert np.array_equal(oracle.rope(x, 1e4), x)
+
+
+def test_rope_preserves_pair_norms():
+    x = _rand((1, 2, 50, 128), 41)
+    y = oracle.rope(x, 5e5, pos_offset=[1000])
+    nx = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    ny = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    assert np.max(np.abs(nx - ny) / nx) < 1e-12
+
+
+def _probe(D, pair, S, theta, offset=0):
+    x = np.zeros((1, 1, S, D))
+    x[..., 2 * pair] = 1.0
+    return oracle.rope(x, theta, pos_offset=[offset])[0, 0]
+
+
+def test_rope_pairs_are_adjacent_channels():
+    D = 16
+    for pair in range(D // 2):
+        y = _probe(D, pair, 5, 1e4, offset=3)
+        others = np.delete(y, [2 * pair, 2 * pair + 1], axis=1)
+        assert np.array_equal(others, np.zeros_like(others))
+
+
+def test_rope_pair_zero_rotates_by_the_position():
+    # the first pair has frequency theta^0 = 1 for every theta
+    for theta in (1e4, 5e5):
+        y = _probe(64, 0, 7, theta, offset=11)
+        p = np.arange(11, 18)
+        assert np.max(np.abs(y[:, 0] - np.cos(p))) < 1e-15
+        assert np.max(np.abs(y[:, 1] - np.sin(p))) < 1e-15
+
+
+def test_rope_middle_pair_frequency_is_inverse_sqrt_theta():
+    # pair D/4 has exponent -1/2: with theta = 1e4 its frequency is 1/100, so
+    # positions 100 and 200 are rotated by exactly one and two radians
+    D = 64
+    c = 2 * (D // 4)
+    y = _probe(D, D // 4, 201, 1e4)
+    assert abs(y[100, c] - math.cos(1.0)) < 1e-14 and abs(y[100, c + 1] - math.sin(1.0)) < 1e-14
+    assert abs(y[200, c] - math.cos(2.0)) < 1e-14 and abs(y[200, c + 1] - math.sin(2.0)) < 1e-14
+
+
+def test_rope_frequencies_decrease_geometrically():
+    D, theta = 32, 1e4
+    ang = []
+    for pair in range(D // 2):
+        y = _probe(D, pair, 2, theta)
+        ang.append(math.atan2(y[1, 2 * pair + 1], y[1, 2 * pair]))   # angle at position 1
+    ratios = np.array(ang[1:]) / np.array(ang[:-1])
+    assert np.all(ratios < 1)
+    assert np.max(np.abs(ratios - ratios[0])) < 1e-12
+    # over D/2 pairs the frequency falls by the factor theta
+    assert abs(ratios[0] ** (D // 2) - 1 / theta) < 1e-15
+
+
+def test_rope_theta_one_rotates_every_pair_by_the_position():
+    y = oracle.rope(np.tile(np.array([1.0, 0.0]), 4).reshape(1, 1, 1, 8), 1.0, [5])
+    assert np.max(np.abs(y[0, 0, 0, 0::2] - math.cos(5))) < 1e-15
+    assert np.max(np.abs(y[0, 0, 0, 1::2] - math.sin(5))) < 1e-15
+
+
+def test_rope_rotations_compose():
+    x = _rand((1, 2, 1, 32), 42)
+    a, b = 37, 4100
+    twice = oracle.rope(oracle.rope(x, 5e5, [a]), 5e5, [b])
+    once = oracle.rope(x, 5e5, [a + b])
+    assert np.max(np.abs(twice - once)) < 1e-11
+
+
+def test_rope_batch_offsets_apply_per_sequence():
+    x = _rand((3, 2, 5, 16), 43)
+    offs = [0, 9, 131066]
+    y = oracle.rope(x, 1e4, offs)
+    for b in range(3):
+        assert np.array_equal(y[b:b + 1], oracle.rope(x[b:b + 1], 1e4, [offs[b]]))
+
+
+def test_rope_makes_scores_depend_on_relative_position_only():
+    B, Hq, Hkv, S, D = 1, 4, 2, 20, 32
+    q, k, v = _rand((B, Hq, S, D), 44), _rand((B, Hkv, S, D), 45), _rand((B, Hkv, S, D), 46)
+    base = oracle.prefill(oracle.rope(q, 1e4), oracle.rope(k, 1e4), v)
+    shifted = oracle.prefill(oracle.rope(q, 1e4, [5000]), oracle.rope(k, 1e4, [5000]), v)
+    assert np.max(np.abs(base - shifted)) < 1e-10
+    # and RoPE is not a no-op on the output
+    plain = oracle.prefill(q, k, v)
+    assert np.max(np.abs(base - plain)) > 1e-3
+
+
+def test_rope_accepts_low_precision_inputs():
+    x = _rand((1, 2, 9, 64), 47)
+    xb = oracle.round_bf16(x)
+    assert np.array_equal(oracle.rope(xb, 1e4, [3]), oracle.rope(oracle.widen(xb), 1e4, [3]))
+    xf = x.astype(np.float32)
+    assert np.array_equal(oracle.rope(xf, 1e4, [3]), oracle.rope(xf.astype(np.float64), 1e4, [3]))
+
+
+# ---------------------------------------------------------------------------
+# Rounding to bf16 / fp32
+# ---------------------------------------------------------------------------
+def test_round_bf16_matches_torch_on_float32_values():
+    rng = np.random.default_rng(48)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),     # subnormals
+        (rng.standard_normal(2000) * 1e38).astype(np.float32),      # near overflow
+        rng.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32).view(np.float32),
+    ])
+    x = x[np.isfinite(x)]
+    ours = oracle.round_bf16(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_round_bf16_ties_go_to_even():
+    cases = {
+        1.0 + 2.0 ** -8: 0x3F80,            # halfway between 1 and 1+2^-7 -> 1 (even)
+        1.0 + 3 * 2.0 ** -8: 0x3F82,        # halfway between 1+2^-7 and 1+2^-6 -> even
+        1.0 + 2.0 ** -8 + 2.0 ** -40: 0x3F81,   # just above halfway -> up
+        -(1.0 + 2.0 ** -8): 0xBF80,
+        3.0 * 2.0 ** 127 * 2: 0x7F80,       # overflow -> +inf
+        -0.0: 0x8000,
+        2.0 ** -133: 0x0001,                # smallest subnormal
+        2.0 ** -134: 0x0000,                # halfway to zero -> even (zero)
+        3 * 2.0 ** -134: 0x0002,            # halfway between 1 and 2 ulps -> even
+    }
+    got = oracle.round_bf16(np.array(list(cases.keys())))
+    assert [int(x) for x in got] == list(cases.values())
+    assert oracle.round_bf16(np.array([np.nan]))[0] & 0x7FFF > 0x7F80
+
+
+def test_round_bf16_does_not_round_twice():
+    # a double just above a bf16 midpoint that float32 rounding would pull onto
+    # the midpoint; direct rounding must still go up
+    x = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert oracle.round_bf16(np.array([x]))[0] == 0x3F81
