@@ -1,1 +1,137 @@
-"""MI355X-native causal grouped-query attention with RoPE (placeholder)."""
+"""MI355X-native causal grouped-query attention with RoPE.
+
+Thin Python binding over the C ABI of ``libattn.so`` (``include/attn.h``):
+argument marshalling only.  Every step runs in the library's gfx950 kernels;
+PyTorch supplies device memory and the current stream.  There is no CPU
+fallback: calling into the library without the built ``libattn.so`` raises.
+
+    rope(x, theta, pos_offset=None, pos_shift=0, out=None)
+    prefill(q, k, v, scale=None, out=None)
+    decode(q, k_cache, v_cache, seqlens, max_len=None, scale=None, out=None, workspace=None)
+    decode_workspace_size(B, Hq, Hkv, max_len, D)
+
+Shapes follow the C ABI: x [B,H,S,D]; q/o [B,Hq,S,D], k/v [B,Hkv,S,D];
+decode q/o [B,Hq,D], caches [B,Hkv,S_cap,D], seqlens int32 [B] on the device.
+"""
+from __future__ import annotations
+
+import math
+
+from ._lib import (  # noqa: F401
+    AttnError, lib, lib_path, DTYPE_CODES, STATUS,
+)
+
+__all__ = ["rope", "prefill", "decode", "decode_workspace_size", "AttnError", "lib_path"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    try:
+        return DTYPE_CODES[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}; use float32 or bfloat16") from None
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _call(fn, *args):
+    rc = fn(*args)
+    if rc != 0:
+        raise AttnError(rc)
+
+
+def rope(x, theta: float, pos_offset=None, pos_shift: int = 0, out=None):
+    """Rotary embedding of x [B,H,S,D]: token s of sequence b is at position
+    pos_offset[b] + pos_shift + s.  out may be x itself (in place)."""
+    torch = _torch()
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, S, D]")
+    B, H, S, D = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x")
+    _check_dev(x, out)
+    po = 0
+    if pos_offset is not None:
+        if pos_offset.dtype != torch.int32 or pos_offset.shape != (B,):
+            raise ValueError("pos_offset must be int32 [B]")
+        _check_dev(pos_offset)
+        po = pos_offset.data_ptr()
+    _call(lib().attn_rope, out.data_ptr(), x.data_ptr(), _dtype_code(x), B, H, S, D, po,
+          int(pos_shift), float(theta), _stream(x))
+    return out
+
+
+def prefill(q, k, v, scale: float | None = None, out=None):
+    """Causal GQA attention: q [B,Hq,S,D], k/v [B,Hkv,S,D] -> [B,Hq,S,D]."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,Hq,S,D] and k, v [B,Hkv,S,D]")
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
+        raise ValueError("k/v must be [B,Hkv,S,D] with q's B, S and D")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev(q, k, v, out)
+    _call(lib().attn_prefill, out.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+          _dtype_code(q), B, Hq, Hkv, S, D, float(scale), _stream(q))
+    return out
+
+
+def decode_workspace_size(B: int, Hq: int, Hkv: int, max_len: int, D: int) -> int:
+    return int(lib().attn_decode_workspace_size(B, Hq, Hkv, max_len, D))
+
+
+def decode(q, k_cache, v_cache, seqlens, max_len: int | None = None, scale: float | None = None,
+           out=None, workspace=None):
+    """One query token per sequence over a contiguous cache.
+
+    q [B,Hq,D]; caches [B,Hkv,S_cap,D]; seqlens device int32 [B] with
+    0 <= seqlens[b] <= max_len <= S_cap (max_len defaults to S_cap, which needs
+    no host synchronisation).  Returns [B,Hq,D]."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,Hq,D] and caches [B,Hkv,S_cap,D]")
+    B, Hq, D = q.shape
+    _, Hkv, S_cap, _ = k_cache.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("caches must be [B,Hkv,S_cap,D] with q's B and D")
+    if seqlens.dtype != torch.int32 or seqlens.shape != (B,):
+        raise ValueError("seqlens must be int32 [B]")
+    if max_len is None:
+        max_len = S_cap
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_size(B, Hq, Hkv, max_len, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_dev(q, k_cache, v_cache, seqlens, out, workspace)
+    _call(lib().attn_decode, out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+          v_cache.data_ptr(), _dtype_code(q), B, Hq, Hkv, S_cap, D, seqlens.data_ptr(),
+          int(max_len), float(scale), workspace.data_ptr(),
+          workspace.numel() * workspace.element_size(), _stream(q))
+    return out

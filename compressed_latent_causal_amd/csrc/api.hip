@@ -1,0 +1,88 @@
+// C ABI of the attention library (declared in include/attn.h): argument
+// validation on the host, then dispatch to the gfx950 kernels.  No HIP call is
+// made before validation passes; the library allocates nothing.
+#include <math.h>
+
+#include "../../include/attn.h"
+#include "kernels.hpp"
+
+#define ATTN_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool supported_dim(int D) { return D == 64 || D == 128; }
+bool known_dtype(int dt) { return dt == ATTN_F32 || dt == ATTN_BF16; }
+bool good_scale(float s) { return isfinite(s) && s > 0.f; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+ATTN_API int attn_rope(void* out, const void* in, int dtype, int B, int H, int S, int D,
+                       const int32_t* pos_offset, int pos_shift, double theta, void* stream) {
+    if (B < 0 || S < 0 || H < 1) return ATTN_ERR_SHAPE;
+    if (!known_dtype(dtype) || !supported_dim(D) || !(theta > 0.0) || !isfinite(theta))
+        return ATTN_ERR_UNSUPPORTED;
+    if (B > kMaxGridYZ) return ATTN_ERR_SHAPE;
+    if (B == 0 || S == 0) return ATTN_OK;
+    if (!out || !in) return ATTN_ERR_NULL;
+    if (!aligned16(out) || !aligned16(in) || ((uintptr_t)pos_offset & 3u)) return ATTN_ERR_ALIGN;
+    return hip_status(attn::launch_rope(out, in, dtype, B, H, S, D, pos_offset, pos_shift, theta,
+                                        (hipStream_t)stream));
+}
+
+ATTN_API int attn_prefill(void* o, const void* q, const void* k, const void* v, int dtype, int B,
+                          int Hq, int Hkv, int S, int D, float scale, void* stream) {
+    if (B < 0 || S < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+    if (!known_dtype(dtype) || !supported_dim(D) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
+    if (B == 0 || S == 0) return ATTN_OK;
+    // one workgroup per (query block, batch, KV head, head slice): stay in a 32-bit grid
+    if ((long long)B * Hq * ((S + 31) / 32) >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    if (!o || !q || !k || !v) return ATTN_ERR_NULL;
+    if (!aligned16(o) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return ATTN_ERR_ALIGN;
+    return hip_status(
+        attn::launch_prefill(o, q, k, v, dtype, B, Hq, Hkv, S, D, scale, (hipStream_t)stream));
+}
+
+ATTN_API size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_len < 0 || !supported_dim(D)) return 0;
+    if (B == 0) return 0;
+    return attn::decode_workspace_bytes(B, Hq, Hkv, max_len, D);
+}
+
+ATTN_API int attn_decode(void* o, const void* q, const void* k_cache, const void* v_cache, int dtype,
+                         int B, int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens,
+                         int max_len, float scale, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_cap < 1 || max_len < 0 || max_len > S_cap)
+        return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_BF16 || !supported_dim(D) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
+    if (B > kMaxGridYZ || (long long)Hkv * ((Hq / Hkv + 15) / 16) > kMaxGridYZ) return ATTN_ERR_SHAPE;
+    if (B == 0) return ATTN_OK;
+    if (!o || !q || !k_cache || !v_cache || !seqlens) return ATTN_ERR_NULL;
+    if (!aligned16(o) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        ((uintptr_t)seqlens & 3u))
+        return ATTN_ERR_ALIGN;
+    const size_t need = attn::decode_workspace_bytes(B, Hq, Hkv, max_len, D);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+    return hip_status(attn::launch_decode(o, q, k_cache, v_cache, B, Hq, Hkv, S_cap, D, seqlens,
+                                          max_len, scale, workspace, (hipStream_t)stream));
+}
+
+ATTN_API const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "invalid sizes (negative, Hq % Hkv != 0, max_len > S_cap, or too large)";
+        case ATTN_ERR_UNSUPPORTED:
+            return "unsupported argument (head dim not 64/128, dtype, theta or scale not positive, f32 decode)";
+        case ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case ATTN_ERR_HIP: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}

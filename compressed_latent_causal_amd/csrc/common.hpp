@@ -1,0 +1,92 @@
+// Device-side building blocks shared by the gfx950 attention kernels:
+// vector types, bf16 conversions, the 16x16x32 bf16 matrix-core product,
+// LDS transpose reads and the XOR swizzle used for K/V tiles in LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// ---------------------------------------------------------------- types
+typedef short bf16x8_t __attribute__((__vector_size__(8 * sizeof(short))));  // 8 bf16 bit patterns
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- bf16
+// bf16 -> fp32 is exact: the 16 bits are the top half of a binary32.
+__device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ inline unsigned pack_bf16x2(float lo, float hi) {
+    f32x2_t f = {lo, hi};
+    bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+    return __builtin_bit_cast(unsigned, b);
+}
+
+// ---------------------------------------------------------------- matrix core
+// D = A * B + C for a 16x16 fp32 tile with K = 32 bf16.
+// Lane l supplies A[m = l%16][k = 8*(l/16) .. +7] and B[k = 8*(l/16) .. +7][n = l%16]
+// and receives D[m = 4*(l/16) + i][n = l%16] in element i.  Any fixed
+// permutation of k applied to both A and B leaves the product unchanged.
+__device__ inline f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- LDS
+// Transpose read of 4 bf16 (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8-byte chunks addressed by
+// lanes 4*j + i/4 for j = 0..3.  If lane L of the group addresses
+// row (r0 + L/4), columns (c0 + 4*(L%4)) .. +3 of a row-major tile, lane i
+// receives column c0 + i of rows r0 .. r0+3.
+__device__ inline bf16x4_t lds_read_tr(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
+}
+
+// Byte offset of 16-byte chunk c of row r in a row-major LDS tile whose rows
+// hold D bf16.  Chunks are XOR-swizzled with row bits so that 16 consecutive
+// lanes reading one logical chunk of 16 consecutive rows (the matrix-core
+// operand pattern) touch 16 distinct 16-byte bank groups.
+template <int D>
+__device__ inline int swz(int r, int c) {
+    static_assert(D == 64 || D == 128, "head dim");
+    if constexpr (D == 128)
+        return r * 256 + ((c ^ (r & 15)) << 4);
+    else
+        return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+// Operand fragment for the transposed product O^T = V^T P^T: A[m = d][k = key],
+// lane l gets V[key][d] for d = d0 + l%16 and the 8 keys
+//   r0 + 4*(l/16) + {0,1,2,3}  and  r0 + 16 + 4*(l/16) + {0,1,2,3}
+// from a swizzled row-major V tile.  (The keys match the rows that element i of
+// the S^T = K Q^T tiles m and m+1 hold in lane group l/16.)
+template <int D>
+__device__ inline bf16x8_t v_frag(const char* vt, int r0, int d0, int lane) {
+    const int g = lane >> 4, L = lane & 15;
+    const int col = d0 + 4 * (L & 3);           // first of the 4 columns this lane addresses
+    const int c16 = col >> 3, half = (col & 7) * 2;  // 16-byte chunk and byte offset inside it
+    const int ra = r0 + 4 * g + (L >> 2);
+    bf16x4_t lo = lds_read_tr(vt + swz<D>(ra, c16) + half);
+    bf16x4_t hi = lds_read_tr(vt + swz<D>(ra + 16, c16) + half);
+    bf16x8_t a;
+    u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+    u32x4_t w = {l2.x, l2.y, h2.x, h2.y};
+    a = __builtin_bit_cast(bf16x8_t, w);
+    return a;
+}
+
+// ---------------------------------------------------------------- cross-lane
+__device__ inline float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
+
+}  // namespace attn

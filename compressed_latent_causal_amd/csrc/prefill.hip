@@ -1,0 +1,353 @@
+// Causal grouped-query attention prefill for gfx950.
+//
+// What is computed ("Grouped Query Attention (GQA)" glossary, section "Cómo
+// funciona GQA"): per query head h, unchanged causal scaled dot-product
+// attention against key/value head h / G, G = Hq / Hkv.  The "Compressed
+// Convolutional Attention" summary ("Methodologie", CCGQA paragraph) runs the
+// same operation in a compressed latent with small head dims (64 here).
+//
+// bf16 kernel design (flash-style, exact up to rounding):
+//  * One workgroup = 8 waves = HPW query heads of one KV group x a block of
+//    queries.  Each wave owns one head and 32 consecutive queries.  The K and V
+//    tile (64 keys x D) is loaded once into LDS and serves every head of the
+//    workgroup, so a KV group's key/value bytes are fetched once per query block
+//    rather than once per query head.
+//  * Scores are formed transposed, S^T = K Q^T, with the 16x16x32 bf16 matrix
+//    core: each lane ends up holding one query and 4 keys per 16x16 tile, so the
+//    softmax row statistics are per-lane scalars (plus a 4-lane reduction).
+//  * Online softmax in fp32 in the exp2 domain (scale * log2 e folded into one
+//    FMA per score); P is rounded to bf16 and fed straight from registers as the
+//    B operand of O^T = V^T P^T.  The A operand (V^T) comes from the row-major
+//    V tile through the LDS transpose read, so V is never transposed in memory.
+//  * K/V tiles are double-buffered through registers: the next tile's global
+//    loads are in flight while the current one is computed.  LDS rows are
+//    XOR-swizzled in 16-byte chunks to keep the operand reads conflict-free.
+//  * Work order: heaviest (last) query blocks are dispatched first, and
+//    consecutive workgroup ids walk (batch, KV head) fastest so a KV group's
+//    blocks share an XCD (and its L2) when B*Hkv is a multiple of 8.
+//  * Only tiles at or left of the diagonal are visited; only diagonal tiles
+//    pay the elementwise mask.
+//
+// fp32 kernel: plain fp32 VALU arithmetic (accuracy target 1e-5), the same
+// work split idea with K/V tiles of 32 keys in LDS shared by up to 4 heads.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+
+namespace {
+
+constexpr int PF_BN = 64;                 // keys per K/V tile
+constexpr int PF_QW = 32;                 // queries per wave
+constexpr int PF_NW = 8;                  // waves per workgroup
+constexpr int PF_THREADS = PF_NW * 64;
+
+template <int D, int HPW>
+__global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, int B, int Hq, int Hkv, int S, float c, int n_qblk, int n_hchunk) {
+    constexpr int CH = D / 8;                   // 16-byte chunks per row
+    constexpr int KSTEPS = D / 32;              // k-steps of S^T = K Q^T
+    constexpr int DT = D / 16;                  // d tiles of O^T
+    constexpr int QPB = (PF_NW / HPW) * PF_QW;  // queries per head per workgroup
+    constexpr int TILE_BYTES = PF_BN * D * 2;
+    constexpr int CPT = PF_BN * CH / PF_THREADS;  // 16-byte chunks per thread per tile
+    static_assert(CPT >= 1 && (PF_BN * CH) % PF_THREADS == 0, "tile split");
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * TILE_BYTES];
+    char* const ks = smem;
+    char* const vs = smem + TILE_BYTES;
+
+    const int G = Hq / Hkv;
+    const int per = B * Hkv * n_hchunk;
+    const int qb = n_qblk - 1 - (int)blockIdx.x / per;  // heaviest query blocks first
+    const int rem = (int)blockIdx.x % per;
+    const int bkv = rem % (B * Hkv), hc = rem / (B * Hkv);
+    const int b = bkv / Hkv, kvh = bkv % Hkv;
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;  // row-in-tile / lane group
+    const int h = kvh * G + hc * HPW + (w % HPW);
+    const int q0 = qb * QPB;
+    const int qw0 = q0 + (w / HPW) * PF_QW;
+
+    const uint16_t* const kg = k + (size_t)(b * Hkv + kvh) * S * D;
+    const uint16_t* const vg = v + (size_t)(b * Hkv + kvh) * S * D;
+    const size_t qo_base = (size_t)(b * Hq + h) * S * D;
+
+    // Q^T fragments (B operand): query qw0 + 16n + lr, dims 32s + 8lg .. +7.
+    bf16x8_t qf[2][KSTEPS];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int row = qw0 + 16 * n + lr;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            u32x4_t x = {0, 0, 0, 0};
+            if (row < S) x = *(const u32x4_t*)(q + qo_base + (size_t)row * D + 32 * s + 8 * lg);
+            qf[n][s] = __builtin_bit_cast(bf16x8_t, x);
+        }
+    }
+
+    u32x4_t kr[CPT], vr[CPT];
+    auto load_tile = [&](int kv0) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ci = tid + u * PF_THREADS, r = ci / CH, cc = ci % CH;
+            const int key = kv0 + r;
+            if (key < S) {
+                kr[u] = *(const u32x4_t*)(kg + (size_t)key * D + cc * 8);
+                vr[u] = *(const u32x4_t*)(vg + (size_t)key * D + cc * 8);
+            } else {
+                kr[u] = u32x4_t{0, 0, 0, 0};
+                vr[u] = u32x4_t{0, 0, 0, 0};
+            }
+        }
+    };
+
+    const int kv_end = min(q0 + QPB, S);
+    const int ntiles = ceil_div(kv_end, PF_BN);
+    const bool active = qw0 < S;
+
+    f32x4_t oacc[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt][0] = oacc[dt][1] = f32x4_t{0, 0, 0, 0};
+    float m_run[2] = {-INFINITY, -INFINITY};
+    float l_run[2] = {0.f, 0.f};
+
+    load_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+        const int kv0 = t * PF_BN;
+        __syncthreads();  // everyone is done reading the previous tile
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ci = tid + u * PF_THREADS, r = ci / CH, cc = ci % CH;
+            *(u32x4_t*)(ks + swz<D>(r, cc)) = kr[u];
+            *(u32x4_t*)(vs + swz<D>(r, cc)) = vr[u];
+        }
+        __syncthreads();
+        if (t + 1 < ntiles) load_tile(kv0 + PF_BN);
+        if (!active || kv0 > qw0 + PF_QW - 1) continue;  // whole tile in this wave's future
+
+        // ---- S^T = K Q^T : tile mt covers keys kv0 + 16mt .. +15
+        f32x4_t sacc[4][2];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) sacc[mt][0] = sacc[mt][1] = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8_t a = *(const bf16x8_t*)(ks + swz<D>(16 * mt + lr, 4 * s + lg));
+                sacc[mt][0] = mfma16(a, qf[0][s], sacc[mt][0]);
+                sacc[mt][1] = mfma16(a, qf[1][s], sacc[mt][1]);
+            }
+        }
+
+        // ---- online softmax; lane holds query qw0 + 16n + lr and keys kv0 + 16mt + 4lg + i
+        const bool diag = kv0 + PF_BN - 1 > qw0;
+        bf16x8_t pf[2][2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int qi = qw0 + 16 * n + lr;
+            if (diag) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (kv0 + 16 * mt + 4 * lg + i > qi) sacc[mt][n][i] = -INFINITY;
+            }
+            float mx = sacc[0][n][0];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[mt][n][i]);
+            mx = fmaxf(mx, xor_shfl(mx, 16));
+            mx = fmaxf(mx, xor_shfl(mx, 32));
+            const float mnew = fmaxf(m_run[n], mx);
+            const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+            const float alpha = __builtin_amdgcn_exp2f((m_run[n] - mref) * c);
+            const float mc = mref * c;
+            float ls = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][i], c, -mc));
+                    sacc[mt][n][i] = p;
+                    ls += p;
+                }
+            l_run[n] = l_run[n] * alpha + ls;
+            m_run[n] = mnew;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt][n] *= alpha;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                u32x4_t pw;
+                pw[0] = pack_bf16x2(sacc[2 * kk][n][0], sacc[2 * kk][n][1]);
+                pw[1] = pack_bf16x2(sacc[2 * kk][n][2], sacc[2 * kk][n][3]);
+                pw[2] = pack_bf16x2(sacc[2 * kk + 1][n][0], sacc[2 * kk + 1][n][1]);
+                pw[3] = pack_bf16x2(sacc[2 * kk + 1][n][2], sacc[2 * kk + 1][n][3]);
+                pf[n][kk] = __builtin_bit_cast(bf16x8_t, pw);
+            }
+        }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8_t a = v_frag<D>(vs, 32 * kk, 16 * dt, lane);
+                oacc[dt][0] = mfma16(a, pf[0][kk], oacc[dt][0]);
+                oacc[dt][1] = mfma16(a, pf[1][kk], oacc[dt][1]);
+            }
+        }
+    }
+
+    // ---- epilogue: O = O^T / l, lane holds query qw0 + 16n + lr, dims 16dt + 4lg .. +3
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        float lt = l_run[n];
+        lt += xor_shfl(lt, 16);
+        lt += xor_shfl(lt, 32);
+        const int qi = qw0 + 16 * n + lr;
+        if (qi >= S) continue;
+        const float inv = 1.f / lt;
+        uint16_t* const orow = o + qo_base + (size_t)qi * D + 4 * lg;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            u32x2_t wv;
+            wv[0] = pack_bf16x2(oacc[dt][n][0] * inv, oacc[dt][n][1] * inv);
+            wv[1] = pack_bf16x2(oacc[dt][n][2] * inv, oacc[dt][n][3] * inv);
+            *(u32x2_t*)(orow + 16 * dt) = wv;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ fp32
+constexpr int PF32_TK = 32;  // keys per tile
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restrict__ q,
+                                                          const float* __restrict__ k,
+                                                          const float* __restrict__ v,
+                                                          float* __restrict__ o, int B, int Hq,
+                                                          int Hkv, int S, float c, int HPW,
+                                                          int n_qblk, int n_hchunk) {
+    constexpr int DP = D / 4;  // dims per thread (4 threads per query row)
+    __shared__ float ks[PF32_TK][D];
+    __shared__ float vs[PF32_TK][D];
+
+    const int G = Hq / Hkv;
+    const int QPH = 64 / HPW;  // queries per head per workgroup
+    const int per = B * Hkv * n_hchunk;
+    const int qb = n_qblk - 1 - (int)blockIdx.x / per;
+    const int rem = (int)blockIdx.x % per;
+    const int bkv = rem % (B * Hkv), hc = rem / (B * Hkv);
+    const int b = bkv / Hkv, kvh = bkv % Hkv;
+
+    const int tid = threadIdx.x, slot = tid >> 2, part = tid & 3;
+    const int h = kvh * G + hc * HPW + slot / QPH;
+    const int qi = qb * QPH + slot % QPH;
+    const size_t qo = ((size_t)(b * Hq + h) * S + qi) * D + part * DP;
+    const float* const kg = k + (size_t)(b * Hkv + kvh) * S * D;
+    const float* const vg = v + (size_t)(b * Hkv + kvh) * S * D;
+
+    float qr[DP], acc[DP];
+#pragma unroll
+    for (int e = 0; e < DP; ++e) {
+        qr[e] = qi < S ? q[qo + e] : 0.f;
+        acc[e] = 0.f;
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int kv_end = min(qb * QPH + QPH, S);
+    const int ntiles = ceil_div(kv_end, PF32_TK);
+    for (int t = 0; t < ntiles; ++t) {
+        const int kv0 = t * PF32_TK;
+        __syncthreads();
+        for (int e = tid; e < PF32_TK * D; e += 256) {
+            const int r = e / D, d = e % D, key = kv0 + r;
+            ks[r][d] = key < S ? kg[(size_t)key * D + d] : 0.f;
+            vs[r][d] = key < S ? vg[(size_t)key * D + d] : 0.f;
+        }
+        __syncthreads();
+        for (int j = 0; j < PF32_TK; ++j) {
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < DP; ++e) dot = fmaf(qr[e], ks[j][part * DP + e], dot);
+            dot += __shfl_xor(dot, 1, 64);
+            dot += __shfl_xor(dot, 2, 64);
+            if (kv0 + j <= qi) {
+                const float mnew = fmaxf(m_run, dot);
+                const float alpha = exp2f((m_run - mnew) * c);
+                const float p = exp2f((dot - mnew) * c);
+                l_run = l_run * alpha + p;
+#pragma unroll
+                for (int e = 0; e < DP; ++e) acc[e] = fmaf(p, vs[j][part * DP + e], acc[e] * alpha);
+                m_run = mnew;
+            }
+        }
+    }
+    if (qi < S) {
+        const float inv = 1.f / l_run;
+#pragma unroll
+        for (int e = 0; e < DP; ++e) o[qo + e] = acc[e] * inv;
+    }
+}
+
+int largest_pow2_divisor(int g, int cap) {
+    int hp = 1;
+    while (hp * 2 <= cap && g % (hp * 2) == 0) hp *= 2;
+    return hp;
+}
+
+template <int D, int HPW>
+hipError_t launch_bf16(void* o, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                       int S, float c, hipStream_t st) {
+    constexpr int QPB = (PF_NW / HPW) * PF_QW;
+    const int G = Hq / Hkv;
+    const int n_qblk = ceil_div(S, QPB), n_hchunk = G / HPW;
+    const long long nblk = (long long)n_qblk * B * Hkv * n_hchunk;
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW>), dim3((unsigned)nblk), dim3(PF_THREADS), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, B,
+                       Hq, Hkv, S, c, n_qblk, n_hchunk);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16_d(void* o, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                         int S, float c, hipStream_t st) {
+    switch (largest_pow2_divisor(Hq / Hkv, PF_NW)) {
+        case 8: return launch_bf16<D, 8>(o, q, k, v, B, Hq, Hkv, S, c, st);
+        case 4: return launch_bf16<D, 4>(o, q, k, v, B, Hq, Hkv, S, c, st);
+        case 2: return launch_bf16<D, 2>(o, q, k, v, B, Hq, Hkv, S, c, st);
+        default: return launch_bf16<D, 1>(o, q, k, v, B, Hq, Hkv, S, c, st);
+    }
+}
+
+template <int D>
+hipError_t launch_f32(void* o, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                      int S, float c, hipStream_t st) {
+    const int G = Hq / Hkv;
+    const int HPW = largest_pow2_divisor(G, 4);
+    const int QPH = 64 / HPW;
+    const int n_qblk = ceil_div(S, QPH), n_hchunk = G / HPW;
+    const long long nblk = (long long)n_qblk * B * Hkv * n_hchunk;
+    hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3((unsigned)nblk), dim3(256), 0, st,
+                       (const float*)q, (const float*)k, (const float*)v, (float*)o, B, Hq, Hkv, S,
+                       c, HPW, n_qblk, n_hchunk);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(void* o, const void* q, const void* k, const void* v, int dtype, int B,
+                          int Hq, int Hkv, int S, int D, float scale, hipStream_t st) {
+    const float c = scale * kLog2e;
+    if (dtype == kBF16)
+        return D == 64 ? launch_bf16_d<64>(o, q, k, v, B, Hq, Hkv, S, c, st)
+                       : launch_bf16_d<128>(o, q, k, v, B, Hq, Hkv, S, c, st);
+    return D == 64 ? launch_f32<64>(o, q, k, v, B, Hq, Hkv, S, c, st)
+                   : launch_f32<128>(o, q, k, v, B, Hq, Hkv, S, c, st);
+}
+
+}  // namespace attn

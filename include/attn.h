@@ -1,0 +1,133 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) causal grouped-query attention
+ * library: rotary position embedding, causal prefill and single-token decode
+ * over a contiguous KV cache.
+ *
+ * What is computed (pages cited by title and section):
+ *  - "Grouped Query Attention (GQA)" glossary, section "Cómo funciona GQA":
+ *    query heads are split into Hkv consecutive groups of G = Hq / Hkv heads;
+ *    every head of group j attends with its own queries to the one key head
+ *    and one value head j, using unchanged scaled dot-product attention.  The
+ *    page's example is causal, and equals multi-head attention with each
+ *    key/value head repeated (interleaved) G times.  G = 1 is multi-head
+ *    attention, Hkv = 1 multi-query attention.
+ *  - same page, section "Por qué GQA reduce la caché KV": in generation the
+ *    keys/values of all earlier tokens sit in a cache that is read in full for
+ *    every new token; its size scales with Hkv, not Hq.
+ *  - "Compressed Convolutional Attention" summary, section "Methodologie"
+ *    (items 1 and 4, and the CCGQA paragraph): attention runs entirely inside
+ *    a compressed latent of small per-head dims, with key/value heads shared by
+ *    groups, and RoPE applied there directly to q and k.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers, contiguous, innermost dim D (stride
+ *    1), and 16-byte aligned.  Element type is given by `dtype`.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued on it; calls return without synchronising.  The caller keeps
+ *    every buffer alive until that work completes.
+ *  - The library allocates and frees nothing and keeps no state between calls;
+ *    calls on different streams may run concurrently on distinct buffers.
+ *  - Arguments are validated on the host before any HIP call.  On a non-zero
+ *    status nothing was enqueued.  ATTN_ERR_HIP reports a failed launch (the
+ *    HIP error is consumed with hipGetLastError).
+ *  - An empty problem (B == 0 or S == 0) returns ATTN_OK and enqueues nothing.
+ *  - Supported head dims: D = 64 and D = 128.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_F32 = 0,   /* IEEE binary32 */
+    ATTN_BF16 = 1   /* bfloat16 (top half of binary32), round to nearest even */
+} attn_dtype;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = 2,        /* negative size, Hq/Hkv < 1, Hq % Hkv != 0, max_len > S_cap, ... */
+    ATTN_ERR_UNSUPPORTED = 3,  /* D not 64/128, unknown dtype, theta <= 0, f32 decode */
+    ATTN_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned */
+    ATTN_ERR_WORKSPACE = 5,    /* decode workspace missing or too small */
+    ATTN_ERR_HIP = 6           /* a kernel launch failed */
+} attn_status;
+
+/*
+ * Rotary position embedding of x [B, H, S, D] into out [B, H, S, D].
+ *
+ * Token s of sequence b sits at the integer position
+ *     p = pos_offset[b] + pos_shift + s        (pos_offset NULL: offsets 0)
+ * and for every head and channel pair i < D/2 the pair (x[2i], x[2i+1]) is
+ * rotated by the angle p * theta^(-2i/D):
+ *     out[2i]   = x[2i] cos(a) - x[2i+1] sin(a)
+ *     out[2i+1] = x[2i] sin(a) + x[2i+1] cos(a).
+ * The pages name RoPE ("Compressed Convolutional Attention", "Methodologie"
+ * item 4; "Latent-Condensed Transformer", section 2B: a nonlinear function of
+ * absolute position) without printing its formula; this is the original
+ * rotary form with adjacent channel pairs.  Use it on Q and on K (never V).
+ * For a decode query [B, Hq, 1, D] pass pos_offset = seqlens, pos_shift = -1.
+ *
+ * out == in is allowed (in place); other overlaps are undefined.
+ * pos_offset: device int32[B] or NULL.  theta > 0.  dtype: F32 or BF16.
+ * The angle is formed from the exact integer position in double precision.
+ */
+int attn_rope(void *out, const void *in, int dtype, int B, int H, int S, int D,
+              const int32_t *pos_offset, int pos_shift, double theta, void *stream);
+
+/*
+ * Causal grouped-query attention over one sequence block ("prefill").
+ *
+ *   q, o: [B, Hq, S, D];  k, v: [B, Hkv, S, D];  Hq % Hkv == 0, G = Hq / Hkv.
+ *   o[b,h,i,:] = sum_{t<=i} softmax_t(scale * <q[b,h,i,:], k[b,h/G,t,:]>) v[b,h/G,t,:]
+ *
+ * Queries and keys share positions (the page's is_causal example: query i sees
+ * keys 0..i).  bf16 inputs use bf16 matrix-core products with fp32
+ * accumulation and an fp32 softmax; the probabilities are rounded to bf16
+ * before the product with V.  fp32 inputs are computed in fp32 throughout.
+ * o must not overlap q, k or v.  scale: usually 1/sqrt(D).
+ */
+int attn_prefill(void *o, const void *q, const void *k, const void *v, int dtype,
+                 int B, int Hq, int Hkv, int S, int D, float scale, void *stream);
+
+/*
+ * Bytes of device workspace attn_decode needs for these sizes (0 on invalid
+ * sizes).  The workspace holds one fp32 partial result per (sequence, query
+ * head, key chunk); chunking depends only on B, Hkv and max_len.
+ */
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D);
+
+/*
+ * One new query token per sequence against a contiguous KV cache ("decode").
+ *
+ *   q, o: [B, Hq, D];  k_cache, v_cache: [B, Hkv, S_cap, D];
+ *   seqlens: device int32[B], seqlens[b] = number of valid cached tokens of
+ *   sequence b (the new token's key/value included), 0 <= seqlens[b] <= max_len.
+ *   o[b,h,:] = sum_{t<len_b} softmax_t(scale * <q[b,h,:], k[b,h/G,t,:]>) v[b,h/G,t,:]
+ *
+ * Cache slots at or beyond seqlens[b] are never read into the result (they may
+ * hold anything, NaN included).  A sequence with seqlens[b] == 0 gets a zero
+ * row.  Out-of-contract lengths are clamped to [0, max_len] on the device.
+ * max_len <= S_cap is a host-side upper bound of the lengths.
+ * workspace: device buffer of at least attn_decode_workspace_size(...) bytes,
+ * 16-byte aligned; its contents on entry do not matter.  dtype: BF16 only.
+ * Two kernels are enqueued: a split pass over key chunks and a merge pass.
+ */
+int attn_decode(void *o, const void *q, const void *k_cache, const void *v_cache, int dtype,
+                int B, int Hq, int Hkv, int S_cap, int D, const int32_t *seqlens,
+                int max_len, float scale, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -113,22 +113,22 @@ void oracle_round_f32(float *out, const double *in, size_t n)
 void oracle_rope(double *out, const void *x, int dt, int B, int H, int S, int D,
                  const int32_t *pos_offset, double theta)
 {
-    for (int b = 0; b < B; ++b) {
+    /* rows are independent: one OpenMP iteration per (b, h, s) row */
+#pragma omp parallel for schedule(static)
+    for (long long flat = 0; flat < (long long)B * H * S; ++flat) {
+        int s = (int)(flat % S);
+        int b = (int)(flat / ((long long)S * H));
         long long off = pos_offset ? pos_offset[b] : 0;
-        for (int h = 0; h < H; ++h) {
-            for (int s = 0; s < S; ++s) {
-                double p = (double)(off + s);
-                size_t row = (((size_t)b * H + h) * S + s) * (size_t)D;
-                for (int i = 0; i < D / 2; ++i) {
-                    double freq = pow(theta, -2.0 * i / D);
-                    double ang = p * freq;
-                    double c = cos(ang), sn = sin(ang);
-                    double x0 = load(x, row + 2 * i, dt);
-                    double x1 = load(x, row + 2 * i + 1, dt);
-                    out[row + 2 * i] = x0 * c - x1 * sn;
-                    out[row + 2 * i + 1] = x0 * sn + x1 * c;
-                }
-            }
+        double p = (double)(off + s);
+        size_t row = (size_t)flat * (size_t)D;
+        for (int i = 0; i < D / 2; ++i) {
+            double freq = pow(theta, -2.0 * i / D);
+            double ang = p * freq;
+            double c = cos(ang), sn = sin(ang);
+            double x0 = load(x, row + 2 * i, dt);
+            double x1 = load(x, row + 2 * i + 1, dt);
+            out[row + 2 * i] = x0 * c - x1 * sn;
+            out[row + 2 * i + 1] = x0 * sn + x1 * c;
         }
     }
 }

@@ -1,0 +1,176 @@
+"""The C ABI library loads, exports what include/attn.h declares, and validates
+arguments on the host (CPU only: every call here fails validation or is an
+empty problem, so no HIP call is made)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import compressed_latent_causal_amd as attn
+from compressed_latent_causal_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP = range(7)
+F32, BF16 = 0, 1
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    declared = _declared()
+    assert declared == sorted(_lib.SIGNATURES), declared
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (attn_\w+)", out))
+    assert set(declared) <= exported
+    # nothing else leaks out under the attn_ prefix, and no C++ symbols are exported
+    assert exported == set(declared)
+    assert not re.search(r" T _Z", out)
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.attn_status_string(s).decode()
+    assert L.attn_status_string(99) == b"unknown status"
+
+
+def test_enum_values_match_header():
+    text = open(HEADER).read()
+    for name, val in [("ATTN_F32", 0), ("ATTN_BF16", 1), ("ATTN_OK", 0), ("ATTN_ERR_NULL", 1),
+                      ("ATTN_ERR_SHAPE", 2), ("ATTN_ERR_UNSUPPORTED", 3), ("ATTN_ERR_ALIGN", 4),
+                      ("ATTN_ERR_WORKSPACE", 5), ("ATTN_ERR_HIP", 6)]:
+        assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
+        if name.startswith("ATTN_ERR") or name == "ATTN_OK":
+            assert _lib.STATUS[val] == name
+
+
+# ---------------------------------------------------------------- rope
+def test_rope_validation(L):
+    r = lambda *a: L.attn_rope(*a)
+    assert r(FAKE, FAKE, BF16, -1, 8, 16, 128, None, 0, 1e4, None) == ESHAPE
+    assert r(FAKE, FAKE, BF16, 1, 0, 16, 128, None, 0, 1e4, None) == ESHAPE
+    assert r(FAKE, FAKE, BF16, 1, 8, -2, 128, None, 0, 1e4, None) == ESHAPE
+    assert r(FAKE, FAKE, BF16, 1, 8, 16, 96, None, 0, 1e4, None) == EUNSUP
+    assert r(FAKE, FAKE, 7, 1, 8, 16, 128, None, 0, 1e4, None) == EUNSUP
+    assert r(FAKE, FAKE, BF16, 1, 8, 16, 128, None, 0, 0.0, None) == EUNSUP
+    assert r(FAKE, FAKE, BF16, 1, 8, 16, 128, None, 0, float("nan"), None) == EUNSUP
+    assert r(None, FAKE, BF16, 1, 8, 16, 128, None, 0, 1e4, None) == ENULL
+    assert r(FAKE, None, BF16, 1, 8, 16, 128, None, 0, 1e4, None) == ENULL
+    assert r(FAKE + 8, FAKE, BF16, 1, 8, 16, 128, None, 0, 1e4, None) == EALIGN
+    assert r(FAKE, FAKE, BF16, 1, 8, 16, 128, FAKE + 2, 0, 1e4, None) == EALIGN
+    assert r(FAKE, FAKE, BF16, 70000, 8, 16, 128, None, 0, 1e4, None) == ESHAPE
+    # empty problems succeed without touching the (NULL) pointers
+    assert r(None, None, BF16, 0, 8, 16, 128, None, 0, 1e4, None) == OK
+    assert r(None, None, F32, 3, 8, 0, 64, None, 0, 1e4, None) == OK
+
+
+# ---------------------------------------------------------------- prefill
+def test_prefill_validation(L):
+    p = lambda *a: L.attn_prefill(*a)
+    args = lambda **kw: [kw.get("o", FAKE), kw.get("q", FAKE), kw.get("k", FAKE), kw.get("v", FAKE),
+                         kw.get("dt", BF16), kw.get("B", 1), kw.get("Hq", 8), kw.get("Hkv", 2),
+                         kw.get("S", 16), kw.get("D", 64), kw.get("scale", 0.125), None]
+    assert p(*args(Hkv=3)) == ESHAPE
+    assert p(*args(Hkv=0)) == ESHAPE
+    assert p(*args(Hq=0)) == ESHAPE
+    assert p(*args(B=-1)) == ESHAPE
+    assert p(*args(S=-5)) == ESHAPE
+    assert p(*args(D=32)) == EUNSUP
+    assert p(*args(dt=2)) == EUNSUP
+    assert p(*args(scale=0.0)) == EUNSUP
+    assert p(*args(scale=-0.1)) == EUNSUP
+    assert p(*args(scale=float("inf"))) == EUNSUP
+    for name in "oqkv":
+        assert p(*args(**{name: None})) == ENULL
+        assert p(*args(**{name: FAKE + 4})) == EALIGN
+    assert p(*args(B=1 << 20, S=1 << 20)) == ESHAPE  # grid would overflow 32 bits
+    assert p(*args(o=None, q=None, k=None, v=None, B=0)) == OK
+    assert p(*args(o=None, q=None, k=None, v=None, S=0)) == OK
+
+
+# ---------------------------------------------------------------- decode
+def test_decode_workspace_size(L):
+    ws = L.attn_decode_workspace_size
+    assert ws(1, 8, 3, 100, 128) == 0          # Hq % Hkv
+    assert ws(1, 8, 2, 100, 96) == 0           # head dim
+    assert ws(0, 8, 2, 100, 128) == 0          # empty
+    n = ws(32, 32, 8, 8192, 128)
+    assert n > 0 and n % (4 * 130) == 0        # (D + 2) floats per partial
+    # partials per (sequence, head, chunk): grows with max_len, never shrinks
+    sizes = [ws(1, 64, 8, L_, 128) for L_ in (1, 512, 4096, 131072)]
+    assert sizes == sorted(sizes) and sizes[0] > 0
+    assert ws(2, 8, 2, 0, 64) > 0              # the merge pass still writes zeros
+
+
+def test_decode_validation(L):
+    d = L.attn_decode
+    big = 1 << 40
+
+    def args(**kw):
+        return [kw.get("o", FAKE), kw.get("q", FAKE), kw.get("kc", FAKE), kw.get("vc", FAKE),
+                kw.get("dt", BF16), kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 2),
+                kw.get("S_cap", 64), kw.get("D", 128), kw.get("lens", FAKE),
+                kw.get("max_len", 64), kw.get("scale", 0.088), kw.get("ws", FAKE),
+                kw.get("ws_bytes", big), None]
+
+    assert d(*args(Hkv=3)) == ESHAPE
+    assert d(*args(max_len=65)) == ESHAPE
+    assert d(*args(max_len=-1)) == ESHAPE
+    assert d(*args(S_cap=0, max_len=0)) == ESHAPE
+    assert d(*args(dt=F32)) == EUNSUP
+    assert d(*args(D=80)) == EUNSUP
+    assert d(*args(scale=0.0)) == EUNSUP
+    for name in ("o", "q", "kc", "vc", "lens"):
+        assert d(*args(**{name: None})) == ENULL
+    for name in ("o", "q", "kc", "vc"):
+        assert d(*args(**{name: FAKE + 8})) == EALIGN
+    assert d(*args(lens=FAKE + 2)) == EALIGN
+    assert d(*args(ws=None)) == EWS
+    need = L.attn_decode_workspace_size(2, 8, 2, 64, 128)
+    assert d(*args(ws_bytes=need - 1)) == EWS
+    assert d(*args(ws=FAKE + 4)) == EALIGN
+    assert d(*args(B=70000)) == ESHAPE
+    assert d(*args(o=None, q=None, kc=None, vc=None, lens=None, ws=None, B=0)) == OK
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "_HERE", str(tmp_path))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()
+
+
+def test_attn_error_carries_status():
+    e = attn.AttnError(ESHAPE)
+    assert e.status == ESHAPE and "ATTN_ERR_SHAPE" in str(e)
+
+
+def test_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "compressed_latent_causal_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "liboracle" not in text, f
+                assert "oracle.c" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert not re.search(r"^\s*(import|from)\s+compressed_latent_causal_amd\b", text,
+                                 re.M), f
+            assert "libattn" not in text, f

@@ -1,0 +1,377 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64 CPU
+oracle on the same seeded inputs (marker `gpu`; needs an MI355X).
+
+Tolerances (the benchmark spec): bf16 attention max |err| <= 2e-2 and mean |err| <=
+2e-3; fp32 attention max |err| <= 1e-5.  RoPE is checked bit for bit: the bf16
+output must equal the oracle's fp64 rotation rounded to nearest even (an
+element whose exact value lies within 1e-9 ulp of a rounding midpoint may
+round either way), and each token's rotation must match its own integer
+position better than any neighbouring one.  No expected value comes from the
+GPU; inputs come from compressed_latent_causal_amd.workloads.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_latent_causal_amd as attn
+import oracle
+from compressed_latent_causal_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, F32_MAX = 2e-2, 2e-3, 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    attn.lib()  # fail loudly if the library was not built
+
+
+DEV = "cuda"
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def bits(t):
+    return wl.to_numpy_bits(t)
+
+
+def dev(t):
+    return t.to(DEV)
+
+
+def host_f64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def assert_close(got, ref, max_tol, mean_tol=None, what=""):
+    diff = np.abs(got - ref)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    mx, mn = float(diff.max()), float(diff.mean())
+    say(f"{what}: max {mx:.3e} mean {mn:.3e}")
+    assert mx <= max_tol, f"{what}: max abs err {mx} > {max_tol}"
+    if mean_tol is not None:
+        assert mn <= mean_tol, f"{what}: mean abs err {mn} > {mean_tol}"
+
+
+def rand_bf16(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(*shape, generator=g).to(torch.bfloat16)
+
+
+# ============================================================== RoPE
+def _bf16_near_midpoint(y):
+    """Elements whose fp64 value is within 1e-9 ulp of a bf16 rounding midpoint."""
+    a = np.abs(y)
+    _, e = np.frexp(a)                 # a = m * 2**e, 0.5 <= m < 1
+    ulp = np.ldexp(1.0, e - 8)         # bf16 keeps 8 significant bits
+    frac = a / ulp - np.floor(a / ulp)
+    return np.abs(frac - 0.5) <= 1e-9
+
+
+@pytest.mark.parametrize("D,theta,B,H,S,offsets", [
+    (128, 5e5, 2, 3, 37, [0, 131000]),
+    (64, 1e4, 1, 8, 300, [5]),
+    (128, 1e4, 3, 2, 16, [0, 1, 2_000_000]),
+    (64, 5e5, 2, 1, 129, None),
+])
+def test_rope_bf16_is_correctly_rounded(D, theta, B, H, S, offsets):
+    x = rand_bf16((B, H, S, D), 100 + S)
+    off = None if offsets is None else torch.tensor(offsets, dtype=torch.int32)
+    say(f"rope bf16 B={B} H={H} S={S} D={D} theta={theta} offsets={offsets}")
+    y = attn.rope(dev(x), theta, None if off is None else dev(off))
+    torch.cuda.synchronize()
+    ref = oracle.rope(bits(x), theta, None if off is None else off.numpy())
+    want = oracle.round_bf16(ref)
+    got = bits(y)
+    mism = got != want
+    if mism.any():
+        assert _bf16_near_midpoint(ref[mism]).all(), f"{mism.sum()} elements differ from RNE(oracle)"
+    assert mism.sum() <= max(1, got.size // 100000)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_position_indexing_is_exact(D):
+    """Every token's output is closest to the oracle at its own position, not a
+    neighbouring one (checked over a window of +-3 positions)."""
+    B, H, S = 2, 2, 64
+    offsets = np.array([0, 131007], dtype=np.int32)
+    x = rand_bf16((B, H, S, D), 7)
+    say(f"rope indexing D={D}")
+    y = host_f64(attn.rope(dev(x), 5e5, dev(torch.from_numpy(offsets))))
+    dists = []
+    for delta in range(-3, 4):
+        r = oracle.widen(oracle.round_bf16(oracle.rope(bits(x), 5e5, offsets + delta)))
+        dists.append(np.abs(y - r).sum(axis=-1))
+    best = np.argmin(np.stack(dists), axis=0)
+    assert (best == 3).all()
+
+
+def test_rope_fp32_and_in_place():
+    x = torch.randn(2, 4, 50, 128, generator=torch.Generator().manual_seed(3))
+    offs = torch.tensor([7, 90000], dtype=torch.int32)
+    say("rope fp32 out-of-place and in place")
+    xd = dev(x)
+    y = attn.rope(xd, 5e5, dev(offs))
+    ref = oracle.rope(x.numpy(), 5e5, offs.numpy())
+    assert_close(host_f64(y), ref, 1e-6, what="rope fp32")
+    attn.rope(xd, 5e5, dev(offs), out=xd)
+    assert torch.equal(xd, y)
+    xb = dev(rand_bf16((1, 3, 20, 64), 4))
+    yb = attn.rope(xb, 1e4)
+    attn.rope(xb, 1e4, out=xb)
+    assert torch.equal(xb, yb)
+
+
+def test_rope_decode_positions_from_lengths():
+    """pos_offset = seqlens and pos_shift = -1 put each decode query at len - 1."""
+    lens = torch.tensor([1, 17, 8192, 131072], dtype=torch.int32)
+    q = rand_bf16((4, 8, 1, 128), 11)
+    say("rope decode positions")
+    y = bits(attn.rope(dev(q), 5e5, dev(lens), pos_shift=-1))
+    want = oracle.round_bf16(oracle.rope(bits(q), 5e5, lens.numpy() - 1))
+    assert (y != want).sum() <= 1
+
+
+# ============================================================== prefill
+def _oracle_prefill_e2e(q, k, v, theta, scale, dtype, rows=None):
+    """Oracle pipeline: RoPE in fp64, rounded to the storage type (the dtype
+    boundary between the two calls), then attention in fp64."""
+    rq = oracle.round_to(oracle.rope(bits(q), theta), dtype)
+    rk = oracle.round_to(oracle.rope(bits(k), theta), dtype)
+    return oracle.prefill(rq, rk, bits(v), scale=scale, rows=rows)
+
+
+def test_prefill_worked_example_fp32_end_to_end():
+    """The GQA glossary's example geometry (8 query heads, 2 KV heads, 16
+    tokens, dim 64, seed 0) with RoPE theta 1e4 and scale 1/8, in fp32."""
+    w = wl.WORKLOADS["tiny_gqa"]
+    q, k, v = wl.make_prefill(w, seed=0)
+    say("tiny fp32 end to end")
+    o = attn.prefill(attn.rope(dev(q), w.theta), attn.rope(dev(k), w.theta), dev(v), w.scale)
+    ref = _oracle_prefill_e2e(q, k, v, w.theta, w.scale, "f32")
+    assert tuple(o.shape) == (1, 8, 16, 64)
+    assert_close(host_f64(o), ref, F32_MAX, what="tiny fp32")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_prefill_worked_example_gqa_equals_repeated_mha(seed):
+    w = wl.WORKLOADS["tiny_gqa"]
+    q, k, v = (dev(t) for t in wl.make_prefill(w, seed=seed))
+    say(f"tiny GQA vs repeat-interleaved MHA seed {seed}")
+    out = attn.prefill(q, k, v)
+    ref = attn.prefill(q, k.repeat_interleave(4, dim=1).contiguous(),
+                       v.repeat_interleave(4, dim=1).contiguous())
+    assert torch.allclose(out, ref, atol=1e-6, rtol=0)
+
+
+GEOMS = [  # B, Hq, Hkv, S, D
+    (1, 8, 2, 1, 64),
+    (1, 8, 2, 16, 64),
+    (1, 8, 2, 63, 64),
+    (1, 8, 2, 64, 64),
+    (1, 8, 2, 65, 64),
+    (1, 8, 2, 130, 64),
+    (2, 8, 2, 257, 64),
+    (2, 8, 2, 200, 128),
+    (1, 4, 4, 300, 128),     # MHA
+    (1, 8, 1, 150, 64),      # MQA, G = 8
+    (1, 32, 2, 70, 128),     # G = 16: two head slices per KV group
+    (2, 6, 2, 100, 64),      # G = 3
+    (1, 12, 2, 90, 128),     # G = 6
+    (3, 4, 2, 513, 128),
+]
+
+
+@pytest.mark.parametrize("geom", GEOMS)
+def test_prefill_bf16_matches_oracle(geom):
+    B, Hq, Hkv, S, D = geom
+    q, k, v = rand_bf16((B, Hq, S, D), 1), rand_bf16((B, Hkv, S, D), 2), rand_bf16((B, Hkv, S, D), 3)
+    say(f"prefill bf16 {geom}")
+    o = attn.prefill(dev(q), dev(k), dev(v))
+    ref = oracle.prefill(bits(q), bits(k), bits(v))
+    assert_close(host_f64(o), ref, BF16_MAX, BF16_MEAN, what=f"prefill bf16 {geom}")
+
+
+@pytest.mark.parametrize("geom", [(1, 8, 2, 1, 64), (1, 8, 2, 77, 64), (2, 4, 4, 100, 128),
+                                  (1, 8, 1, 40, 128), (1, 6, 2, 33, 64)])
+def test_prefill_fp32_matches_oracle(geom):
+    B, Hq, Hkv, S, D = geom
+    g = torch.Generator().manual_seed(5)
+    q, k, v = (torch.randn(*s, generator=g) for s in [(B, Hq, S, D), (B, Hkv, S, D), (B, Hkv, S, D)])
+    say(f"prefill fp32 {geom}")
+    o = attn.prefill(dev(q), dev(k), dev(v))
+    ref = oracle.prefill(q.numpy(), k.numpy(), v.numpy())
+    assert_close(host_f64(o), ref, F32_MAX, what=f"prefill fp32 {geom}")
+
+
+def test_prefill_gqa_equals_repeated_mha_bitwise():
+    B, Hq, Hkv, S, D = 2, 8, 2, 333, 128
+    q, k, v = (dev(rand_bf16(s, i)) for i, s in enumerate([(B, Hq, S, D), (B, Hkv, S, D), (B, Hkv, S, D)]))
+    say("prefill GQA vs MHA bitwise")
+    out = attn.prefill(q, k, v)
+    mha = attn.prefill(q, k.repeat_interleave(Hq // Hkv, dim=1).contiguous(),
+                       v.repeat_interleave(Hq // Hkv, dim=1).contiguous())
+    assert torch.equal(out, mha)
+
+
+def test_prefill_is_causal_on_gpu():
+    B, Hq, Hkv, S, D = 1, 8, 2, 200, 64
+    q, k, v = rand_bf16((B, Hq, S, D), 8), rand_bf16((B, Hkv, S, D), 9), rand_bf16((B, Hkv, S, D), 10)
+    say("prefill causality")
+    base = attn.prefill(dev(q), dev(k), dev(v))
+    i = 120
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, i + 1:] = rand_bf16(k2[:, :, i + 1:].shape, 11)
+    v2[:, :, i + 1:] = 1e3
+    pert = attn.prefill(dev(q), dev(k2), dev(v2))
+    assert torch.equal(pert[:, :, :i + 1], base[:, :, :i + 1])
+
+
+def test_prefill_scale_and_errors():
+    q, k, v = rand_bf16((1, 4, 40, 64), 12), rand_bf16((1, 2, 40, 64), 13), rand_bf16((1, 2, 40, 64), 14)
+    say("prefill explicit scale")
+    o = attn.prefill(dev(q), dev(k), dev(v), scale=0.3)
+    assert_close(host_f64(o), oracle.prefill(bits(q), bits(k), bits(v), scale=0.3), BF16_MAX,
+                 BF16_MEAN, what="scale 0.3")
+    with pytest.raises(attn.AttnError) as e:
+        attn.prefill(dev(rand_bf16((1, 4, 8, 96), 1)), dev(rand_bf16((1, 2, 8, 96), 2)),
+                     dev(rand_bf16((1, 2, 8, 96), 3)))
+    assert e.value.status == 3
+    with pytest.raises(ValueError):
+        attn.prefill(dev(q), dev(k).float(), dev(v))
+
+
+def _sample_rows(B, Hq, S, n_random, seed):
+    """Row indices (b*Hq + h)*S + i: both ends of every head, tile edges and
+    random interior rows."""
+    rng = np.random.default_rng(seed)
+    edge = [0, 1, 31, 32, 63, 64, 65, S // 2, S - 65, S - 2, S - 1]
+    rows = []
+    for b in range(B):
+        for h in range(Hq):
+            if (b + h) % 3 == 0:
+                rows += [(b * Hq + h) * S + i for i in edge]
+    rows += list(rng.integers(0, B * Hq * S, n_random))
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+@pytest.mark.parametrize("name", ["llama8b_prefill", "ccgqa_prefill"])
+def test_prefill_full_size_sampled_rows(name):
+    """Full-size workloads in the launch configuration the benchmark times:
+    RoPE on Q and K, then prefill, end to end from the raw inputs; the oracle
+    recomputes a sample of output rows."""
+    w = wl.WORKLOADS[name]
+    q, k, v = wl.make_prefill(w, seed=0)
+    say(f"{name} full size: rope + prefill")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o = attn.prefill(attn.rope(qd, w.theta), attn.rope(kd, w.theta), vd, w.scale)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.B, w.Hq, w.S, 200, 42)
+    got = o.reshape(-1, w.D)[torch.from_numpy(rows).to(DEV)].double().cpu().numpy()
+    del o, qd, kd, vd
+    # oracle: RoPE of the sampled query rows and of all keys, rounded to bf16
+    rk = oracle.round_bf16(oracle.rope(bits(k), w.theta))
+    qsel = bits(q).reshape(-1, w.D)[rows].reshape(-1, 1, 1, w.D)   # one "sequence" per row
+    pos = (rows % w.S).astype(np.int32)                               # its token position
+    rq_sel = oracle.round_bf16(oracle.rope(qsel, w.theta, pos))
+    rq = np.zeros(w.B * w.Hq * w.S * w.D, dtype=np.uint16).reshape(-1, w.D)
+    rq[rows] = rq_sel.reshape(-1, w.D)
+    ref = oracle.prefill(rq.reshape(w.B, w.Hq, w.S, w.D), rk, bits(v), scale=w.scale, rows=rows)
+    assert_close(got, ref, BF16_MAX, BF16_MEAN, what=f"{name} sampled rows")
+
+
+# ============================================================== decode
+def _decode_e2e(w, seed, poison=True, max_len=None):
+    q, kc, vc, lens = wl.make_decode(w, seed=seed, poison_tail=poison)
+    say(f"decode {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} S_cap={w.S} D={w.D} "
+        f"lens {int(lens.min())}..{int(lens.max())}")
+    ld = dev(lens)
+    qr = attn.rope(dev(q).unsqueeze(2), w.theta, ld, pos_shift=-1).squeeze(2)
+    o = attn.decode(qr, dev(kc), dev(vc), ld, max_len=max_len, scale=w.scale)
+    torch.cuda.synchronize()
+    rq = oracle.round_bf16(oracle.rope(bits(q)[:, :, None, :], w.theta, lens.numpy() - 1))[:, :, 0]
+    ref = oracle.decode(rq, bits(kc), bits(vc), lens.numpy(), scale=w.scale)
+    return host_f64(o), ref
+
+
+@pytest.mark.parametrize("name", ["gqa_decode", "long_decode"])
+def test_decode_full_size_end_to_end(name):
+    """Full-size decode workloads, every output checked; the gqa workload's
+    cache tail past each length is NaN."""
+    w = wl.WORKLOADS[name]
+    got, ref = _decode_e2e(w, seed=0, poison=(name == "gqa_decode"))
+    assert_close(got, ref, BF16_MAX, BF16_MEAN, what=name)
+
+
+DECODE_CASES = [  # B, Hq, Hkv, S_cap, D, lengths
+    (9, 8, 2, 1100, 128, [0, 1, 31, 32, 33, 511, 512, 513, 1100]),
+    (4, 8, 8, 300, 64, [300, 1, 129, 64]),        # MHA, D = 64
+    (3, 8, 1, 700, 128, [700, 350, 2]),           # MQA, G = 8
+    (2, 32, 2, 260, 128, [260, 100]),             # G = 16
+    (2, 64, 2, 100, 64, [100, 37]),               # G = 32: two head slices
+    (2, 12, 4, 90, 128, [90, 45]),                # G = 3
+    (1, 4, 1, 5000, 128, [4999]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES)
+def test_decode_edge_cases(case):
+    B, Hq, Hkv, S_cap, D, lens = case
+    g = torch.Generator().manual_seed(B * 1000 + S_cap)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kc = torch.randn(B, Hkv, S_cap, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Hkv, S_cap, D, generator=g).to(torch.bfloat16)
+    lt = torch.tensor(lens, dtype=torch.int32)
+    wl.poison_cache_tail(kc, lt)
+    wl.poison_cache_tail(vc, lt)
+    say(f"decode edge {case}")
+    o = attn.decode(dev(q), dev(kc), dev(vc), dev(lt), max_len=max(lens))
+    ref = oracle.decode(bits(q), bits(kc), bits(vc), lt.numpy())
+    got = host_f64(o)
+    assert_close(got, ref, BF16_MAX, BF16_MEAN, what=f"decode {case}")
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert (got[b] == 0).all()
+
+
+def test_decode_ignores_workspace_contents_and_default_max_len():
+    B, Hq, Hkv, S_cap, D = 3, 8, 2, 600, 128
+    q, kc, vc = rand_bf16((B, Hq, D), 20), rand_bf16((B, Hkv, S_cap, D), 21), rand_bf16((B, Hkv, S_cap, D), 22)
+    lens = torch.tensor([600, 5, 300], dtype=torch.int32)
+    need = attn.decode_workspace_size(B, Hq, Hkv, S_cap, D)
+    ws = torch.full((need // 4,), float("nan"), device=DEV)
+    say("decode NaN workspace")
+    o1 = attn.decode(dev(q), dev(kc), dev(vc), dev(lens), workspace=ws)
+    o2 = attn.decode(dev(q), dev(kc), dev(vc), dev(lens), max_len=600)
+    assert torch.equal(o1, o2)
+    ref = oracle.decode(bits(q), bits(kc), bits(vc), lens.numpy())
+    assert_close(host_f64(o1), ref, BF16_MAX, BF16_MEAN, what="decode ws")
+
+
+def test_decode_matches_last_prefill_row():
+    B, Hq, Hkv, S, D = 2, 8, 2, 777, 128
+    q, k, v = rand_bf16((B, Hq, S, D), 30), rand_bf16((B, Hkv, S, D), 31), rand_bf16((B, Hkv, S, D), 32)
+    say("decode vs prefill last row")
+    pre = attn.prefill(dev(q), dev(k), dev(v))
+    dec = attn.decode(dev(q[:, :, S - 1].contiguous()), dev(k), dev(v),
+                      dev(torch.full((B,), S, dtype=torch.int32)))
+    assert_close(host_f64(dec), host_f64(pre[:, :, S - 1]), BF16_MAX, BF16_MEAN, what="dec vs pre")
+
+
+def test_decode_rejects_fp32_and_small_workspace():
+    q = torch.zeros(1, 4, 128, device=DEV)
+    kc = torch.zeros(1, 2, 16, 128, device=DEV)
+    with pytest.raises(attn.AttnError) as e:
+        attn.decode(q, kc, kc, torch.ones(1, dtype=torch.int32, device=DEV))
+    assert e.value.status == 3
+    qb, kb = q.bfloat16(), kc.bfloat16()
+    with pytest.raises(attn.AttnError) as e:
+        attn.decode(qb, kb, kb, torch.ones(1, dtype=torch.int32, device=DEV),
+                    workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == 5
