@@ -1,0 +1,227 @@
+"""Benchmark of the causal GQA attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+Headline workload: the Llama-3.1-8B-shaped prefill layer (batch 4, 32 query
+heads, 8 KV heads, head dim 128, 4096 tokens, bf16, RoPE theta 5e5).  One step
+is one pass of the prefill hot path over that batch: RoPE on Q, RoPE on K, then
+causal GQA attention.  `value` is algorithmic prefill TFLOP/s over the whole
+step (4*B*Hq*D*S(S+1)/2 flops: QK^T and PV over unmasked pairs only), inputs
+resident in HBM.  The `roofline` object prices the prefill kernel alone, timed
+with HIP events on the stream it runs on.  The `decode` object reports KV-cache
+GB/s of the two decode workloads (split + merge, a cache flush between
+iterations), and `cpu_baseline` times the fp64 CPU oracle on a bounded sample
+of the same prefill workload.  Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill attention TFLOP/s & decode KV GB/s (1 MI355X, % of roofline)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(B, Hq, S, D):
+    """QK^T and PV over the S(S+1)/2 unmasked (query, key) pairs of each head."""
+    return 4.0 * B * Hq * D * (S * (S + 1) / 2)
+
+
+def decode_bytes(lens, Hkv, D, elem_bytes=2):
+    """Valid K and V cache bytes read for one token of every sequence."""
+    return float(sum(int(n) for n in lens)) * Hkv * D * 2 * elem_bytes
+
+
+# ---------------------------------------------------------------------------
+def bench_prefill(w, steps, warmup):
+    import torch
+    import compressed_latent_causal_amd as attn
+    from compressed_latent_causal_amd import workloads as wl
+
+    q, k, v = wl.make_prefill(w, seed=0)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    del q, k, v
+    qr, kr, o = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        attn.rope(qd, w.theta, out=qr)
+        attn.rope(kd, w.theta, out=kr)
+        if ev is not None:
+            ev[0].record(stream)
+        attn.prefill(qr, kr, vd, w.scale, out=o)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    return wall * 1e3 / steps, sum(kern_ms) / len(kern_ms), sorted(kern_ms)
+
+
+def bench_decode(w, iters, warmup):
+    import torch
+    import compressed_latent_causal_amd as attn
+    from compressed_latent_causal_amd import workloads as wl
+
+    q, kc, vc, lens = wl.make_decode(w, seed=0)
+    qd, kcd, vcd, ld = q.cuda().unsqueeze(2), kc.cuda(), vc.cuda(), lens.cuda()
+    del kc, vc
+    qr = torch.empty_like(qd)
+    o = torch.empty(w.B, w.Hq, w.D, dtype=qd.dtype, device="cuda")
+    ws = torch.empty(attn.decode_workspace_size(w.B, w.Hq, w.Hkv, w.S, w.D), dtype=torch.uint8,
+                     device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        attn.rope(qd, w.theta, ld, pos_shift=-1, out=qr)
+        attn.decode(qr.squeeze(2), kcd, vcd, ld, max_len=w.S, scale=w.scale, out=o, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    ms = []
+    for _ in range(iters):
+        flush.zero_()  # evict L2 / MALL: every iteration reads the cache from HBM
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    ms.sort()
+    med = ms[len(ms) // 2]
+    nbytes = decode_bytes(lens.tolist(), w.Hkv, w.D)
+    gbs = nbytes / (med * 1e-3) / 1e9
+    return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+            "head_dim": w.D, "cache_capacity": w.S, "sum_len": int(lens.sum()),
+            "kv_bytes": nbytes, "ms_median": round(med, 5), "ms_min": round(ms[0], 5),
+            "GB_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "iters": iters, "step": "rope(q at len-1) + split + merge"}
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The oracle (fp64 C, OpenMP) on a random sample of output rows of the
+    same prefill workload: RoPE of all keys and of the sampled queries, then
+    attention for those rows.  Rows are drawn uniformly, so their mean causal
+    length is that of the whole job; throughput is reported in TFLOP/s of the
+    same algorithmic count."""
+    import numpy as np
+    import oracle
+    from compressed_latent_causal_amd import workloads as wl
+
+    q, k, v = wl.make_prefill(w, seed=0)
+    qb, kb, vb = (wl.to_numpy_bits(t) for t in (q, k, v))
+    rng = np.random.default_rng(0)
+    n_rows, flops, elapsed = 0, 0.0, 0.0
+    batch = 64
+    rq_full = np.zeros((w.B * w.Hq * w.S, w.D), dtype=np.uint16)
+    t_start = time.perf_counter()
+    rk = oracle.round_bf16(oracle.rope(kb, w.theta))
+    while elapsed < budget_s:
+        rows = rng.integers(0, w.B * w.Hq * w.S, batch)
+        qsel = qb.reshape(-1, w.D)[rows].reshape(-1, 1, 1, w.D)
+        rq = oracle.round_bf16(oracle.rope(qsel, w.theta, (rows % w.S).astype(np.int32)))
+        rq_full[rows] = rq.reshape(-1, w.D)
+        oracle.prefill(rq_full.reshape(w.B, w.Hq, w.S, w.D), rk, vb, scale=w.scale, rows=rows)
+        n_rows += batch
+        flops += float(np.sum(4.0 * w.D * ((rows % w.S) + 1)))
+        elapsed = time.perf_counter() - t_start
+        batch = min(batch * 2, 4096)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_rows} uniformly drawn output rows of {w.name} (of {w.B * w.Hq * w.S}), "
+                      f"RoPE of all keys included, {elapsed:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-iters", type=int, default=30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--only", choices=["prefill", "gqa_decode", "long_decode", "ccgqa_prefill"],
+                    help="time one workload alone and print its line (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the attention path is built and timed on a single "
+              "MI355X (no sharding or collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import compressed_latent_causal_amd as attn
+    from compressed_latent_causal_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    attn.lib()
+
+    if args.only in ("gqa_decode", "long_decode"):
+        d = bench_decode(wl.WORKLOADS[args.only], args.decode_iters, args.warmup)
+        print(json.dumps(d), flush=True)
+        return
+    w = wl.WORKLOADS["ccgqa_prefill" if args.only == "ccgqa_prefill" else "llama8b_prefill"]
+    flops = prefill_flops(w.B, w.Hq, w.S, w.D)
+    log(f"prefill {w.name}: {flops:.4e} flop per step")
+    ms_step, ms_kern, kern_sorted = bench_prefill(w, args.steps, args.warmup)
+    tflops_step = flops / (ms_step * 1e-3) / 1e12
+    tflops_kern = flops / (ms_kern * 1e-3) / 1e12
+    log(f"step {ms_step:.4f} ms ({tflops_step:.1f} TFLOP/s); prefill kernel mean {ms_kern:.4f} ms "
+        f"({tflops_kern:.1f} TFLOP/s), min {kern_sorted[0]:.4f} max {kern_sorted[-1]:.4f}")
+
+    result = {
+        "metric": METRIC, "value": round(tflops_step, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "seq_len": w.S, "rope_theta": w.theta, "causal": True,
+                   "step": "rope(Q) + rope(K) + causal GQA prefill"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,4>",
+                     "achieved": round(tflops_kern, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops_kern / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel_ms_mean": round(ms_kern, 5),
+                     "flop_per_launch": flops},
+    }
+    if args.only:
+        print(json.dumps(result), flush=True)
+        return
+    if not args.no_decode:
+        dec = {}
+        for name in ("gqa_decode", "long_decode"):
+            d = bench_decode(wl.WORKLOADS[name], args.decode_iters, 3)
+            log(f"decode {name}: {d['ms_median']:.4f} ms, {d['GB_per_s']:.0f} GB/s")
+            dec[name] = d
+        result["decode"] = dec
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

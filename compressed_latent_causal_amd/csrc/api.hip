@@ -26,7 +26,7 @@ ATTN_API int attn_rope(void* out, const void* in, int dtype, int B, int H, int S
     if (B < 0 || S < 0 || H < 1) return ATTN_ERR_SHAPE;
     if (!known_dtype(dtype) || !supported_dim(D) || !(theta > 0.0) || !isfinite(theta))
         return ATTN_ERR_UNSUPPORTED;
-    if (B > kMaxGridYZ) return ATTN_ERR_SHAPE;
+    if (B > kMaxGridYZ || H > kMaxGridYZ) return ATTN_ERR_SHAPE;
     if (B == 0 || S == 0) return ATTN_OK;
     if (!out || !in) return ATTN_ERR_NULL;
     if (!aligned16(out) || !aligned16(in) || ((uintptr_t)pos_offset & 3u)) return ATTN_ERR_ALIGN;

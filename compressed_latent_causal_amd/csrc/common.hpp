@@ -53,12 +53,20 @@ __device__ inline bf16x4_t lds_read_tr(const void* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
 }
 
-// Byte offset of 16-byte chunk c of row r in a row-major LDS tile whose rows
-// hold D bf16.  Chunks are XOR-swizzled with row bits so that 16 consecutive
-// lanes reading one logical chunk of 16 consecutive rows (the matrix-core
-// operand pattern) touch 16 distinct 16-byte bank groups.
+// LDS tile layouts.  Tiles are row-major (rows of D bf16, no padding) with the
+// 16-byte chunks of each row XOR-permuted by bits of the row index.  Two
+// permutations are used, one per read pattern (both measured free of bank
+// conflicts on gfx950):
+//  * swz_k: 16 consecutive lanes read one logical chunk of 16 consecutive rows
+//    with ds_read_b128 (the matrix-core K operand): chunk c ^ (r & 15) for
+//    D = 128, c ^ ((r >> 1) & 7) for D = 64;
+//  * swz_v: the transpose read, where each 16-lane group reads 32 contiguous
+//    bytes of 4 consecutive rows: chunk c ^ (((r & 7) << 1) | ((r >> 3) & 1))
+//    for D = 128 and c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1)) for D = 64.
+// A whole row is always written by 16 (or 8) consecutive lanes, which any
+// in-row permutation keeps conflict-free.
 template <int D>
-__device__ inline int swz(int r, int c) {
+__device__ inline int swz_k(int r, int c) {
     static_assert(D == 64 || D == 128, "head dim");
     if constexpr (D == 128)
         return r * 256 + ((c ^ (r & 15)) << 4);
@@ -66,24 +74,37 @@ __device__ inline int swz(int r, int c) {
         return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
 }
 
-// Operand fragment for the transposed product O^T = V^T P^T: A[m = d][k = key],
-// lane l gets V[key][d] for d = d0 + l%16 and the 8 keys
-//   r0 + 4*(l/16) + {0,1,2,3}  and  r0 + 16 + 4*(l/16) + {0,1,2,3}
-// from a swizzled row-major V tile.  (The keys match the rows that element i of
-// the S^T = K Q^T tiles m and m+1 hold in lane group l/16.)
 template <int D>
-__device__ inline bf16x8_t v_frag(const char* vt, int r0, int d0, int lane) {
+__device__ inline int swz_v(int r, int c) {
+    static_assert(D == 64 || D == 128, "head dim");
+    if constexpr (D == 128)
+        return r * 256 + ((c ^ (((r & 7) << 1) | ((r >> 3) & 1))) << 4);
+    else
+        return r * 128 + ((c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))) << 4);
+}
+
+// Per-lane byte offsets of the O^T = V^T P^T operand reads in a swz_v tile.
+// For d tile dt, lane l reads V[key][d] for d = 16 dt + l%16 and the 8 keys
+//   r0 + 4*(l/16) + {0,1,2,3}  and  r0 + 16 + 4*(l/16) + {0,1,2,3}
+// (two transpose reads).  The keys match the rows that element i of the S^T =
+// K Q^T tiles m and m+1 hold in lane group l/16.  Because the swizzle depends
+// only on row bits 0..3, the offset of rows r0 = 32k (+16) is the dt offset
+// plus the constant 32k * D * 2 (+ 16 * D * 2).
+template <int D>
+__device__ inline int v_frag_off(int dt, int lane) {
     const int g = lane >> 4, L = lane & 15;
-    const int col = d0 + 4 * (L & 3);           // first of the 4 columns this lane addresses
-    const int c16 = col >> 3, half = (col & 7) * 2;  // 16-byte chunk and byte offset inside it
-    const int ra = r0 + 4 * g + (L >> 2);
-    bf16x4_t lo = lds_read_tr(vt + swz<D>(ra, c16) + half);
-    bf16x4_t hi = lds_read_tr(vt + swz<D>(ra + 16, c16) + half);
-    bf16x8_t a;
+    const int col = 16 * dt + 4 * (L & 3);  // first of the 4 columns this lane addresses
+    return swz_v<D>(4 * g + (L >> 2), col >> 3) + (col & 7) * 2;
+}
+
+template <int D>
+__device__ inline bf16x8_t v_frag_at(const char* p) {
+    constexpr int kRow16 = 16 * D * 2;
+    bf16x4_t lo = lds_read_tr(p);
+    bf16x4_t hi = lds_read_tr(p + kRow16);
     u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
     u32x4_t w = {l2.x, l2.y, h2.x, h2.y};
-    a = __builtin_bit_cast(bf16x8_t, w);
-    return a;
+    return __builtin_bit_cast(bf16x8_t, w);
 }
 
 // ---------------------------------------------------------------- cross-lane

@@ -86,9 +86,11 @@ __global__ __launch_bounds__(DC_NW * 64) void decode_split_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4_t{0, 0, 0, 0};
 
-    for (int t0 = wb; t0 < we; t0 += DC_SUB) {
-        // K operand: token t0 + 16mt + lr, dims 32s + 8lg .. +7
-        bf16x8_t kf[2][KSTEPS];
+    // K operand of a sub-tile: token t0 + 16mt + lr, dims 32s + 8lg .. +7 (zero
+    // past the valid range).  V rows: chunk lane + 64u of the 32 x D sub-tile.
+    bf16x8_t kf[2][KSTEPS];
+    u32x4_t vr[VCPL];
+    auto load_sub = [&](int t0, bf16x8_t (&kd)[2][KSTEPS], u32x4_t (&vd)[VCPL]) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int tok = t0 + 16 * mt + lr;
@@ -96,24 +98,32 @@ __global__ __launch_bounds__(DC_NW * 64) void decode_split_kernel(
             for (int s = 0; s < KSTEPS; ++s) {
                 u32x4_t x = {0, 0, 0, 0};
                 if (tok < we) x = *(const u32x4_t*)(kg + (size_t)tok * D + 32 * s + 8 * lg);
-                kf[mt][s] = __builtin_bit_cast(bf16x8_t, x);
+                kd[mt][s] = __builtin_bit_cast(bf16x8_t, x);
             }
         }
-        // V rows -> this wave's LDS slot (zeros past the valid range)
-        u32x4_t vr[VCPL];
 #pragma unroll
         for (int u = 0; u < VCPL; ++u) {
             const int ci = lane + 64 * u, r = ci / CH, cc = ci % CH;
             const int tok = t0 + r;
-            vr[u] = u32x4_t{0, 0, 0, 0};
-            if (tok < we) vr[u] = *(const u32x4_t*)(vg + (size_t)tok * D + cc * 8);
+            vd[u] = u32x4_t{0, 0, 0, 0};
+            if (tok < we) vd[u] = *(const u32x4_t*)(vg + (size_t)tok * D + cc * 8);
         }
+    };
+    if (wb < we) load_sub(wb, kf, vr);
+
+    for (int t0 = wb; t0 < we; t0 += DC_SUB) {
+        // the loads of the next sub-tile stay in flight while this one is computed
+        bf16x8_t kn[2][KSTEPS];
+        u32x4_t vn[VCPL];
+        const bool more = t0 + DC_SUB < we;
+        if (more) load_sub(t0 + DC_SUB, kn, vn);
+
         // the previous sub-tile's transpose reads must be done before overwriting
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int u = 0; u < VCPL; ++u) {
             const int ci = lane + 64 * u, r = ci / CH, cc = ci % CH;
-            *(u32x4_t*)(vst + swz<D>(r, cc)) = vr[u];
+            *(u32x4_t*)(vst + swz_v<D>(r, cc)) = vr[u];
         }
 
         // S^T = K Q^T; lane holds head lr, tokens t0 + 16mt + 4lg + i
@@ -158,8 +168,16 @@ __global__ __launch_bounds__(DC_NW * 64) void decode_split_kernel(
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V rows are in LDS
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8_t a = v_frag<D>(vst, 0, 16 * dt, lane);
+            const bf16x8_t a = v_frag_at<D>(vst + v_frag_off<D>(dt, lane));
             oacc[dt] = mfma16(a, pf, oacc[dt] * alpha);
+        }
+        if (more) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) kf[mt][s] = kn[mt][s];
+#pragma unroll
+            for (int u = 0; u < VCPL; ++u) vr[u] = vn[u];
         }
     }
 
@@ -201,34 +219,55 @@ __global__ __launch_bounds__(DC_NW * 64) void decode_split_kernel(
     }
 }
 
+constexpr int MG_NW = 16;  // waves per merge workgroup
+constexpr int MG_UNROLL = 4;
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ ws_o,
-                                                           const float* __restrict__ ws_ml,
-                                                           const int32_t* __restrict__ seqlens,
-                                                           uint16_t* __restrict__ o, int Hq,
-                                                           int max_len, int T, int NC, float c) {
+__global__ __launch_bounds__(MG_NW * 64) void decode_merge_kernel(const float* __restrict__ ws_o,
+                                                                 const float* __restrict__ ws_ml,
+                                                                 const int32_t* __restrict__ seqlens,
+                                                                 uint16_t* __restrict__ o, int Hq,
+                                                                 int max_len, int T, int NC, float c) {
     constexpr int EPL = D / 64;  // output dims per lane
-    __shared__ float sm[4], sl[4];
-    __shared__ float so[4][D];
+    __shared__ float sm[MG_NW], sl[MG_NW];
+    __shared__ float so[MG_NW][D];
     const int h = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int len = min(max(seqlens[b], 0), max_len);
     const int nc = ceil_div(len, T);
     const size_t base = (size_t)(b * Hq + h) * NC;
 
+    // wave w folds chunks w, w + 16, ...; MG_UNROLL independent loads in flight
     float M = -INFINITY, L = 0.f, acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    for (int ch = w; ch < nc; ch += 4) {
-        const float mc = ws_ml[(base + ch) * 2], lc = ws_ml[(base + ch) * 2 + 1];
-        const float* const src = ws_o + (base + ch) * D + lane * EPL;
-        const float Mn = fmaxf(M, mc);
-        const float a = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((M - Mn) * c);
-        const float f = __builtin_amdgcn_exp2f((mc - Mn) * c);
-        L = L * a + lc * f;
+    for (int ch0 = w; ch0 < nc; ch0 += MG_NW * MG_UNROLL) {
+        float mc[MG_UNROLL], lc[MG_UNROLL], oc[MG_UNROLL][EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * a + f * src[e];
-        M = Mn;
+        for (int u = 0; u < MG_UNROLL; ++u) {
+            const int ch = ch0 + u * MG_NW;
+            mc[u] = -INFINITY;
+            lc[u] = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) oc[u][e] = 0.f;
+            if (ch < nc) {
+                mc[u] = ws_ml[(base + ch) * 2];
+                lc[u] = ws_ml[(base + ch) * 2 + 1];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) oc[u][e] = ws_o[(base + ch) * D + lane * EPL + e];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < MG_UNROLL; ++u) {
+            if (mc[u] == -INFINITY) continue;
+            const float Mn = fmaxf(M, mc[u]);
+            const float a = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((M - Mn) * c);
+            const float f = __builtin_amdgcn_exp2f((mc[u] - Mn) * c);
+            L = L * a + lc[u] * f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * a + f * oc[u][e];
+            M = Mn;
+        }
     }
     if (lane == 0) {
         sm[w] = M;
@@ -238,12 +277,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     for (int e = 0; e < EPL; ++e) so[w][lane * EPL + e] = acc[e];
     __syncthreads();
     if (w != 0) return;
-    float Mt = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < MG_NW; ++ww) Mt = fmaxf(Mt, sm[ww]);
     float Lt = 0.f, out[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) out[e] = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < MG_NW; ++ww) {
         const float f = (sm[ww] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sm[ww] - Mt) * c);
         Lt += f * sl[ww];
 #pragma unroll
@@ -276,7 +317,7 @@ hipError_t launch_decode_d(void* o, const void* q, const void* k_cache, const vo
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(Hq, B), dim3(256), 0, st, ws_o, ws_ml, seqlens,
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(Hq, B), dim3(MG_NW * 64), 0, st, ws_o, ws_ml, seqlens,
                        (uint16_t*)o, Hq, max_len, T, NC, c);
     return hipGetLastError();
 }

@@ -7,8 +7,10 @@
 // same operation in a compressed latent with small head dims (64 here).
 //
 // bf16 kernel design (flash-style, exact up to rounding):
-//  * One workgroup = 8 waves = HPW query heads of one KV group x a block of
-//    queries.  Each wave owns one head and 32 consecutive queries.  The K and V
+//  * One workgroup = 4 waves = HPW query heads of one KV group x a block of
+//    queries.  Each wave owns one head and 32 consecutive queries; two
+//    workgroups share a CU, and their independent barriers let one
+//    workgroup's matrix-core phase overlap the other's softmax.  The K and V
 //    tile (64 keys x D) is loaded once into LDS and serves every head of the
 //    workgroup, so a KV group's key/value bytes are fetched once per query block
 //    rather than once per query head.
@@ -16,12 +18,17 @@
 //    core: each lane ends up holding one query and 4 keys per 16x16 tile, so the
 //    softmax row statistics are per-lane scalars (plus a 4-lane reduction).
 //  * Online softmax in fp32 in the exp2 domain (scale * log2 e folded into one
-//    FMA per score); P is rounded to bf16 and fed straight from registers as the
+//    FMA per score).  The reference max moves only when a tile raises it by
+//    more than 2^8, so almost every tile skips rescaling O (the normalisation
+//    at the end is exact for any reference).  P is rounded to bf16 and fed
+//    straight from registers as the
 //    B operand of O^T = V^T P^T.  The A operand (V^T) comes from the row-major
 //    V tile through the LDS transpose read, so V is never transposed in memory.
 //  * K/V tiles are double-buffered through registers: the next tile's global
 //    loads are in flight while the current one is computed.  LDS rows are
-//    XOR-swizzled in 16-byte chunks to keep the operand reads conflict-free.
+//    XOR-swizzled in 16-byte chunks, with one permutation for K and another for
+//    V, each conflict-free for its read pattern; per-lane operand offsets are
+//    computed once, so the tile loop addresses LDS with immediate offsets.
 //  * Work order: heaviest (last) query blocks are dispatched first, and
 //    consecutive workgroup ids walk (batch, KV head) fastest so a KV group's
 //    blocks share an XCD (and its L2) when B*Hkv is a multiple of 8.
@@ -37,10 +44,19 @@ namespace attn {
 
 namespace {
 
+#ifndef ATTN_PF_WAVES
+#define ATTN_PF_WAVES 4
+#endif
 constexpr int PF_BN = 64;                 // keys per K/V tile
 constexpr int PF_QW = 32;                 // queries per wave
-constexpr int PF_NW = 8;                  // waves per workgroup
+constexpr int PF_NW = ATTN_PF_WAVES;      // waves per workgroup
 constexpr int PF_THREADS = PF_NW * 64;
+
+// Online-softmax running max is only moved when a tile's max exceeds it by more
+// than this many log2 units; until then the stale max is used as the reference
+// (probabilities up to 2^8, exact in the final normalisation) and the wave
+// skips rescaling O.
+constexpr float PF_RESCALE_LOG2 = 8.f;
 
 template <int D, int HPW>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
@@ -50,9 +66,11 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     constexpr int KSTEPS = D / 32;              // k-steps of S^T = K Q^T
     constexpr int DT = D / 16;                  // d tiles of O^T
     constexpr int QPB = (PF_NW / HPW) * PF_QW;  // queries per head per workgroup
-    constexpr int TILE_BYTES = PF_BN * D * 2;
+    constexpr int ROW = D * 2;                  // bytes per LDS row
+    constexpr int TILE_BYTES = PF_BN * ROW;
     constexpr int CPT = PF_BN * CH / PF_THREADS;  // 16-byte chunks per thread per tile
     static_assert(CPT >= 1 && (PF_BN * CH) % PF_THREADS == 0, "tile split");
+    static_assert(HPW <= PF_NW && PF_NW % HPW == 0, "one head per wave at most");
 
     __shared__ __attribute__((aligned(16))) char smem[2 * TILE_BYTES];
     char* const ks = smem;
@@ -88,6 +106,14 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         }
     }
 
+    // Per-lane LDS offsets, fixed for the whole loop: the K operand of k-step s
+    // (rows 16mt + lr add the constant 16mt * ROW) and the V operand of d tile dt.
+    int koff[KSTEPS], voff[DT];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) koff[s] = swz_k<D>(lr, 4 * s + lg);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) voff[dt] = v_frag_off<D>(dt, lane);
+
     u32x4_t kr[CPT], vr[CPT];
     auto load_tile = [&](int kv0) {
 #pragma unroll
@@ -121,8 +147,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
             const int ci = tid + u * PF_THREADS, r = ci / CH, cc = ci % CH;
-            *(u32x4_t*)(ks + swz<D>(r, cc)) = kr[u];
-            *(u32x4_t*)(vs + swz<D>(r, cc)) = vr[u];
+            *(u32x4_t*)(ks + swz_k<D>(r, cc)) = kr[u];
+            *(u32x4_t*)(vs + swz_v<D>(r, cc)) = vr[u];
         }
         __syncthreads();
         if (t + 1 < ntiles) load_tile(kv0 + PF_BN);
@@ -136,7 +162,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8_t a = *(const bf16x8_t*)(ks + swz<D>(16 * mt + lr, 4 * s + lg));
+                const bf16x8_t a = *(const bf16x8_t*)(ks + koff[s] + 16 * mt * ROW);
                 sacc[mt][0] = mfma16(a, qf[0][s], sacc[mt][0]);
                 sacc[mt][1] = mfma16(a, qf[1][s], sacc[mt][1]);
             }
@@ -145,6 +171,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         // ---- online softmax; lane holds query qw0 + 16n + lr and keys kv0 + 16mt + 4lg + i
         const bool diag = kv0 + PF_BN - 1 > qw0;
         bf16x8_t pf[2][2];
+        float alpha[2];
+        bool rescale = false;
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const int qi = qw0 + 16 * n + lr;
@@ -162,10 +190,13 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[mt][n][i]);
             mx = fmaxf(mx, xor_shfl(mx, 16));
             mx = fmaxf(mx, xor_shfl(mx, 32));
-            const float mnew = fmaxf(m_run[n], mx);
-            const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f((m_run[n] - mref) * c);
-            const float mc = mref * c;
+            // move the reference max only when the tile's max is well above it
+            const bool up = (mx - m_run[n]) * c > PF_RESCALE_LOG2;
+            const float mnew = up ? mx : m_run[n];
+            alpha[n] = up ? __builtin_amdgcn_exp2f((m_run[n] - mnew) * c) : 1.f;
+            rescale |= up;
+            m_run[n] = mnew;
+            const float mc = (mnew == -INFINITY) ? 0.f : mnew * c;
             float ls = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -175,10 +206,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                     sacc[mt][n][i] = p;
                     ls += p;
                 }
-            l_run[n] = l_run[n] * alpha + ls;
-            m_run[n] = mnew;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) oacc[dt][n] *= alpha;
+            l_run[n] = fmaf(l_run[n], alpha[n], ls);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 u32x4_t pw;
@@ -189,13 +217,20 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                 pf[n][kk] = __builtin_bit_cast(bf16x8_t, pw);
             }
         }
+        if (__any(rescale)) {  // wave-uniform: most tiles keep the reference max
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                oacc[dt][0] *= alpha[0];
+                oacc[dt][1] *= alpha[1];
+            }
+        }
 
         // ---- O^T += V^T P^T
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8_t a = v_frag<D>(vs, 32 * kk, 16 * dt, lane);
+                const bf16x8_t a = v_frag_at<D>(vs + voff[dt] + 32 * kk * ROW);
                 oacc[dt][0] = mfma16(a, pf[0][kk], oacc[dt][0]);
                 oacc[dt][1] = mfma16(a, pf[1][kk], oacc[dt][1]);
             }
@@ -316,12 +351,13 @@ hipError_t launch_bf16(void* o, const void* q, const void* k, const void* v, int
 template <int D>
 hipError_t launch_bf16_d(void* o, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
                          int S, float c, hipStream_t st) {
-    switch (largest_pow2_divisor(Hq / Hkv, PF_NW)) {
-        case 8: return launch_bf16<D, 8>(o, q, k, v, B, Hq, Hkv, S, c, st);
-        case 4: return launch_bf16<D, 4>(o, q, k, v, B, Hq, Hkv, S, c, st);
-        case 2: return launch_bf16<D, 2>(o, q, k, v, B, Hq, Hkv, S, c, st);
-        default: return launch_bf16<D, 1>(o, q, k, v, B, Hq, Hkv, S, c, st);
-    }
+    // heads per workgroup: the largest power of two dividing G, at most one per wave
+    const int hpw = largest_pow2_divisor(Hq / Hkv, PF_NW);
+    if constexpr (PF_NW >= 8)
+        if (hpw == 8) return launch_bf16<D, 8>(o, q, k, v, B, Hq, Hkv, S, c, st);
+    if (hpw >= 4) return launch_bf16<D, 4>(o, q, k, v, B, Hq, Hkv, S, c, st);
+    if (hpw == 2) return launch_bf16<D, 2>(o, q, k, v, B, Hq, Hkv, S, c, st);
+    return launch_bf16<D, 1>(o, q, k, v, B, Hq, Hkv, S, c, st);
 }
 
 template <int D>

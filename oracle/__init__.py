@@ -76,8 +76,15 @@ def _load():
             lib.oracle_round_bf16.restype = None
             lib.oracle_round_f32.argtypes = [P, P, ctypes.c_size_t]
             lib.oracle_round_f32.restype = None
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = i
             _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def _as_input(x: np.ndarray, dtype: str) -> np.ndarray:

@@ -33,6 +33,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* Element type of an input buffer. */
 enum { OR_F64 = 0, OR_F32 = 1, OR_BF16 = 2 };
@@ -49,6 +52,16 @@ static double load(const void *p, size_t i, int dt)
     float f;
     memcpy(&f, &w, sizeof f);
     return (double)f;
+}
+
+/* Threads an OpenMP parallel region of this library uses. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* ------------------------------------------------------------------ */
