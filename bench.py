@@ -86,24 +86,27 @@ def bench_decode(w, iters, warmup):
     from compressed_latent_causal_amd import workloads as wl
 
     q, kc, vc, lens = wl.make_decode(w, seed=0)
-    qd, kcd, vcd, ld = q.cuda().unsqueeze(2), kc.cuda(), vc.cuda(), lens.cuda()
+    qd, kcd, vcd, ld = q.cuda(), kc.cuda(), vc.cuda(), lens.cuda()
     del kc, vc
-    qr = torch.empty_like(qd)
     o = torch.empty(w.B, w.Hq, w.D, dtype=qd.dtype, device="cuda")
     ws = torch.empty(attn.decode_workspace_size(w.B, w.Hq, w.Hkv, w.S, w.D), dtype=torch.uint8,
                      device="cuda")
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # Reading 1 GiB between iterations evicts the KV cache from L2 and the
+    # memory-side cache with clean lines (a write flush would leave dirty lines
+    # whose write-back would then land inside the timed decode).
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
-        attn.rope(qd, w.theta, ld, pos_shift=-1, out=qr)
-        attn.decode(qr.squeeze(2), kcd, vcd, ld, max_len=w.S, scale=w.scale, out=o, workspace=ws)
+    def step():  # RoPE of the new query is fused into the split pass
+        attn.decode(qd, kcd, vcd, ld, max_len=w.S, scale=w.scale, rope_theta=w.theta, out=o,
+                    workspace=ws)
 
     for _ in range(warmup):
         step()
     ms = []
     for _ in range(iters):
-        flush.zero_()  # evict L2 / MALL: every iteration reads the cache from HBM
+        flush.sum()  # evict L2 / MALL: every iteration reads the cache from HBM
+        torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         step()
@@ -118,7 +121,7 @@ def bench_decode(w, iters, warmup):
             "head_dim": w.D, "cache_capacity": w.S, "sum_len": int(lens.sum()),
             "kv_bytes": nbytes, "ms_median": round(med, 5), "ms_min": round(ms[0], 5),
             "GB_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "iters": iters, "step": "rope(q at len-1) + split + merge"}
+            "iters": iters, "step": "split (with q RoPE at len-1) + merge"}
 
 
 def cpu_baseline(w, budget_s=15.0):

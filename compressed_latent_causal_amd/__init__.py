@@ -7,7 +7,8 @@ fallback: calling into the library without the built ``libattn.so`` raises.
 
     rope(x, theta, pos_offset=None, pos_shift=0, out=None)
     prefill(q, k, v, scale=None, out=None)
-    decode(q, k_cache, v_cache, seqlens, max_len=None, scale=None, out=None, workspace=None)
+    decode(q, k_cache, v_cache, seqlens, max_len=None, scale=None, rope_theta=0.0, out=None,
+           workspace=None)
     decode_workspace_size(B, Hq, Hkv, max_len, D)
 
 Shapes follow the C ABI: x [B,H,S,D]; q/o [B,Hq,S,D], k/v [B,Hkv,S,D];
@@ -105,12 +106,14 @@ def decode_workspace_size(B: int, Hq: int, Hkv: int, max_len: int, D: int) -> in
 
 
 def decode(q, k_cache, v_cache, seqlens, max_len: int | None = None, scale: float | None = None,
-           out=None, workspace=None):
+           rope_theta: float = 0.0, out=None, workspace=None):
     """One query token per sequence over a contiguous cache.
 
     q [B,Hq,D]; caches [B,Hkv,S_cap,D]; seqlens device int32 [B] with
     0 <= seqlens[b] <= max_len <= S_cap (max_len defaults to S_cap, which needs
-    no host synchronisation).  Returns [B,Hq,D]."""
+    no host synchronisation).  rope_theta > 0 rotates q at position
+    seqlens[b] - 1 inside the kernel; 0 takes q as already rotated.
+    Returns [B,Hq,D]."""
     torch = _torch()
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("q must be [B,Hq,D] and caches [B,Hkv,S_cap,D]")
@@ -132,6 +135,6 @@ def decode(q, k_cache, v_cache, seqlens, max_len: int | None = None, scale: floa
     _check_dev(q, k_cache, v_cache, seqlens, out, workspace)
     _call(lib().attn_decode, out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
           v_cache.data_ptr(), _dtype_code(q), B, Hq, Hkv, S_cap, D, seqlens.data_ptr(),
-          int(max_len), float(scale), workspace.data_ptr(),
+          int(max_len), float(scale), float(rope_theta), workspace.data_ptr(),
           workspace.numel() * workspace.element_size(), _stream(q))
     return out

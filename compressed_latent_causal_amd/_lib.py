@@ -26,7 +26,7 @@ SIGNATURES = {
     "attn_rope": (I, [P, P, I, I, I, I, I, P, I, D, P]),
     "attn_prefill": (I, [P, P, P, P, I, I, I, I, I, I, F, P]),
     "attn_decode_workspace_size": (SZ, [I, I, I, I, I]),
-    "attn_decode": (I, [P, P, P, P, I, I, I, I, I, I, P, I, F, P, SZ, P]),
+    "attn_decode": (I, [P, P, P, P, I, I, I, I, I, I, P, I, F, D, P, SZ, P]),
     "attn_status_string": (ctypes.c_char_p, [I]),
 }
 

@@ -55,11 +55,12 @@ ATTN_API size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, 
 
 ATTN_API int attn_decode(void* o, const void* q, const void* k_cache, const void* v_cache, int dtype,
                          int B, int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens,
-                         int max_len, float scale, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         int max_len, float scale, double rope_theta, void* workspace,
+                         size_t workspace_bytes, void* stream) {
     if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_cap < 1 || max_len < 0 || max_len > S_cap)
         return ATTN_ERR_SHAPE;
     if (dtype != ATTN_BF16 || !supported_dim(D) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
+    if (!(rope_theta >= 0.0) || !isfinite(rope_theta)) return ATTN_ERR_UNSUPPORTED;
     if (B > kMaxGridYZ || (long long)Hkv * ((Hq / Hkv + 15) / 16) > kMaxGridYZ) return ATTN_ERR_SHAPE;
     if (B == 0) return ATTN_OK;
     if (!o || !q || !k_cache || !v_cache || !seqlens) return ATTN_ERR_NULL;
@@ -70,7 +71,8 @@ ATTN_API int attn_decode(void* o, const void* q, const void* k_cache, const void
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
     return hip_status(attn::launch_decode(o, q, k_cache, v_cache, B, Hq, Hkv, S_cap, D, seqlens,
-                                          max_len, scale, workspace, (hipStream_t)stream));
+                                          max_len, scale, rope_theta, workspace,
+                                          (hipStream_t)stream));
 }
 
 ATTN_API const char* attn_status_string(int status) {
@@ -79,7 +81,7 @@ ATTN_API const char* attn_status_string(int status) {
         case ATTN_ERR_NULL: return "a required pointer is NULL";
         case ATTN_ERR_SHAPE: return "invalid sizes (negative, Hq % Hkv != 0, max_len > S_cap, or too large)";
         case ATTN_ERR_UNSUPPORTED:
-            return "unsupported argument (head dim not 64/128, dtype, theta or scale not positive, f32 decode)";
+            return "unsupported argument (head dim not 64/128, dtype, theta or scale out of range, f32 decode)";
         case ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
         case ATTN_ERR_HIP: return "kernel launch failed";

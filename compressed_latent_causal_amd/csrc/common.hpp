@@ -107,6 +107,35 @@ __device__ inline bf16x8_t v_frag_at(const char* p) {
     return __builtin_bit_cast(bf16x8_t, w);
 }
 
+// ---------------------------------------------------------------- RoPE
+// Rotary embedding of channel pair (2i, 2i+1) at integer position p by the
+// angle p * theta^(-2i/D).  The frequencies come from the host in double; the
+// angle and its reduction to [-pi, pi] are formed in double from the exact
+// position, sine and cosine of the reduced angle in fp32, and the rotation is
+// one product and one FMA per output.  Every kernel that applies RoPE uses
+// these two functions, so fused and stand-alone rotations agree bit for bit.
+constexpr int kMaxPairs = 64;  // D / 2 for D = 128
+
+struct RopeFreqs {
+    double f[kMaxPairs];  // theta^(-2i/D), i < D/2
+};
+
+__device__ inline void rope_cos_sin(long long p, double freq, float& cs, float& sn) {
+    const double two_pi_hi = 6.28318530717958623200;      // 2*pi rounded to double
+    const double two_pi_lo = 2.44929359829470635445e-16;  // 2*pi - two_pi_hi
+    const double ang = (double)p * freq;
+    const double k = rint(ang * 0.15915494309189533577);  // ang / (2 pi)
+    double r = fma(-k, two_pi_hi, ang);
+    r = fma(-k, two_pi_lo, r);
+    sincosf((float)r, &sn, &cs);
+}
+
+// (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos)
+__device__ inline void rope_rotate(float x0, float x1, float cs, float sn, float& y0, float& y1) {
+    y0 = fmaf(x0, cs, -x1 * sn);
+    y1 = fmaf(x0, sn, x1 * cs);
+}
+
 // ---------------------------------------------------------------- cross-lane
 __device__ inline float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
 

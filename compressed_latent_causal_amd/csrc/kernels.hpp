@@ -12,20 +12,25 @@ namespace attn {
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
+struct RopeFreqs;
+// theta^(-2i/D) for i < D/2, in double (host side)
+RopeFreqs rope_freqs(double theta, int D);
+
 hipError_t launch_rope(void* out, const void* in, int dtype, int B, int H, int S, int D,
                        const int32_t* pos_offset, int pos_shift, double theta, hipStream_t st);
 
 hipError_t launch_prefill(void* o, const void* q, const void* k, const void* v, int dtype, int B,
                           int Hq, int Hkv, int S, int D, float scale, hipStream_t st);
 
-// Decode key-chunk length (tokens per split workgroup) for these sizes.
-int decode_chunk_tokens(int B, int Hkv, int max_len);
-// Number of key chunks and workspace bytes for these sizes.
+// Split workgroups (partial results) per (sequence, KV head) and workspace
+// bytes for these sizes.
 int decode_num_chunks(int B, int Hkv, int max_len);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int D);
 
+// rope_theta > 0 rotates each query at position seqlens[b] - 1 on the fly;
+// rope_theta == 0 takes q as already rotated.
 hipError_t launch_decode(void* o, const void* q, const void* k_cache, const void* v_cache, int B,
                          int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens, int max_len,
-                         float scale, void* workspace, hipStream_t st);
+                         float scale, double rope_theta, void* workspace, hipStream_t st);
 
 }  // namespace attn

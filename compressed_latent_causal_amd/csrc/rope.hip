@@ -25,16 +25,10 @@ namespace attn {
 
 namespace {
 
-constexpr int kMaxPairs = 64;  // D / 2 for D = 128
-
-struct Freqs {
-    double f[kMaxPairs];  // theta^(-2i/D), i < D/2
-};
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_kernel(T* out, const T* in, int H, int S, int HB,
                                                    const int32_t* __restrict__ pos_offset,
-                                                   int pos_shift, Freqs fr) {
+                                                   int pos_shift, RopeFreqs fr) {
     constexpr int EPT = 16 / sizeof(T);  // elements per 16-byte chunk
     constexpr int PPT = EPT / 2;         // channel pairs per thread
     constexpr int CH = D / EPT;          // chunks per row
@@ -46,17 +40,9 @@ __global__ __launch_bounds__(256) void rope_kernel(T* out, const T* in, int H, i
     if (s >= S) return;
 
     const long long p = (long long)(pos_offset ? pos_offset[b] : 0) + pos_shift + s;
-    const double two_pi_hi = 6.28318530717958623200;      // 2*pi rounded to double
-    const double two_pi_lo = 2.44929359829470635445e-16;  // 2*pi - two_pi_hi
     float cs[PPT], sn[PPT];
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-        const double ang = (double)p * fr.f[c * PPT + j];
-        const double k = rint(ang * 0.15915494309189533577);  // ang / (2 pi)
-        double r = fma(-k, two_pi_hi, ang);
-        r = fma(-k, two_pi_lo, r);
-        sincosf((float)r, &sn[j], &cs[j]);
-    }
+    for (int j = 0; j < PPT; ++j) rope_cos_sin(p, fr.f[c * PPT + j], cs[j], sn[j]);
 
     const size_t head_stride = (size_t)S * D;
     const size_t off = ((size_t)b * H * S + s) * D + (size_t)c * EPT;
@@ -76,16 +62,18 @@ __global__ __launch_bounds__(256) void rope_kernel(T* out, const T* in, int H, i
             if constexpr (sizeof(T) == 2) {
 #pragma unroll
                 for (int j = 0; j < PPT; ++j) {
-                    const float x0 = bf16_lo(x[u][j]), x1 = bf16_hi(x[u][j]);
-                    y[j] = pack_bf16x2(fmaf(x0, cs[j], -x1 * sn[j]), fmaf(x0, sn[j], x1 * cs[j]));
+                    float y0, y1;
+                    rope_rotate(bf16_lo(x[u][j]), bf16_hi(x[u][j]), cs[j], sn[j], y0, y1);
+                    y[j] = pack_bf16x2(y0, y1);
                 }
             } else {
 #pragma unroll
                 for (int j = 0; j < PPT; ++j) {
-                    const float x0 = __uint_as_float(x[u][2 * j]);
-                    const float x1 = __uint_as_float(x[u][2 * j + 1]);
-                    y[2 * j] = __float_as_uint(fmaf(x0, cs[j], -x1 * sn[j]));
-                    y[2 * j + 1] = __float_as_uint(fmaf(x0, sn[j], x1 * cs[j]));
+                    float y0, y1;
+                    rope_rotate(__uint_as_float(x[u][2 * j]), __uint_as_float(x[u][2 * j + 1]),
+                                cs[j], sn[j], y0, y1);
+                    y[2 * j] = __float_as_uint(y0);
+                    y[2 * j + 1] = __float_as_uint(y1);
                 }
             }
             *(u32x4_t*)(out + off + (size_t)(h0 + u) * head_stride) = y;
@@ -97,8 +85,7 @@ template <typename T, int D>
 hipError_t launch_rope_t(void* out, const void* in, int B, int H, int S, const int32_t* pos_offset,
                          int pos_shift, double theta, hipStream_t st) {
     constexpr int TS = 256 / (D / (16 / sizeof(T)));
-    Freqs fr;
-    for (int i = 0; i < D / 2; ++i) fr.f[i] = pow(theta, -2.0 * i / D);
+    const RopeFreqs fr = rope_freqs(theta, D);
     // Heads per workgroup: all of them when the token blocks alone fill the
     // chip (the angles are then formed once per token), fewer for short inputs
     // such as a decode step's single token.
@@ -113,6 +100,12 @@ hipError_t launch_rope_t(void* out, const void* in, int B, int H, int S, const i
 }
 
 }  // namespace
+
+RopeFreqs rope_freqs(double theta, int D) {
+    RopeFreqs fr{};
+    for (int i = 0; i < D / 2; ++i) fr.f[i] = pow(theta, -2.0 * i / D);
+    return fr;
+}
 
 hipError_t launch_rope(void* out, const void* in, int dtype, int B, int H, int S, int D,
                        const int32_t* pos_offset, int pos_shift, double theta, hipStream_t st) {

@@ -52,7 +52,7 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
     ATTN_ERR_SHAPE = 2,        /* negative size, Hq/Hkv < 1, Hq % Hkv != 0, max_len > S_cap, ... */
-    ATTN_ERR_UNSUPPORTED = 3,  /* D not 64/128, unknown dtype, theta <= 0, f32 decode */
+    ATTN_ERR_UNSUPPORTED = 3,  /* D not 64/128, unknown dtype, theta/scale out of range, f32 decode */
     ATTN_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_WORKSPACE = 5,    /* decode workspace missing or too small */
     ATTN_ERR_HIP = 6           /* a kernel launch failed */
@@ -90,15 +90,16 @@ int attn_rope(void *out, const void *in, int dtype, int B, int H, int S, int D,
  * keys 0..i).  bf16 inputs use bf16 matrix-core products with fp32
  * accumulation and an fp32 softmax; the probabilities are rounded to bf16
  * before the product with V.  fp32 inputs are computed in fp32 throughout.
- * o must not overlap q, k or v.  scale: usually 1/sqrt(D).
+ * o must not overlap q, k or v.  scale > 0 and finite, usually 1/sqrt(D).
  */
 int attn_prefill(void *o, const void *q, const void *k, const void *v, int dtype,
                  int B, int Hq, int Hkv, int S, int D, float scale, void *stream);
 
 /*
  * Bytes of device workspace attn_decode needs for these sizes (0 on invalid
- * sizes).  The workspace holds one fp32 partial result per (sequence, query
- * head, key chunk); chunking depends only on B, Hkv and max_len.
+ * sizes).  The workspace holds fp32 partial results (D + 2 floats) per
+ * (sequence, query head, split workgroup); the number of split workgroups of
+ * a sequence depends only on its length, so max_len bounds it.
  */
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D);
 
@@ -114,14 +115,19 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D);
  * hold anything, NaN included).  A sequence with seqlens[b] == 0 gets a zero
  * row.  Out-of-contract lengths are clamped to [0, max_len] on the device.
  * max_len <= S_cap is a host-side upper bound of the lengths.
+ * rope_theta > 0: q is taken unrotated and each sequence's query is rotated
+ * on the fly at position seqlens[b] - 1 (bit for bit what attn_rope with
+ * pos_offset = seqlens, pos_shift = -1 produces); rope_theta == 0: q is used
+ * as given (already rotated).  The cache holds keys already rotated.
  * workspace: device buffer of at least attn_decode_workspace_size(...) bytes,
  * 16-byte aligned; its contents on entry do not matter.  dtype: BF16 only.
- * Two kernels are enqueued: a split pass over key chunks and a merge pass.
+ * scale > 0 and finite.  Two kernels are enqueued: a split pass over key
+ * chunks and a merge pass.
  */
 int attn_decode(void *o, const void *q, const void *k_cache, const void *v_cache, int dtype,
                 int B, int Hq, int Hkv, int S_cap, int D, const int32_t *seqlens,
-                int max_len, float scale, void *workspace, size_t workspace_bytes,
-                void *stream);
+                int max_len, float scale, double rope_theta, void *workspace,
+                size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *attn_status_string(int status);

@@ -124,8 +124,8 @@ def test_decode_validation(L):
         return [kw.get("o", FAKE), kw.get("q", FAKE), kw.get("kc", FAKE), kw.get("vc", FAKE),
                 kw.get("dt", BF16), kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 2),
                 kw.get("S_cap", 64), kw.get("D", 128), kw.get("lens", FAKE),
-                kw.get("max_len", 64), kw.get("scale", 0.088), kw.get("ws", FAKE),
-                kw.get("ws_bytes", big), None]
+                kw.get("max_len", 64), kw.get("scale", 0.088), kw.get("theta", 0.0),
+                kw.get("ws", FAKE), kw.get("ws_bytes", big), None]
 
     assert d(*args(Hkv=3)) == ESHAPE
     assert d(*args(max_len=65)) == ESHAPE
@@ -134,6 +134,8 @@ def test_decode_validation(L):
     assert d(*args(dt=F32)) == EUNSUP
     assert d(*args(D=80)) == EUNSUP
     assert d(*args(scale=0.0)) == EUNSUP
+    assert d(*args(theta=-1.0)) == EUNSUP
+    assert d(*args(theta=float("nan"))) == EUNSUP
     for name in ("o", "q", "kc", "vc", "lens"):
         assert d(*args(**{name: None})) == ENULL
     for name in ("o", "q", "kc", "vc"):

@@ -315,16 +315,31 @@ def test_prefill_full_size_sampled_rows(name):
 
 # ============================================================== decode
 def _decode_e2e(w, seed, poison=True, max_len=None):
+    """Decode with the query's RoPE fused into the kernel (rope_theta), against
+    the oracle pipeline: RoPE of q at position len - 1 in fp64, rounded to bf16,
+    then decode in fp64."""
     q, kc, vc, lens = wl.make_decode(w, seed=seed, poison_tail=poison)
     say(f"decode {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} S_cap={w.S} D={w.D} "
         f"lens {int(lens.min())}..{int(lens.max())}")
-    ld = dev(lens)
-    qr = attn.rope(dev(q).unsqueeze(2), w.theta, ld, pos_shift=-1).squeeze(2)
-    o = attn.decode(qr, dev(kc), dev(vc), ld, max_len=max_len, scale=w.scale)
+    o = attn.decode(dev(q), dev(kc), dev(vc), dev(lens), max_len=max_len, scale=w.scale,
+                    rope_theta=w.theta)
     torch.cuda.synchronize()
     rq = oracle.round_bf16(oracle.rope(bits(q)[:, :, None, :], w.theta, lens.numpy() - 1))[:, :, 0]
     ref = oracle.decode(rq, bits(kc), bits(vc), lens.numpy(), scale=w.scale)
     return host_f64(o), ref
+
+
+def test_decode_fused_rope_equals_separate_rope():
+    """rope_theta > 0 rotates q in the split kernel exactly as attn_rope does."""
+    B, Hq, Hkv, S_cap, D = 5, 16, 2, 700, 128
+    q, kc, vc = rand_bf16((B, Hq, D), 40), rand_bf16((B, Hkv, S_cap, D), 41), rand_bf16((B, Hkv, S_cap, D), 42)
+    lens = torch.tensor([700, 1, 333, 64, 0], dtype=torch.int32)
+    say("decode fused vs separate RoPE")
+    ld = dev(lens)
+    qr = attn.rope(dev(q).unsqueeze(2), 5e5, ld, pos_shift=-1).squeeze(2)
+    sep = attn.decode(qr, dev(kc), dev(vc), ld)
+    fused = attn.decode(dev(q), dev(kc), dev(vc), ld, rope_theta=5e5)
+    assert torch.equal(sep, fused)
 
 
 @pytest.mark.parametrize("name", ["gqa_decode", "long_decode"])
