@@ -41,6 +41,8 @@ ATTN_API int attn_prefill(void* o, const void* q, const void* k, const void* v, 
     if (B == 0 || S == 0) return ATTN_OK;
     // one workgroup per (query block, batch, KV head, head slice): stay in a 32-bit grid
     if ((long long)B * Hq * ((S + 31) / 32) >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    // one head's keys (or values) are addressed with 32-bit byte offsets
+    if ((long long)S * D * (dtype == ATTN_BF16 ? 2 : 4) >= (1ll << 31)) return ATTN_ERR_SHAPE;
     if (!o || !q || !k || !v) return ATTN_ERR_NULL;
     if (!aligned16(o) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return ATTN_ERR_ALIGN;
     return hip_status(

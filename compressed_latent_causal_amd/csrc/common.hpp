@@ -139,4 +139,36 @@ __device__ inline void rope_rotate(float x0, float x1, float cs, float sn, float
 // ---------------------------------------------------------------- cross-lane
 __device__ inline float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (the lane groups that
+// share a row of a 16x16 matrix-core result) with the cross-row swap
+// instructions: each swap, given the same register twice, returns one copy
+// holding the lanes' own rows and one holding the partner rows.
+__device__ inline float group4_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float group4_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing, no stride).
+// Loads through it that fall past `bytes` return zeros instead of touching
+// memory.  The last word selects 32-bit data format, as raw loads require.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One wave-wide 16-byte-per-lane load from `rs` at byte voff + soff straight
+// into LDS: lane l's data lands at lds + 16 l (lds must be wave-uniform).
+__device__ __attribute__((always_inline)) inline void dma16(__amdgpu_buffer_rsrc_t rs, char* lds,
+                                                            int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+
 }  // namespace attn

@@ -24,11 +24,17 @@
 //    straight from registers as the
 //    B operand of O^T = V^T P^T.  The A operand (V^T) comes from the row-major
 //    V tile through the LDS transpose read, so V is never transposed in memory.
-//  * K/V tiles are double-buffered through registers: the next tile's global
-//    loads are in flight while the current one is computed.  LDS rows are
-//    XOR-swizzled in 16-byte chunks, with one permutation for K and another for
-//    V, each conflict-free for its read pattern; per-lane operand offsets are
-//    computed once, so the tile loop addresses LDS with immediate offsets.
+//  * K/V tiles are double-buffered in LDS and loaded with buffer loads that
+//    write LDS directly (no staging registers, no LDS store instructions, no
+//    address arithmetic per tile: the tile start is a scalar offset).  The
+//    load of tile t + 1 is issued right after the barrier that opens tile t
+//    and lands while tile t is computed.  LDS rows are XOR-swizzled in
+//    16-byte chunks, with one permutation for K and another for V, each
+//    conflict-free for its read pattern; the swizzle is applied by choosing
+//    each lane's source chunk.  Per-lane operand offsets are computed once, so
+//    the tile loop addresses LDS with immediate offsets.
+//  * Row statistics are combined across the four lanes that share a query
+//    with the cross-row lane swap instructions, not through LDS.
 //  * Work order: heaviest (last) query blocks are dispatched first, and
 //    consecutive workgroup ids walk (batch, KV head) fastest so a KV group's
 //    blocks share an XCD (and its L2) when B*Hkv is a multiple of 8.
@@ -62,19 +68,22 @@ template <int D, int HPW>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, int B, int Hq, int Hkv, int S, float c, int n_qblk, int n_hchunk) {
-    constexpr int CH = D / 8;                   // 16-byte chunks per row
     constexpr int KSTEPS = D / 32;              // k-steps of S^T = K Q^T
     constexpr int DT = D / 16;                  // d tiles of O^T
     constexpr int QPB = (PF_NW / HPW) * PF_QW;  // queries per head per workgroup
     constexpr int ROW = D * 2;                  // bytes per LDS row
-    constexpr int TILE_BYTES = PF_BN * ROW;
-    constexpr int CPT = PF_BN * CH / PF_THREADS;  // 16-byte chunks per thread per tile
-    static_assert(CPT >= 1 && (PF_BN * CH) % PF_THREADS == 0, "tile split");
+    constexpr int TILE = PF_BN * ROW;
+    constexpr int RPI = 1024 / ROW;             // rows per 1 KiB (one wave-wide 16-byte load)
+    constexpr int NI = TILE / 1024 / PF_NW;     // such loads per wave per tile, for K and for V
+    static_assert(NI >= 1 && TILE % (1024 * PF_NW) == 0, "tile split");
     static_assert(HPW <= PF_NW && PF_NW % HPW == 0, "one head per wave at most");
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * TILE_BYTES];
-    char* const ks = smem;
-    char* const vs = smem + TILE_BYTES;
+    // Two K and two V tile buffers as separate objects, so the compiler can
+    // tell the buffer being filled from the one being read.
+    __shared__ __attribute__((aligned(1024))) char k0[TILE];
+    __shared__ __attribute__((aligned(1024))) char k1[TILE];
+    __shared__ __attribute__((aligned(1024))) char v0[TILE];
+    __shared__ __attribute__((aligned(1024))) char v1[TILE];
 
     const int G = Hq / Hkv;
     const int per = B * Hkv * n_hchunk;
@@ -83,7 +92,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     const int bkv = rem % (B * Hkv), hc = rem / (B * Hkv);
     const int b = bkv / Hkv, kvh = bkv % Hkv;
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;  // row-in-tile / lane group
     const int h = kvh * G + hc * HPW + (w % HPW);
     const int q0 = qb * QPB;
@@ -114,25 +124,35 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) voff[dt] = v_frag_off<D>(dt, lane);
 
-    u32x4_t kr[CPT], vr[CPT];
-    auto load_tile = [&](int kv0) {
+    // Tiles go from global memory straight into LDS (buffer loads with the LDS
+    // destination: no registers, no LDS store instructions).  Such a load puts
+    // lane l's 16 bytes at byte 16 l of a 1 KiB destination, so the swizzled
+    // layout is produced by choosing the source: the lane landing on physical
+    // chunk p of row r fetches logical chunk p ^ f(r) (each swizzle is an
+    // XOR, its own inverse).  Offsets are relative to the tile's first row;
+    // the tile start is the scalar offset.  Rows past the sequence fall outside
+    // the buffer resource and arrive as zeros (those keys are masked anyway).
+    int kvo[NI], vvo[NI];
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int ci = tid + u * PF_THREADS, r = ci / CH, cc = ci % CH;
-            const int key = kv0 + r;
-            if (key < S) {
-                kr[u] = *(const u32x4_t*)(kg + (size_t)key * D + cc * 8);
-                vr[u] = *(const u32x4_t*)(vg + (size_t)key * D + cc * 8);
-            } else {
-                kr[u] = u32x4_t{0, 0, 0, 0};
-                vr[u] = u32x4_t{0, 0, 0, 0};
-            }
+    for (int i = 0; i < NI; ++i) {
+        const int r = (w * NI + i) * RPI + lane / (ROW / 16), pc = lane % (ROW / 16);
+        kvo[i] = r * ROW + ((swz_k<D>(r, pc) - r * ROW) & ~15);
+        vvo[i] = r * ROW + ((swz_v<D>(r, pc) - r * ROW) & ~15);
+    }
+    const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kg, S * ROW);
+    const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vg, S * ROW);
+    auto issue = [&](int t, char* kb, char* vb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            dma16(krs, kb + (w * NI + i) * 1024, kvo[i], t * TILE);
+            dma16(vrs, vb + (w * NI + i) * 1024, vvo[i], t * TILE);
         }
     };
 
     const int kv_end = min(q0 + QPB, S);
     const int ntiles = ceil_div(kv_end, PF_BN);
-    const bool active = qw0 < S;
+    // last tile this wave needs (-1: none, the wave's queries are all past S)
+    const int last = qw0 < S ? min(ntiles - 1, (qw0 + PF_QW - 1) / PF_BN) : -1;
 
     f32x4_t oacc[DT][2];
 #pragma unroll
@@ -140,20 +160,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     float m_run[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
 
-    load_tile(0);
-    for (int t = 0; t < ntiles; ++t) {
+    auto compute = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
         const int kv0 = t * PF_BN;
-        __syncthreads();  // everyone is done reading the previous tile
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int ci = tid + u * PF_THREADS, r = ci / CH, cc = ci % CH;
-            *(u32x4_t*)(ks + swz_k<D>(r, cc)) = kr[u];
-            *(u32x4_t*)(vs + swz_v<D>(r, cc)) = vr[u];
-        }
-        __syncthreads();
-        if (t + 1 < ntiles) load_tile(kv0 + PF_BN);
-        if (!active || kv0 > qw0 + PF_QW - 1) continue;  // whole tile in this wave's future
-
         // ---- S^T = K Q^T : tile mt covers keys kv0 + 16mt .. +15
         f32x4_t sacc[4][2];
 #pragma unroll
@@ -169,27 +177,28 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         }
 
         // ---- online softmax; lane holds query qw0 + 16n + lr and keys kv0 + 16mt + 4lg + i
-        const bool diag = kv0 + PF_BN - 1 > qw0;
+        if (t == last && kv0 + PF_BN - 1 > qw0) {  // the diagonal tile: mask future keys
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int lim = qw0 + 16 * n + lr - kv0 - 4 * lg;  // key offsets above lim are masked
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * mt + i > lim) sacc[mt][n][i] = -INFINITY;
+            }
+        }
         bf16x8_t pf[2][2];
         float alpha[2];
         bool rescale = false;
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-            const int qi = qw0 + 16 * n + lr;
-            if (diag) {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (kv0 + 16 * mt + 4 * lg + i > qi) sacc[mt][n][i] = -INFINITY;
-            }
             float mx = sacc[0][n][0];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[mt][n][i]);
-            mx = fmaxf(mx, xor_shfl(mx, 16));
-            mx = fmaxf(mx, xor_shfl(mx, 32));
+            mx = group4_max(mx);
             // move the reference max only when the tile's max is well above it
             const bool up = (mx - m_run[n]) * c > PF_RESCALE_LOG2;
             const float mnew = up ? mx : m_run[n];
@@ -235,14 +244,32 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                 oacc[dt][1] = mfma16(a, pf[1][kk], oacc[dt][1]);
             }
         }
+    };
+
+    // Tile t sits in buffer t & 1.  Each step waits for its own share of tile
+    // t, meets the other waves (so all of tile t has landed and everyone has
+    // finished reading tile t - 1), starts loading tile t + 1 into the buffer
+    // tile t - 1 used, and computes on tile t while that load is in flight.
+    auto step = [&](int t, const char* ks, const char* vs, char* kn, char* vn)
+                    __attribute__((always_inline)) {
+        // vmcnt(0) lgkmcnt(0) (expcnt left alone), as the builtin so the
+        // compiler's own wait bookkeeping sees it
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+        if (t + 1 < ntiles) issue(t + 1, kn, vn);
+        if (t <= last) compute(t, ks, vs);
+    };
+    issue(0, k0, v0);
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, k0, v0, k1, v1);
+        if (t + 1 >= ntiles) break;
+        step(t + 1, k1, v1, k0, v0);
     }
 
     // ---- epilogue: O = O^T / l, lane holds query qw0 + 16n + lr, dims 16dt + 4lg .. +3
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-        float lt = l_run[n];
-        lt += xor_shfl(lt, 16);
-        lt += xor_shfl(lt, 32);
+        const float lt = group4_sum(l_run[n]);
         const int qi = qw0 + 16 * n + lr;
         if (qi >= S) continue;
         const float inv = 1.f / lt;

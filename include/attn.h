@@ -91,6 +91,8 @@ int attn_rope(void *out, const void *in, int dtype, int B, int H, int S, int D,
  * accumulation and an fp32 softmax; the probabilities are rounded to bf16
  * before the product with V.  fp32 inputs are computed in fp32 throughout.
  * o must not overlap q, k or v.  scale > 0 and finite, usually 1/sqrt(D).
+ * One head's keys must span less than 2 GiB (S * D * element size < 2^31),
+ * else ATTN_ERR_SHAPE.
  */
 int attn_prefill(void *o, const void *q, const void *k, const void *v, int dtype,
                  int B, int Hq, int Hkv, int S, int D, float scale, void *stream);

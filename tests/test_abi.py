@@ -98,6 +98,8 @@ def test_prefill_validation(L):
         assert p(*args(**{name: None})) == ENULL
         assert p(*args(**{name: FAKE + 4})) == EALIGN
     assert p(*args(B=1 << 20, S=1 << 20)) == ESHAPE  # grid would overflow 32 bits
+    assert p(*args(B=1, Hq=1, Hkv=1, S=1 << 23, D=128)) == ESHAPE  # one head's K spans 2 GiB
+    assert p(*args(B=1, Hq=1, Hkv=1, S=1 << 23, D=128, dt=F32)) == ESHAPE
     assert p(*args(o=None, q=None, k=None, v=None, B=0)) == OK
     assert p(*args(o=None, q=None, k=None, v=None, S=0)) == OK
 
