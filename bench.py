@@ -29,6 +29,14 @@ if ROOT not in sys.path:
 METRIC = "prefill attention TFLOP/s & decode KV GB/s (1 MI355X, % of roofline)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COPY_BYTES = 256 << 20      # calibration copy: bytes read (and written) per launch
+
+# HBM traffic of the prefill kernel comes from rocprofv3 counter runs whose
+# summary is kept under profiles/; it is used only while the kernel source is
+# the one those counters were taken on.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "prefill_bf16_kernel_llama8b_prefill_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "compressed_latent_causal_amd", "csrc", f)
+                  for f in ("prefill.hip", "common.hpp")]
 
 
 def log(*a):
@@ -40,9 +48,70 @@ def prefill_flops(B, Hq, S, D):
     return 4.0 * B * Hq * D * (S * (S + 1) / 2)
 
 
+def min_prefill_bytes(w, elem_bytes=2):
+    """Compulsory HBM bytes of one prefill launch: read Q, K, V once, write O."""
+    return float(2 * w.B * w.Hq * w.S * w.D + 2 * w.B * w.Hkv * w.S * w.D) * elem_bytes
+
+
 def decode_bytes(lens, Hkv, D, elem_bytes=2):
     """Valid K and V cache bytes read for one token of every sequence."""
     return float(sum(int(n) for n in lens)) * Hkv * D * 2 * elem_bytes
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic():
+    """(bytes per launch, note) from the committed counter summary, or (None,
+    reason) when there is none or the kernel source changed since."""
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None, "no counter summary"
+    m_sha = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
+    m_b = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    if not (m_sha and m_b):
+        return None, "counter summary unreadable"
+    if m_sha.group(1) != kernel_source_digest():
+        return None, "kernel changed since the counters were taken"
+    return int(m_b.group(1)), os.path.relpath(TRAFFIC_PROFILE, ROOT)
+
+
+def settle(fn, seconds=1.0):
+    """Run `fn` untimed until the GPU has been busy for `seconds`: clocks ramp
+    up from idle over a fraction of a second, and the timed steps should see
+    the steady state."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
+def bench_copy(iters=20):
+    """Plain device copy of COPY_BYTES (the counter calibration kernel)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    settle(lambda: dst.copy_(src), 0.3)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    return {"workload": "copy", "bytes_read_per_launch": COPY_BYTES,
+            "bytes_written_per_launch": COPY_BYTES, "ms_mean": round(ms, 5),
+            "GB_per_s": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}
 
 
 # ---------------------------------------------------------------------------
@@ -66,6 +135,7 @@ def bench_prefill(w, steps, warmup):
         if ev is not None:
             ev[1].record(stream)
 
+    settle(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -127,9 +197,10 @@ def bench_decode(w, iters, warmup):
 def cpu_baseline(w, budget_s=15.0):
     """The oracle (fp64 C, OpenMP) on a random sample of output rows of the
     same prefill workload: RoPE of all keys and of the sampled queries, then
-    attention for those rows.  Rows are drawn uniformly, so their mean causal
-    length is that of the whole job; throughput is reported in TFLOP/s of the
-    same algorithmic count."""
+    attention for those rows.  Rows are drawn without repetition in random
+    order (so the sample's mean causal length is that of the whole job) until
+    the time budget is spent or every row is done; throughput is reported in
+    TFLOP/s of the same algorithmic count."""
     import numpy as np
     import oracle
     from compressed_latent_causal_amd import workloads as wl
@@ -137,13 +208,16 @@ def cpu_baseline(w, budget_s=15.0):
     q, k, v = wl.make_prefill(w, seed=0)
     qb, kb, vb = (wl.to_numpy_bits(t) for t in (q, k, v))
     rng = np.random.default_rng(0)
+    n_total = w.B * w.Hq * w.S
+    order = rng.permutation(n_total)  # rows without repetition, in random order
     n_rows, flops, elapsed = 0, 0.0, 0.0
     batch = 64
-    rq_full = np.zeros((w.B * w.Hq * w.S, w.D), dtype=np.uint16)
+    rq_full = np.zeros((n_total, w.D), dtype=np.uint16)
     t_start = time.perf_counter()
     rk = oracle.round_bf16(oracle.rope(kb, w.theta))
-    while elapsed < budget_s:
-        rows = rng.integers(0, w.B * w.Hq * w.S, batch)
+    while elapsed < budget_s and n_rows < n_total:
+        rows = order[n_rows:n_rows + batch]
+        batch = len(rows)
         qsel = qb.reshape(-1, w.D)[rows].reshape(-1, 1, 1, w.D)
         rq = oracle.round_bf16(oracle.rope(qsel, w.theta, (rows % w.S).astype(np.int32)))
         rq_full[rows] = rq.reshape(-1, w.D)
@@ -154,7 +228,7 @@ def cpu_baseline(w, budget_s=15.0):
         batch = min(batch * 2, 4096)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{n_rows} uniformly drawn output rows of {w.name} (of {w.B * w.Hq * w.S}), "
+            "sample": f"{n_rows} randomly drawn distinct output rows of {w.name} (of {n_total}), "
                       f"RoPE of all keys included, {elapsed:.1f} s wall"}
 
 
@@ -167,8 +241,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "gqa_decode", "long_decode", "ccgqa_prefill"],
-                    help="time one workload alone and print its line (profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "gqa_decode", "long_decode", "ccgqa_prefill", "copy"],
+                    help="time one workload alone and print its line (profiling runs; `copy` is "
+                         "the plain copy that calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the attention path is built and timed on a single "
@@ -183,6 +258,9 @@ def main():
         sys.exit("bench.py needs a GPU")
     attn.lib()
 
+    if args.only == "copy":
+        print(json.dumps(bench_copy()), flush=True)
+        return
     if args.only in ("gqa_decode", "long_decode"):
         d = bench_decode(wl.WORKLOADS[args.only], args.decode_iters, args.warmup)
         print(json.dumps(d), flush=True)
@@ -210,6 +288,12 @@ def main():
                      "traffic": None, "kernel_ms_mean": round(ms_kern, 5),
                      "flop_per_launch": flops},
     }
+    if w.name == "llama8b_prefill":
+        traffic, note = profiled_traffic()
+        result["roofline"]["traffic"] = traffic
+        result["roofline"]["traffic_source"] = note
+        if traffic:
+            result["roofline"]["traffic_over_min_bytes"] = round(traffic / min_prefill_bytes(w), 3)
     if args.only:
         print(json.dumps(result), flush=True)
         return
