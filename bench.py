@@ -9,9 +9,10 @@ causal GQA attention.  `value` is algorithmic prefill TFLOP/s over the whole
 step (4*B*Hq*D*S(S+1)/2 flops: QK^T and PV over unmasked pairs only), inputs
 resident in HBM.  The `roofline` object prices the prefill kernel alone, timed
 with HIP events on the stream it runs on.  The `decode` object reports KV-cache
-GB/s of the two decode workloads (split + merge, a cache flush between
-iterations), and `cpu_baseline` times the fp64 CPU oracle on a bounded sample
-of the same prefill workload.  Prints one JSON line on stdout.
+GB/s of the two decode workloads (one decode step over several layers' caches
+back to back, caches evicted before each timed step), and `cpu_baseline` times
+the fp64 CPU oracle on a bounded sample of the same prefill workload.  Prints
+one JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -150,48 +151,60 @@ def bench_prefill(w, steps, warmup):
     return wall * 1e3 / steps, sum(kern_ms) / len(kern_ms), sorted(kern_ms)
 
 
-def bench_decode(w, iters, warmup):
+def bench_decode(w, iters, warmup, layers):
+    """One decode step of a `layers`-layer model: the same call on `layers`
+    distinct KV caches back to back (as a serving step walks its layers), the
+    whole group timed with HIP events.  Together the caches far exceed the
+    L2 and memory-side caches, and a 1 GiB read before every timed group evicts
+    them too, so every layer reads its cache from HBM."""
     import torch
     import compressed_latent_causal_amd as attn
     from compressed_latent_causal_amd import workloads as wl
 
     q, kc, vc, lens = wl.make_decode(w, seed=0)
-    qd, kcd, vcd, ld = q.cuda(), kc.cuda(), vc.cuda(), lens.cuda()
+    qd, ld = q.cuda(), lens.cuda()
+    kcs = [kc.cuda() for _ in range(layers)]  # same values, distinct memory
+    vcs = [vc.cuda() for _ in range(layers)]
     del kc, vc
     o = torch.empty(w.B, w.Hq, w.D, dtype=qd.dtype, device="cuda")
     ws = torch.empty(attn.decode_workspace_size(w.B, w.Hq, w.Hkv, w.S, w.D), dtype=torch.uint8,
                      device="cuda")
-    # Reading 1 GiB between iterations evicts the KV cache from L2 and the
-    # memory-side cache with clean lines (a write flush would leave dirty lines
-    # whose write-back would then land inside the timed decode).
+    # Reading 1 GiB evicts the caches with clean lines (a write flush would
+    # leave dirty lines whose write-back would land inside the timed region).
     flush = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():  # RoPE of the new query is fused into the split pass
-        attn.decode(qd, kcd, vcd, ld, max_len=w.S, scale=w.scale, rope_theta=w.theta, out=o,
-                    workspace=ws)
+    def step():  # RoPE of the new query is fused into the decode kernel
+        for l in range(layers):
+            attn.decode(qd, kcs[l], vcs[l], ld, max_len=w.S, scale=w.scale, rope_theta=w.theta,
+                        out=o, workspace=ws)
 
+    settle(step, 0.5)
     for _ in range(warmup):
         step()
     ms = []
     for _ in range(iters):
-        flush.sum()  # evict L2 / MALL: every iteration reads the cache from HBM
+        flush.sum()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         step()
         b.record(stream)
         torch.cuda.synchronize()
-        ms.append(a.elapsed_time(b))
+        ms.append(a.elapsed_time(b) / layers)
     ms.sort()
     med = ms[len(ms) // 2]
     nbytes = decode_bytes(lens.tolist(), w.Hkv, w.D)
     gbs = nbytes / (med * 1e-3) / 1e9
     return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
             "head_dim": w.D, "cache_capacity": w.S, "sum_len": int(lens.sum()),
-            "kv_bytes": nbytes, "ms_median": round(med, 5), "ms_min": round(ms[0], 5),
-            "GB_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "iters": iters, "step": "split (with q RoPE at len-1) + merge"}
+            "kv_bytes_per_layer": nbytes, "layers": layers, "ms_per_layer_median": round(med, 5),
+            "ms_per_layer_min": round(ms[0], 5), "GB_per_s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "iters": iters,
+            "step": "one fused decode launch per layer (query RoPE at len-1, split-K, merge)"}
+
+
+DECODE_LAYERS = {"gqa_decode": 4, "long_decode": 8}  # 4 GiB of caches either way
 
 
 def cpu_baseline(w, budget_s=15.0):
@@ -262,7 +275,8 @@ def main():
         print(json.dumps(bench_copy()), flush=True)
         return
     if args.only in ("gqa_decode", "long_decode"):
-        d = bench_decode(wl.WORKLOADS[args.only], args.decode_iters, args.warmup)
+        d = bench_decode(wl.WORKLOADS[args.only], args.decode_iters, args.warmup,
+                         DECODE_LAYERS[args.only])
         print(json.dumps(d), flush=True)
         return
     w = wl.WORKLOADS["ccgqa_prefill" if args.only == "ccgqa_prefill" else "llama8b_prefill"]
@@ -300,8 +314,8 @@ def main():
     if not args.no_decode:
         dec = {}
         for name in ("gqa_decode", "long_decode"):
-            d = bench_decode(wl.WORKLOADS[name], args.decode_iters, 3)
-            log(f"decode {name}: {d['ms_median']:.4f} ms, {d['GB_per_s']:.0f} GB/s")
+            d = bench_decode(wl.WORKLOADS[name], args.decode_iters, 3, DECODE_LAYERS[name])
+            log(f"decode {name}: {d['ms_per_layer_median']:.4f} ms per layer, {d['GB_per_s']:.0f} GB/s")
             dec[name] = d
         result["decode"] = dec
     if not args.no_cpu_baseline:

@@ -24,11 +24,16 @@
 //     wave's own LDS slot and read back with the LDS transpose read as the A
 //     operand of O^T = V^T P^T, P taken from registers as bf16;
 //   * the softmax is online in fp32 (exp2 domain), one query head per lane.
-// The four waves then merge in LDS and write one unnormalised partial
-// (max, sum, o[D]) per (sequence, head, workgroup) to the fp32 workspace.
-// Merge pass: one workgroup per (head, sequence) combines the chunk partials
-// (log-sum-exp rescaling) and writes the bf16 output.  Cache slots at or past
-// a sequence's length are never loaded.
+// The four waves then merge in LDS.  A sequence with a single split workgroup
+// writes its bf16 output right there.  Otherwise each workgroup writes one
+// unnormalised partial (max, sum, o[D]) per head to the fp32 workspace and
+// tags it; a workgroup that finds every partial of its (sequence, KV head,
+// head slice) tagged by this call combines them (log-sum-exp rescaling) and
+// writes the output, so one launch does the whole step.  Cache slots at or past a
+// sequence's length are never loaded.
+#include <atomic>
+#include <chrono>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,6 +44,7 @@ namespace {
 constexpr int DC_NW = 4;      // waves per split workgroup
 constexpr int DC_SUB = 32;    // tokens per wave sub-tile
 constexpr int DC_HEADS = 16;  // query heads per split workgroup (MFMA N)
+constexpr int DC_MB = 256;    // partials per block of the last workgroup's merge
 
 #ifndef ATTN_DC_SUBS_PER_WAVE
 #define ATTN_DC_SUBS_PER_WAVE 32
@@ -53,19 +59,38 @@ __host__ __device__ inline int decode_partials(int len) {
     return ceil_div(ceil_div(len, DC_SUB), DC_SUBS_PER_WG);
 }
 
+// Device-coherent (agent-scope) float accesses for the split partials.
+__device__ inline void store_agent(float* p, float x) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline f32x4_t load4_agent(const float* p) {
+    // two 8-byte device-coherent loads (p is 16-byte aligned)
+    unsigned long long* const q = (unsigned long long*)const_cast<float*>(p);
+    const unsigned long long v0 = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long v1 = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x4_t{__uint_as_float((unsigned)v0), __uint_as_float((unsigned)(v0 >> 32)),
+                   __uint_as_float((unsigned)v1), __uint_as_float((unsigned)(v1 >> 32))};
+}
+
 template <int D>
 struct DecodeSmem {
     static constexpr int kStage = 2 * DC_NW * DC_SUB * D * 2;          // V staging, 2 slots per wave
     static constexpr int kOStride = D + 4;                             // padded row (floats)
     static constexpr int kMerge = (2 * DC_NW * DC_HEADS + DC_NW * DC_HEADS * kOStride) * 4;
-    static constexpr int kBytes = kStage > kMerge ? kStage : kMerge;
+    static constexpr int kFinal = (2 * DC_HEADS * DC_MB + 3 * DC_HEADS) * 4;  // last-workgroup merge
+    static constexpr int kMax2 = kStage > kMerge ? kStage : kMerge;
+    static constexpr int kBytes = kMax2 > kFinal ? kMax2 : kFinal;
 };
 
 template <int D>
 __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ seqlens, float* __restrict__ ws_o, float* __restrict__ ws_ml, int Hq,
-    int Hkv, int S_cap, int max_len, int NC, float c, int n_hchunk, int rope, RopeFreqs fr) {
+    const int32_t* __restrict__ seqlens, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    unsigned long long* __restrict__ ws_tag, uint16_t* __restrict__ o, int Hq, int Hkv, int S_cap,
+    int max_len, int NC, float c, int n_hchunk, int rope, RopeFreqs fr, unsigned long long tag) {
     constexpr int KSTEPS = D / 32, DT = D / 16;
     constexpr int ROW = D * 2;                 // bytes per cache row
     constexpr int VSUB = DC_SUB * ROW;         // bytes of one V sub-tile
@@ -80,8 +105,10 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     const int GH = min(DC_HEADS, G - hc * DC_HEADS);
     const int len = min(max(seqlens[b], 0), max_len);
     const int n_sub = ceil_div(len, DC_SUB);  // 32-token sub-tiles of this sequence
-    const int nwg = decode_partials(len);     // split workgroups of this sequence
-    if (chunk >= nwg) return;  // uniform: the merge pass never reads this partial
+    // split workgroups of this sequence (an empty one still gets one, which
+    // writes its zero rows)
+    const int nwg = max(1, decode_partials(len));
+    if (chunk >= nwg) return;  // uniform across the workgroup
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
@@ -243,6 +270,27 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     for (int dt = 0; dt < DT; ++dt)
         *(f32x4_t*)(co + (w * DC_HEADS + lr) * OS + 16 * dt + 4 * lg) = oacc[dt];
     __syncthreads();
+    if (nwg == 1) {
+        // the sequence's only workgroup: normalise and write the output here
+        for (int e = tid; e < GH * (D / 2); e += DC_NW * 64) {
+            const int hd = e / (D / 2), d = 2 * (e % (D / 2));
+            float M = -INFINITY;
+#pragma unroll
+            for (int ww = 0; ww < DC_NW; ++ww) M = fmaxf(M, cm[ww * DC_HEADS + hd]);
+            float L = 0.f, O0 = 0.f, O1 = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < DC_NW; ++ww) {
+                const float mw = cm[ww * DC_HEADS + hd];
+                const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * c);
+                L += f * cl[ww * DC_HEADS + hd];
+                O0 += f * co[(ww * DC_HEADS + hd) * OS + d];
+                O1 += f * co[(ww * DC_HEADS + hd) * OS + d + 1];
+            }
+            const float inv = L > 0.f ? 1.f / L : 0.f;  // L == 0 only for an empty sequence
+            *(unsigned*)(o + (size_t)(b * Hq + h0 + hd) * D + d) = pack_bf16x2(O0 * inv, O1 * inv);
+        }
+        return;
+    }
     for (int e = tid; e < GH * D; e += DC_NW * 64) {
         const int hd = e / D, d = e % D;
         float M = -INFINITY;
@@ -257,115 +305,161 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
             O += f * co[(ww * DC_HEADS + hd) * OS + d];
         }
         const size_t slot = (size_t)(b * Hq + h0 + hd) * NC + chunk;
-        ws_o[slot * D + d] = O;
+        store_agent(ws_o + slot * D + d, O);
         if (d == 0) {
-            ws_ml[slot * 2] = M;
-            ws_ml[slot * 2 + 1] = L;
+            store_agent(ws_ml + slot * 2, M);
+            store_agent(ws_ml + slot * 2 + 1, L);
         }
     }
-}
 
-constexpr int MG_NW = 16;  // waves per merge workgroup
-constexpr int MG_UNROLL = 8;
+    // ---- publish the partial, then look for the others.  Each partial slot of
+    // a (sequence, KV head, head slice) carries the tag of the call that wrote
+    // it, stored once the partial itself is complete.  A workgroup that, after
+    // its own tag store has completed, finds this call's tag in every slot
+    // merges all of them.  At least one workgroup always does: of two
+    // workgroups that finish together, the one whose tag store completes last
+    // sees the other's tag.  Two may both merge (identical results, written
+    // twice).  Slots written by other calls, or holding anything at all, carry
+    // another tag, so the workspace needs no clearing between calls.
+    // Partials and tags are written and read with device-coherent
+    // (agent-scope) accesses, which bypass the per-XCD L2's non-coherent
+    // lines: once such a store has completed it is visible to every CU, and no
+    // device-wide fence (an L2 write-back and invalidate, costly for the
+    // workgroups still streaming the cache) is needed.
+    unsigned long long* const tags =
+        ws_tag + (((size_t)b * Hkv + kvh) * (size_t)n_hchunk + (size_t)hc) * (size_t)NC;
+    __builtin_amdgcn_s_waitcnt(0x0070);  // this thread's partial stores completed
+    __syncthreads();
+    if (tid == 0) {
+        __hip_atomic_store(tags + chunk, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0x0070);  // the tag store completed
+    }
+    __syncthreads();
+    int mine = 1;
+    for (int ch = tid; ch < nwg; ch += DC_NW * 64)
+        mine &= __hip_atomic_load(tags + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+    if (!__syncthreads_and(mine)) return;
 
-template <int D>
-__global__ __launch_bounds__(MG_NW * 64) void decode_merge_kernel(const float* __restrict__ ws_o,
-                                                                 const float* __restrict__ ws_ml,
-                                                                 const int32_t* __restrict__ seqlens,
-                                                                 uint16_t* __restrict__ o, int Hq,
-                                                                 int max_len, int NC, float c) {
-    constexpr int EPL = D / 64;  // output dims per lane
-    __shared__ float sm[MG_NW], sl[MG_NW];
-    __shared__ float so[MG_NW][D];
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int len = min(max(seqlens[b], 0), max_len);
-    const int nc = decode_partials(len);  // partials the split pass wrote (<= NC)
-    const size_t base = (size_t)(b * Hq + h) * NC;
-
-    // wave w folds chunks w, w + 16, ...; MG_UNROLL independent loads in flight
-    float M = -INFINITY, L = 0.f, acc[EPL];
+    // ---- merge (log-sum-exp over the nwg partials).  Partials are taken in
+    // blocks of MB: the block's (max, sum) pairs are staged in LDS with one
+    // parallel load, each head's running max / factor / sum are updated there,
+    // and every thread folds the o vectors of its items (a head and 4
+    // consecutive dims each) with 16-byte loads, MU of them in flight.
+    constexpr int MB = DC_MB, MU = 8, EPI = 4;
+    constexpr int NITEM = DC_HEADS * D / EPI / (DC_NW * 64);  // items per thread, at most
+    float* const bm = (float*)smem;        // [DC_HEADS][MB] max, then factor
+    float* const bl = bm + DC_HEADS * MB;  // [DC_HEADS][MB] sum
+    float* const run = bl + DC_HEADS * MB;  // [DC_HEADS] running max, [DC_HEADS] alpha, [DC_HEADS] L
+    if (tid < DC_HEADS) {
+        run[tid] = -INFINITY;
+        run[2 * DC_HEADS + tid] = 0.f;
+    }
+    float acc[NITEM][EPI];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    for (int ch0 = w; ch0 < nc; ch0 += MG_NW * MG_UNROLL) {
-        float mc[MG_UNROLL], lc[MG_UNROLL], oc[MG_UNROLL][EPL];
+    for (int it = 0; it < NITEM; ++it)
 #pragma unroll
-        for (int u = 0; u < MG_UNROLL; ++u) {
-            const int ch = ch0 + u * MG_NW;
-            mc[u] = -INFINITY;
-            lc[u] = 0.f;
+        for (int e = 0; e < EPI; ++e) acc[it][e] = 0.f;
+    for (int c0 = 0; c0 < nwg; c0 += MB) {
+        const int nb = min(MB, nwg - c0);
+        __syncthreads();
+        for (int e = tid; e < GH * nb; e += DC_NW * 64) {
+            const int hd = e / nb, ch = e % nb;
+            const size_t sl = (size_t)(b * Hq + h0 + hd) * NC + c0 + ch;
+            bm[hd * MB + ch] = load_agent(ws_ml + sl * 2);
+            bl[hd * MB + ch] = load_agent(ws_ml + sl * 2 + 1);
+        }
+        __syncthreads();
+        for (int hd = w; hd < GH; hd += DC_NW) {  // per head: running max, rescale, factors, sum
+            const float mprev = run[hd];
+            float mx = mprev;
+            for (int ch = lane; ch < nb; ch += 64) mx = fmaxf(mx, bm[hd * MB + ch]);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) oc[u][e] = 0.f;
-            if (ch < nc) {
-                mc[u] = ws_ml[(base + ch) * 2];
-                lc[u] = ws_ml[(base + ch) * 2 + 1];
+            for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, xor_shfl(mx, sh));
+            const float mref = (mx == -INFINITY) ? 0.f : mx;
+            const float alpha = (mprev == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mprev - mref) * c);
+            float ls = 0.f;
+            for (int ch = lane; ch < nb; ch += 64) {
+                const float m = bm[hd * MB + ch];
+                const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mref) * c);
+                bm[hd * MB + ch] = f;
+                ls = fmaf(f, bl[hd * MB + ch], ls);
+            }
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) oc[u][e] = ws_o[(base + ch) * D + lane * EPL + e];
+            for (int sh = 32; sh >= 1; sh >>= 1) ls += xor_shfl(ls, sh);
+            if (lane == 0) {
+                run[hd] = mx;
+                run[DC_HEADS + hd] = alpha;
+                run[2 * DC_HEADS + hd] = fmaf(run[2 * DC_HEADS + hd], alpha, ls);
             }
         }
+        __syncthreads();
 #pragma unroll
-        for (int u = 0; u < MG_UNROLL; ++u) {
-            if (mc[u] == -INFINITY) continue;
-            const float Mn = fmaxf(M, mc[u]);
-            const float a = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((M - Mn) * c);
-            const float f = __builtin_amdgcn_exp2f((mc[u] - Mn) * c);
-            L = L * a + lc[u] * f;
+        for (int it = 0; it < NITEM; ++it) {
+            const int item = tid + it * DC_NW * 64;
+            if (item >= GH * (D / EPI)) break;
+            const int hd = item / (D / EPI), d = EPI * (item % (D / EPI));
+            const float alpha = run[DC_HEADS + hd];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * a + f * oc[u][e];
-            M = Mn;
+            for (int e = 0; e < EPI; ++e) acc[it][e] *= alpha;
+            const size_t sb = (size_t)(b * Hq + h0 + hd) * NC + c0;
+            for (int ch0 = 0; ch0 < nb; ch0 += MU) {
+                f32x4_t oc[MU];
+#pragma unroll
+                for (int u = 0; u < MU; ++u)
+                    oc[u] = (ch0 + u < nb) ? load4_agent(ws_o + (sb + ch0 + u) * D + d)
+                                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < MU; ++u) {
+                    const float f = (ch0 + u < nb) ? bm[hd * MB + ch0 + u] : 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPI; ++e) acc[it][e] = fmaf(f, oc[u][e], acc[it][e]);
+                }
+            }
         }
     }
-    if (lane == 0) {
-        sm[w] = M;
-        sl[w] = L;
-    }
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) so[w][lane * EPL + e] = acc[e];
-    __syncthreads();
-    if (w != 0) return;
-    float Mt = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < MG_NW; ++ww) Mt = fmaxf(Mt, sm[ww]);
-    float Lt = 0.f, out[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) out[e] = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < MG_NW; ++ww) {
-        const float f = (sm[ww] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sm[ww] - Mt) * c);
-        Lt += f * sl[ww];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) out[e] += f * so[ww][lane * EPL + e];
-    }
-    const float inv = (len > 0) ? 1.f / Lt : 0.f;
-    uint16_t* const dst = o + (size_t)(b * Hq + h) * D + lane * EPL;
-    if constexpr (EPL == 2) {
-        *(unsigned*)dst = pack_bf16x2(out[0] * inv, out[1] * inv);
-    } else {
-        dst[0] = (uint16_t)(pack_bf16x2(out[0] * inv, 0.f) & 0xffffu);
+    for (int it = 0; it < NITEM; ++it) {
+        const int item = tid + it * DC_NW * 64;
+        if (item >= GH * (D / EPI)) break;
+        const int hd = item / (D / EPI), d = EPI * (item % (D / EPI));
+        const float L = run[2 * DC_HEADS + hd];
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        u32x2_t wv;
+        wv[0] = pack_bf16x2(acc[it][0] * inv, acc[it][1] * inv);
+        wv[1] = pack_bf16x2(acc[it][2] * inv, acc[it][3] * inv);
+        *(u32x2_t*)(o + (size_t)(b * Hq + h0 + hd) * D + d) = wv;
     }
 }
 
 template <int D>
 hipError_t launch_decode_d(void* o, const void* q, const void* k_cache, const void* v_cache, int B,
                            int Hq, int Hkv, int S_cap, const int32_t* seqlens, int max_len, float c,
-                           double rope_theta, void* workspace, hipStream_t st) {
+                           double rope_theta, void* workspace, unsigned long long tag,
+                           hipStream_t st) {
     const int NC = decode_num_chunks(B, Hkv, max_len);
     const int G = Hq / Hkv;
     const int n_hchunk = ceil_div(G, DC_HEADS);
     float* const ws_o = (float*)workspace;
     float* const ws_ml = ws_o + (size_t)B * Hq * NC * D;
-    if (max_len > 0) {
-        hipLaunchKernelGGL((decode_split_kernel<D>), dim3(NC, Hkv * n_hchunk, B), dim3(DC_NW * 64), 0,
-                           st, (const uint16_t*)q, (const uint16_t*)k_cache,
-                           (const uint16_t*)v_cache, seqlens, ws_o, ws_ml, Hq, Hkv, S_cap, max_len,
-                           NC, c, n_hchunk, rope_theta > 0 ? 1 : 0,
-                           rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D));
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(Hq, B), dim3(MG_NW * 64), 0, st, ws_o, ws_ml, seqlens,
-                       (uint16_t*)o, Hq, max_len, NC, c);
+    unsigned long long* const ws_tag = (unsigned long long*)(ws_ml + (size_t)B * Hq * NC * 2);
+    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(NC, Hkv * n_hchunk, B), dim3(DC_NW * 64), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, seqlens,
+                       ws_o, ws_ml, ws_tag, (uint16_t*)o, Hq, Hkv, S_cap, max_len, NC, c, n_hchunk,
+                       rope_theta > 0 ? 1 : 0, rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D), tag);
     return hipGetLastError();
+}
+
+// Call tags for the partial slots: distinct for every call in the process
+// (40 bits, never zero), starting from a value that differs between processes.
+unsigned long long next_decode_tag() {
+    static std::atomic<unsigned long long> seq{
+        (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull};
+    constexpr unsigned long long kMask = (1ull << 40) - 1;
+    unsigned long long t;
+    do {
+        t = seq.fetch_add(1, std::memory_order_relaxed) & kMask;
+    } while (t == 0);
+    return t;
 }
 
 }  // namespace
@@ -376,18 +470,23 @@ int decode_num_chunks(int B, int Hkv, int max_len) {
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int D) {
+    // fp32 partials (o[D], max, sum) per (sequence, query head, split workgroup),
+    // then one 64-bit call tag per (sequence, KV head, head slice, split workgroup)
     const size_t NC = (size_t)decode_num_chunks(B, Hkv, max_len);
-    return (size_t)B * Hq * NC * (size_t)(D + 2) * sizeof(float);
+    const size_t n_hchunk = (size_t)ceil_div(Hq / Hkv, DC_HEADS);
+    return (size_t)B * Hq * NC * (size_t)(D + 2) * sizeof(float) +
+           (size_t)B * Hkv * n_hchunk * NC * sizeof(unsigned long long);
 }
 
 hipError_t launch_decode(void* o, const void* q, const void* k_cache, const void* v_cache, int B,
                          int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens, int max_len,
                          float scale, double rope_theta, void* workspace, hipStream_t st) {
     const float c = scale * kLog2e;
+    const unsigned long long tag = next_decode_tag();
     return D == 64 ? launch_decode_d<64>(o, q, k_cache, v_cache, B, Hq, Hkv, S_cap, seqlens, max_len,
-                                         c, rope_theta, workspace, st)
+                                         c, rope_theta, workspace, tag, st)
                    : launch_decode_d<128>(o, q, k_cache, v_cache, B, Hq, Hkv, S_cap, seqlens, max_len,
-                                          c, rope_theta, workspace, st);
+                                          c, rope_theta, workspace, tag, st);
 }
 
 }  // namespace attn

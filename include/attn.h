@@ -25,7 +25,8 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
  *    is enqueued on it; calls return without synchronising.  The caller keeps
  *    every buffer alive until that work completes.
- *  - The library allocates and frees nothing and keeps no state between calls;
+ *  - The library allocates and frees nothing and keeps no state between calls
+ *    (apart from a process-wide sequence number that tags each decode call);
  *    calls on different streams may run concurrently on distinct buffers.
  *  - Arguments are validated on the host before any HIP call.  On a non-zero
  *    status nothing was enqueued.  ATTN_ERR_HIP reports a failed launch (the
@@ -100,8 +101,10 @@ int attn_prefill(void *o, const void *q, const void *k, const void *v, int dtype
 /*
  * Bytes of device workspace attn_decode needs for these sizes (0 on invalid
  * sizes).  The workspace holds fp32 partial results (D + 2 floats) per
- * (sequence, query head, split workgroup); the number of split workgroups of
- * a sequence depends only on its length, so max_len bounds it.
+ * (sequence, query head, split workgroup) and one 64-bit call tag per
+ * (sequence, KV head, slice of up to 16 query heads, split workgroup); the
+ * number of split workgroups of a sequence depends only on its length, so
+ * max_len bounds it.
  */
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D);
 
@@ -122,9 +125,11 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D);
  * pos_offset = seqlens, pos_shift = -1 produces); rope_theta == 0: q is used
  * as given (already rotated).  The cache holds keys already rotated.
  * workspace: device buffer of at least attn_decode_workspace_size(...) bytes,
- * 16-byte aligned; its contents on entry do not matter.  dtype: BF16 only.
- * scale > 0 and finite.  Two kernels are enqueued: a split pass over key
- * chunks and a merge pass.
+ * 16-byte aligned; its contents on entry do not matter (each call tags the
+ * partial results it writes), and it must not be shared by calls that may
+ * overlap.  dtype: BF16 only.  scale > 0 and finite.  One kernel is enqueued:
+ * workgroups split each sequence's keys, and one that finds all partial
+ * results of its (sequence, KV head) written merges them.
  */
 int attn_decode(void *o, const void *q, const void *k_cache, const void *v_cache, int dtype,
                 int B, int Hq, int Hkv, int S_cap, int D, const int32_t *seqlens,

@@ -359,6 +359,11 @@ DECODE_CASES = [  # B, Hq, Hkv, S_cap, D, lengths
     (2, 64, 2, 100, 64, [100, 37]),               # G = 32: two head slices
     (2, 12, 4, 90, 128, [90, 45]),                # G = 3
     (1, 4, 1, 5000, 128, [4999]),
+    # several split workgroups per sequence (merged by the last one to finish)
+    # next to single-workgroup sequences in the same batch
+    (3, 16, 2, 20000, 64, [20000, 4097, 1]),
+    (2, 64, 2, 9000, 128, [9000, 8193]),          # two head slices, 3 partials each
+    (1, 2, 1, 1100000, 64, [1100000]),            # > 256 partials: blocked final merge
 ]
 
 
@@ -394,6 +399,32 @@ def test_decode_ignores_workspace_contents_and_default_max_len():
     assert torch.equal(o1, o2)
     ref = oracle.decode(bits(q), bits(kc), bits(vc), lens.numpy())
     assert_close(host_f64(o1), ref, BF16_MAX, BF16_MEAN, what="decode ws")
+
+
+def test_decode_reuses_a_workspace_across_calls():
+    """Completion counters left in the workspace by earlier calls (or any
+    bytes at all) must not disturb a later call, including one with other
+    lengths on the same buffer."""
+    B, Hq, Hkv, S_cap, D = 3, 16, 4, 12000, 128
+    q, kc, vc = rand_bf16((B, Hq, D), 50), rand_bf16((B, Hkv, S_cap, D), 51), rand_bf16((B, Hkv, S_cap, D), 52)
+    lens_a = torch.tensor([12000, 4500, 700], dtype=torch.int32)
+    lens_b = torch.tensor([9000, 12000, 4097], dtype=torch.int32)
+    need = attn.decode_workspace_size(B, Hq, Hkv, S_cap, D)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    say("decode workspace reuse")
+    qd, kd, vd = dev(q), dev(kc), dev(vc)
+    outs_a, outs_b = [], []
+    for _ in range(3):
+        outs_a.append(attn.decode(qd, kd, vd, dev(lens_a), max_len=S_cap, workspace=ws))
+        outs_b.append(attn.decode(qd, kd, vd, dev(lens_b), max_len=S_cap, workspace=ws))
+    for o in outs_a[1:]:
+        assert torch.equal(o, outs_a[0])
+    for o in outs_b[1:]:
+        assert torch.equal(o, outs_b[0])
+    ref_a = oracle.decode(bits(q), bits(kc), bits(vc), lens_a.numpy())
+    ref_b = oracle.decode(bits(q), bits(kc), bits(vc), lens_b.numpy())
+    assert_close(host_f64(outs_a[0]), ref_a, BF16_MAX, BF16_MEAN, what="decode reuse a")
+    assert_close(host_f64(outs_b[0]), ref_b, BF16_MAX, BF16_MEAN, what="decode reuse b")
 
 
 def test_decode_matches_last_prefill_row():
