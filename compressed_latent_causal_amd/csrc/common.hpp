@@ -143,11 +143,11 @@ __device__ inline float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); 
 // share a row of a 16x16 matrix-core result) with the cross-row swap
 // instructions: each swap, given the same register twice, returns one copy
 // holding the lanes' own rows and one holding the partner rows.
-__device__ inline float group4_max(float x) {
+__device__ inline float group4_max(float x) {  // NaN-propagating maximum
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ inline float group4_sum(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -158,7 +158,14 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt][0] = oacc[dt][1] = f32x4_t{0, 0, 0, 0};
     float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
+    // Row sums of P: with D = 64 the softmax, not the matrix core, bounds the
+    // tile, so the sums move to the matrix core (4 more products per tile, 32
+    // fewer vector adds); with D = 128 they stay vector adds per lane, reduced
+    // over the lane group at the end.
+    constexpr bool kMatrixSums = (D == 64);
+    f32x4_t lacc[2] = {f32x4_t{0, 0, 0, 0}, f32x4_t{0, 0, 0, 0}};  // element 0 = row sum
+    const bf16x8_t kOnes = __builtin_bit_cast(
+        bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});  // bf16 1.0
 
     auto compute = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
         const int kv0 = t * PF_BN;
@@ -189,23 +196,24 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
             }
         }
         bf16x8_t pf[2][2];
-        float alpha[2];
+        float mold[2], lpart[2];
         bool rescale = false;
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
+            // NaN-propagating maximum: one 3-input instruction per pair, no
+            // operand canonicalisation (scores are finite or -inf)
             float mx = sacc[0][n][0];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[mt][n][i]);
+                for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_maximum(mx, sacc[mt][n][i]);
             mx = group4_max(mx);
             // move the reference max only when the tile's max is well above it
             const bool up = (mx - m_run[n]) * c > PF_RESCALE_LOG2;
-            const float mnew = up ? mx : m_run[n];
-            alpha[n] = up ? __builtin_amdgcn_exp2f((m_run[n] - mnew) * c) : 1.f;
+            mold[n] = m_run[n];
             rescale |= up;
-            m_run[n] = mnew;
-            const float mc = (mnew == -INFINITY) ? 0.f : mnew * c;
+            if (up) m_run[n] = mx;
+            const float mc = (m_run[n] == -INFINITY) ? 0.f : m_run[n] * c;
             float ls = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -213,9 +221,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                 for (int i = 0; i < 4; ++i) {
                     const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][i], c, -mc));
                     sacc[mt][n][i] = p;
-                    ls += p;
+                    if constexpr (!kMatrixSums) ls += p;
                 }
-            l_run[n] = fmaf(l_run[n], alpha[n], ls);
+            if constexpr (!kMatrixSums) lpart[n] = ls;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 u32x4_t pw;
@@ -228,9 +236,30 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         }
         if (__any(rescale)) {  // wave-uniform: most tiles keep the reference max
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                oacc[dt][0] *= alpha[0];
-                oacc[dt][1] *= alpha[1];
+            for (int n = 0; n < 2; ++n) {
+                // the old reference is -inf only before the first tile (nothing accumulated)
+                const float alpha = (mold[n] == -INFINITY)
+                                        ? 0.f
+                                        : __builtin_amdgcn_exp2f((mold[n] - m_run[n]) * c);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) oacc[dt][n] *= alpha;
+                lacc[n] *= alpha;
+            }
+        }
+        if constexpr (!kMatrixSums) {
+            lacc[0][0] += lpart[0];
+            lacc[1][0] += lpart[1];
+        }
+
+        // ---- row sums of the bf16 probabilities on the matrix core: a tile of
+        // ones times P^T puts each query's sum over the tile's keys in every
+        // element of its lane (no lane reduction), and it sums exactly the
+        // values the P V product weights.
+        if constexpr (kMatrixSums) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                lacc[0] = mfma16(kOnes, pf[0][kk], lacc[0]);
+                lacc[1] = mfma16(kOnes, pf[1][kk], lacc[1]);
             }
         }
 
@@ -269,7 +298,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     // ---- epilogue: O = O^T / l, lane holds query qw0 + 16n + lr, dims 16dt + 4lg .. +3
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-        const float lt = group4_sum(l_run[n]);
+        const float lt = kMatrixSums ? lacc[n][0] : group4_sum(lacc[n][0]);
         const int qi = qw0 + 16 * n + lr;
         if (qi >= S) continue;
         const float inv = 1.f / lt;
