@@ -80,8 +80,11 @@ def rope(x, theta: float, pos_offset=None, pos_shift: int = 0, out=None):
     return out
 
 
-def prefill(q, k, v, scale: float | None = None, out=None):
-    """Causal GQA attention: q [B,Hq,S,D], k/v [B,Hkv,S,D] -> [B,Hq,S,D]."""
+def prefill(q, k, v, scale: float | None = None, out=None, rope_theta: float = 0.0):
+    """Causal GQA attention: q [B,Hq,S,D], k/v [B,Hkv,S,D] -> [B,Hq,S,D].
+
+    rope_theta > 0 rotates query i at position i inside the kernel (k must
+    already be rotated); 0 takes q as already rotated."""
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("q must be [B,Hq,S,D] and k, v [B,Hkv,S,D]")
@@ -97,7 +100,7 @@ def prefill(q, k, v, scale: float | None = None, out=None):
         out = torch.empty_like(q)
     _check_dev(q, k, v, out)
     _call(lib().attn_prefill, out.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-          _dtype_code(q), B, Hq, Hkv, S, D, float(scale), _stream(q))
+          _dtype_code(q), B, Hq, Hkv, S, D, float(scale), float(rope_theta), _stream(q))
     return out
 
 

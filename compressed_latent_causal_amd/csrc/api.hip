@@ -35,9 +35,11 @@ ATTN_API int attn_rope(void* out, const void* in, int dtype, int B, int H, int S
 }
 
 ATTN_API int attn_prefill(void* o, const void* q, const void* k, const void* v, int dtype, int B,
-                          int Hq, int Hkv, int S, int D, float scale, void* stream) {
+                          int Hq, int Hkv, int S, int D, float scale, double rope_theta,
+                          void* stream) {
     if (B < 0 || S < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
     if (!known_dtype(dtype) || !supported_dim(D) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
+    if (!(rope_theta >= 0.0) || !isfinite(rope_theta)) return ATTN_ERR_UNSUPPORTED;
     if (B == 0 || S == 0) return ATTN_OK;
     // one workgroup per (query block, batch, KV head, head slice): stay in a 32-bit grid
     if ((long long)B * Hq * ((S + 31) / 32) >= (1ll << 31)) return ATTN_ERR_SHAPE;
@@ -45,8 +47,8 @@ ATTN_API int attn_prefill(void* o, const void* q, const void* k, const void* v, 
     if ((long long)S * D * (dtype == ATTN_BF16 ? 2 : 4) >= (1ll << 31)) return ATTN_ERR_SHAPE;
     if (!o || !q || !k || !v) return ATTN_ERR_NULL;
     if (!aligned16(o) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return ATTN_ERR_ALIGN;
-    return hip_status(
-        attn::launch_prefill(o, q, k, v, dtype, B, Hq, Hkv, S, D, scale, (hipStream_t)stream));
+    return hip_status(attn::launch_prefill(o, q, k, v, dtype, B, Hq, Hkv, S, D, scale, rope_theta,
+                                           (hipStream_t)stream));
 }
 
 ATTN_API size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D) {

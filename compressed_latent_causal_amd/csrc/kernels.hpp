@@ -19,8 +19,11 @@ RopeFreqs rope_freqs(double theta, int D);
 hipError_t launch_rope(void* out, const void* in, int dtype, int B, int H, int S, int D,
                        const int32_t* pos_offset, int pos_shift, double theta, hipStream_t st);
 
+// rope_theta > 0 rotates each query at its token index on the fly (k must
+// already be rotated); rope_theta == 0 takes q as given.
 hipError_t launch_prefill(void* o, const void* q, const void* k, const void* v, int dtype, int B,
-                          int Hq, int Hkv, int S, int D, float scale, hipStream_t st);
+                          int Hq, int Hkv, int S, int D, float scale, double rope_theta,
+                          hipStream_t st);
 
 // Split workgroups (partial results) per (sequence, KV head) and workspace
 // bytes for these sizes.

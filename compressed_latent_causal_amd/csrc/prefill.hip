@@ -67,7 +67,8 @@ constexpr float PF_RESCALE_LOG2 = 8.f;
 template <int D, int HPW>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, int B, int Hq, int Hkv, int S, float c, int n_qblk, int n_hchunk) {
+    uint16_t* __restrict__ o, int B, int Hq, int Hkv, int S, float c, int n_qblk, int n_hchunk,
+    int rope, RopeFreqs fr) {
     constexpr int KSTEPS = D / 32;              // k-steps of S^T = K Q^T
     constexpr int DT = D / 16;                  // d tiles of O^T
     constexpr int QPB = (PF_NW / HPW) * PF_QW;  // queries per head per workgroup
@@ -103,6 +104,22 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     const uint16_t* const vg = v + (size_t)(b * Hkv + kvh) * S * D;
     const size_t qo_base = (size_t)(b * Hq + h) * S * D;
 
+    // With the query RoPE fused, the cosines and sines of the workgroup's query
+    // positions are formed once into a table shared by its heads (rows 0..31
+    // in the not yet used k1, rows 32..63 in v1: 32 rows x D/2 pairs x 8 bytes
+    // fill one tile buffer).  Workgroups of 128 queries (one head each) form
+    // them per lane instead.
+    constexpr bool kRopeTable = QPB <= 64;
+    if (rope && kRopeTable) {
+        for (int idx = tid; idx < QPB * (D / 2); idx += PF_THREADS) {
+            const int r = idx / (D / 2), pr = idx % (D / 2);
+            float cs, sn;
+            rope_cos_sin(q0 + r, fr.f[pr], cs, sn);
+            *(float2*)((r < 32 ? k1 : v1) + ((r & 31) * (D / 2) + pr) * 8) = float2{cs, sn};
+        }
+        __syncthreads();
+    }
+
     // Q^T fragments (B operand): query qw0 + 16n + lr, dims 32s + 8lg .. +7.
     bf16x8_t qf[2][KSTEPS];
 #pragma unroll
@@ -112,6 +129,25 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         for (int s = 0; s < KSTEPS; ++s) {
             u32x4_t x = {0, 0, 0, 0};
             if (row < S) x = *(const u32x4_t*)(q + qo_base + (size_t)row * D + 32 * s + 8 * lg);
+            if (rope) {
+                // query `row` sits at position row; word e of x holds channel
+                // pair 16s + 4lg + e (the same arithmetic as the RoPE kernel)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int pr = 16 * s + 4 * lg + e;
+                    float cs, sn, y0, y1;
+                    if constexpr (kRopeTable) {
+                        const float2 t = *(const float2*)((w / HPW == 0 ? k1 : v1) +
+                                                          ((16 * n + lr) * (D / 2) + pr) * 8);
+                        cs = t.x;
+                        sn = t.y;
+                    } else {
+                        rope_cos_sin(row, fr.f[pr], cs, sn);
+                    }
+                    rope_rotate(bf16_lo(x[e]), bf16_hi(x[e]), cs, sn, y0, y1);
+                    x[e] = pack_bf16x2(y0, y1);
+                }
+            }
             qf[n][s] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
@@ -322,7 +358,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restric
                                                           const float* __restrict__ v,
                                                           float* __restrict__ o, int B, int Hq,
                                                           int Hkv, int S, float c, int HPW,
-                                                          int n_qblk, int n_hchunk) {
+                                                          int n_qblk, int n_hchunk, int rope,
+                                                          RopeFreqs fr) {
     constexpr int DP = D / 4;  // dims per thread (4 threads per query row)
     __shared__ float ks[PF32_TK][D];
     __shared__ float vs[PF32_TK][D];
@@ -347,6 +384,16 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restric
     for (int e = 0; e < DP; ++e) {
         qr[e] = qi < S ? q[qo + e] : 0.f;
         acc[e] = 0.f;
+    }
+    if (rope) {  // dims part*DP .. +DP-1 are whole channel pairs of query qi at position qi
+#pragma unroll
+        for (int e = 0; e < DP; e += 2) {
+            float cs, sn, y0, y1;
+            rope_cos_sin(qi, fr.f[(part * DP + e) / 2], cs, sn);
+            rope_rotate(qr[e], qr[e + 1], cs, sn, y0, y1);
+            qr[e] = y0;
+            qr[e + 1] = y1;
+        }
     }
     float m_run = -INFINITY, l_run = 0.f;
 
@@ -393,32 +440,33 @@ int largest_pow2_divisor(int g, int cap) {
 
 template <int D, int HPW>
 hipError_t launch_bf16(void* o, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
-                       int S, float c, hipStream_t st) {
+                       int S, float c, double rope_theta, hipStream_t st) {
     constexpr int QPB = (PF_NW / HPW) * PF_QW;
     const int G = Hq / Hkv;
     const int n_qblk = ceil_div(S, QPB), n_hchunk = G / HPW;
     const long long nblk = (long long)n_qblk * B * Hkv * n_hchunk;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW>), dim3((unsigned)nblk), dim3(PF_THREADS), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, B,
-                       Hq, Hkv, S, c, n_qblk, n_hchunk);
+                       Hq, Hkv, S, c, n_qblk, n_hchunk, rope_theta > 0 ? 1 : 0,
+                       rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D));
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bf16_d(void* o, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
-                         int S, float c, hipStream_t st) {
+                         int S, float c, double th, hipStream_t st) {
     // heads per workgroup: the largest power of two dividing G, at most one per wave
     const int hpw = largest_pow2_divisor(Hq / Hkv, PF_NW);
     if constexpr (PF_NW >= 8)
-        if (hpw == 8) return launch_bf16<D, 8>(o, q, k, v, B, Hq, Hkv, S, c, st);
-    if (hpw >= 4) return launch_bf16<D, 4>(o, q, k, v, B, Hq, Hkv, S, c, st);
-    if (hpw == 2) return launch_bf16<D, 2>(o, q, k, v, B, Hq, Hkv, S, c, st);
-    return launch_bf16<D, 1>(o, q, k, v, B, Hq, Hkv, S, c, st);
+        if (hpw == 8) return launch_bf16<D, 8>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
+    if (hpw >= 4) return launch_bf16<D, 4>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
+    if (hpw == 2) return launch_bf16<D, 2>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
+    return launch_bf16<D, 1>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
 }
 
 template <int D>
 hipError_t launch_f32(void* o, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
-                      int S, float c, hipStream_t st) {
+                      int S, float c, double th, hipStream_t st) {
     const int G = Hq / Hkv;
     const int HPW = largest_pow2_divisor(G, 4);
     const int QPH = 64 / HPW;
@@ -426,20 +474,20 @@ hipError_t launch_f32(void* o, const void* q, const void* k, const void* v, int 
     const long long nblk = (long long)n_qblk * B * Hkv * n_hchunk;
     hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3((unsigned)nblk), dim3(256), 0, st,
                        (const float*)q, (const float*)k, (const float*)v, (float*)o, B, Hq, Hkv, S,
-                       c, HPW, n_qblk, n_hchunk);
+                       c, HPW, n_qblk, n_hchunk, th > 0 ? 1 : 0, rope_freqs(th > 0 ? th : 1.0, D));
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(void* o, const void* q, const void* k, const void* v, int dtype, int B,
-                          int Hq, int Hkv, int S, int D, float scale, hipStream_t st) {
+                          int Hq, int Hkv, int S, int D, float scale, double th, hipStream_t st) {
     const float c = scale * kLog2e;
     if (dtype == kBF16)
-        return D == 64 ? launch_bf16_d<64>(o, q, k, v, B, Hq, Hkv, S, c, st)
-                       : launch_bf16_d<128>(o, q, k, v, B, Hq, Hkv, S, c, st);
-    return D == 64 ? launch_f32<64>(o, q, k, v, B, Hq, Hkv, S, c, st)
-                   : launch_f32<128>(o, q, k, v, B, Hq, Hkv, S, c, st);
+        return D == 64 ? launch_bf16_d<64>(o, q, k, v, B, Hq, Hkv, S, c, th, st)
+                       : launch_bf16_d<128>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
+    return D == 64 ? launch_f32<64>(o, q, k, v, B, Hq, Hkv, S, c, th, st)
+                   : launch_f32<128>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
 }
 
 }  // namespace attn

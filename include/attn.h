@@ -92,11 +92,16 @@ int attn_rope(void *out, const void *in, int dtype, int B, int H, int S, int D,
  * accumulation and an fp32 softmax; the probabilities are rounded to bf16
  * before the product with V.  fp32 inputs are computed in fp32 throughout.
  * o must not overlap q, k or v.  scale > 0 and finite, usually 1/sqrt(D).
+ * rope_theta > 0: q is taken unrotated and query i is rotated on the fly at
+ * position i (bit for bit what attn_rope with pos_offset NULL, pos_shift 0
+ * produces); k must already be rotated (attn_rope on K).  rope_theta == 0: q
+ * is used as given.
  * One head's keys must span less than 2 GiB (S * D * element size < 2^31),
  * else ATTN_ERR_SHAPE.
  */
 int attn_prefill(void *o, const void *q, const void *k, const void *v, int dtype,
-                 int B, int Hq, int Hkv, int S, int D, float scale, void *stream);
+                 int B, int Hq, int Hkv, int S, int D, float scale, double rope_theta,
+                 void *stream);
 
 /*
  * Bytes of device workspace attn_decode needs for these sizes (0 on invalid

@@ -83,7 +83,8 @@ def test_prefill_validation(L):
     p = lambda *a: L.attn_prefill(*a)
     args = lambda **kw: [kw.get("o", FAKE), kw.get("q", FAKE), kw.get("k", FAKE), kw.get("v", FAKE),
                          kw.get("dt", BF16), kw.get("B", 1), kw.get("Hq", 8), kw.get("Hkv", 2),
-                         kw.get("S", 16), kw.get("D", 64), kw.get("scale", 0.125), None]
+                         kw.get("S", 16), kw.get("D", 64), kw.get("scale", 0.125),
+                         kw.get("theta", 0.0), None]
     assert p(*args(Hkv=3)) == ESHAPE
     assert p(*args(Hkv=0)) == ESHAPE
     assert p(*args(Hq=0)) == ESHAPE
@@ -94,6 +95,9 @@ def test_prefill_validation(L):
     assert p(*args(scale=0.0)) == EUNSUP
     assert p(*args(scale=-0.1)) == EUNSUP
     assert p(*args(scale=float("inf"))) == EUNSUP
+    assert p(*args(theta=-1.0)) == EUNSUP
+    assert p(*args(theta=float("nan"))) == EUNSUP
+    assert p(*args(theta=float("inf"))) == EUNSUP
     for name in "oqkv":
         assert p(*args(**{name: None})) == ENULL
         assert p(*args(**{name: FAKE + 4})) == EALIGN

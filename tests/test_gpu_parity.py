@@ -186,6 +186,43 @@ def test_prefill_worked_example_fp32_end_to_end():
     assert_close(host_f64(o), ref, F32_MAX, what="tiny fp32")
 
 
+def test_prefill_worked_example_fp32_fused_rope():
+    """Same example with the query rotation done inside the prefill kernel."""
+    w = wl.WORKLOADS["tiny_gqa"]
+    q, k, v = wl.make_prefill(w, seed=0)
+    say("tiny fp32 end to end, fused query RoPE")
+    o = attn.prefill(dev(q), attn.rope(dev(k), w.theta), dev(v), w.scale, rope_theta=w.theta)
+    ref = _oracle_prefill_e2e(q, k, v, w.theta, w.scale, "f32")
+    assert_close(host_f64(o), ref, F32_MAX, what="tiny fp32 fused")
+
+
+FUSED_ROPE_GEOMS = [  # B, Hq, Hkv, S, D, dtype, theta
+    (1, 8, 2, 16, 64, "bf16", 1e4),
+    (2, 8, 2, 257, 64, "bf16", 1e4),
+    (2, 8, 2, 200, 128, "bf16", 5e5),
+    (1, 32, 2, 70, 128, "bf16", 5e5),    # G = 16: two head slices
+    (1, 12, 2, 90, 128, "bf16", 1e4),    # G = 6
+    (1, 8, 2, 100, 64, "f32", 1e4),
+    (1, 4, 4, 70, 128, "f32", 5e5),
+]
+
+
+@pytest.mark.parametrize("geom", FUSED_ROPE_GEOMS)
+def test_prefill_fused_rope_equals_separate_rope(geom):
+    """rope_theta > 0 rotates q in the prefill kernel exactly as attn_rope does."""
+    B, Hq, Hkv, S, D, dt, theta = geom
+    g = torch.Generator().manual_seed(S * 7 + D)
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    q, k, v = (torch.randn(*shp, generator=g).to(dtype) for shp in
+               ((B, Hq, S, D), (B, Hkv, S, D), (B, Hkv, S, D)))
+    say(f"prefill fused vs separate RoPE {geom}")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    kr = attn.rope(kd, theta)
+    sep = attn.prefill(attn.rope(qd, theta), kr, vd)
+    fused = attn.prefill(qd, kr, vd, rope_theta=theta)
+    assert torch.equal(sep, fused)
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_prefill_worked_example_gqa_equals_repeated_mha(seed):
     w = wl.WORKLOADS["tiny_gqa"]
@@ -291,13 +328,13 @@ def _sample_rows(B, Hq, S, n_random, seed):
 @pytest.mark.parametrize("name", ["llama8b_prefill", "ccgqa_prefill"])
 def test_prefill_full_size_sampled_rows(name):
     """Full-size workloads in the launch configuration the benchmark times:
-    RoPE on Q and K, then prefill, end to end from the raw inputs; the oracle
-    recomputes a sample of output rows."""
+    RoPE on K, then prefill with the query rotation fused, end to end from the
+    raw inputs; the oracle recomputes a sample of output rows."""
     w = wl.WORKLOADS[name]
     q, k, v = wl.make_prefill(w, seed=0)
-    say(f"{name} full size: rope + prefill")
+    say(f"{name} full size: rope(K) + prefill with fused query RoPE")
     qd, kd, vd = dev(q), dev(k), dev(v)
-    o = attn.prefill(attn.rope(qd, w.theta), attn.rope(kd, w.theta), vd, w.scale)
+    o = attn.prefill(qd, attn.rope(kd, w.theta), vd, w.scale, rope_theta=w.theta)
     torch.cuda.synchronize()
     rows = _sample_rows(w.B, w.Hq, w.S, 200, 42)
     got = o.reshape(-1, w.D)[torch.from_numpy(rows).to(DEV)].double().cpu().numpy()
