@@ -30,7 +30,8 @@
 // tags it; a workgroup that finds every partial of its (sequence, KV head,
 // head slice) tagged by this call combines them (log-sum-exp rescaling) and
 // writes the output, so one launch does the whole step.  Cache slots at or past a
-// sequence's length are never loaded.
+// sequence's length never reach the result: loads of rows past it re-read the
+// last valid row (row 0 of an empty sequence) and their scores are masked.
 #include <atomic>
 #include <chrono>
 
@@ -44,7 +45,6 @@ namespace {
 constexpr int DC_NW = 4;      // waves per split workgroup
 constexpr int DC_SUB = 32;    // tokens per wave sub-tile
 constexpr int DC_HEADS = 16;  // query heads per split workgroup (MFMA N)
-constexpr int DC_MB = 256;    // partials per block of the last workgroup's merge
 
 #ifndef ATTN_DC_SUBS_PER_WAVE
 #define ATTN_DC_SUBS_PER_WAVE 32
@@ -77,13 +77,15 @@ __device__ inline f32x4_t load4_agent(const float* p) {
 
 template <int D>
 struct DecodeSmem {
-    static constexpr int kStage = 2 * DC_NW * DC_SUB * D * 2;          // V staging, 2 slots per wave
-    static constexpr int kOStride = D + 4;                             // padded row (floats)
-    static constexpr int kMerge = (2 * DC_NW * DC_HEADS + DC_NW * DC_HEADS * kOStride) * 4;
-    static constexpr int kFinal = (2 * DC_HEADS * DC_MB + 3 * DC_HEADS) * 4;  // last-workgroup merge
-    static constexpr int kMax2 = kStage > kMerge ? kStage : kMerge;
-    static constexpr int kBytes = kMax2 > kFinal ? kMax2 : kFinal;
+    // one V sub-tile slot per wave, in each of two arrays
+    static constexpr int kSlots = DC_NW * DC_SUB * D * 2;
+    // partials per block of the final merge: its (factor, sum) table fills one array
+    static constexpr int kMB = kSlots / (2 * DC_HEADS * 4);
 };
+
+// s_waitcnt immediates: vmcnt(n) alone, and lgkmcnt(0) alone
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+constexpr int kWaitLgkm0 = 0xC07F;
 
 template <int D>
 __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
@@ -96,7 +98,12 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     constexpr int VSUB = DC_SUB * ROW;         // bytes of one V sub-tile
     constexpr int VINST = VSUB / 1024;         // 1 KiB LDS-DMA instructions per sub-tile
     constexpr int RPI = 1024 / ROW;            // rows per DMA instruction
-    __shared__ __attribute__((aligned(16))) char smem[DecodeSmem<D>::kBytes];
+    // V slots: two arrays (the compiler then sees that the slot being filled is
+    // not the one being read); after the loop the first holds the waves'
+    // partial o vectors and, in the final merge, the partials' factors and sums.
+    __shared__ __attribute__((aligned(1024))) char vs0[DecodeSmem<D>::kSlots];
+    __shared__ __attribute__((aligned(1024))) char vs1[DecodeSmem<D>::kSlots];
+    __shared__ float sstat[2 * DC_NW * DC_HEADS];  // waves' max and sum; then running stats
 
     const int chunk = blockIdx.x, b = blockIdx.z;
     const int kvh = (int)blockIdx.y / n_hchunk, hc = (int)blockIdx.y % n_hchunk;
@@ -113,30 +120,11 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
 
-    // Q^T fragments (B operand, N = head): head h0 + lr (zero past the group), dims 32s + 8lg.
-    bf16x8_t qf[KSTEPS];
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        u32x4_t x = {0, 0, 0, 0};
-        if (lr < GH) x = *(const u32x4_t*)(q + (size_t)(b * Hq + h0 + lr) * D + 32 * s + 8 * lg);
-        if (rope) {
-            // the new token sits at position len - 1; word e of x holds channel
-            // pair 16s + 4lg + e
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float cs, sn, y0, y1;
-                rope_cos_sin((long long)len - 1, fr.f[16 * s + 4 * lg + e], cs, sn);
-                rope_rotate(bf16_lo(x[e]), bf16_hi(x[e]), cs, sn, y0, y1);
-                x[e] = pack_bf16x2(y0, y1);
-            }
-        }
-        qf[s] = __builtin_bit_cast(bf16x8_t, x);
-    }
-
     const size_t kvb = (size_t)(b * Hkv + kvh) * S_cap * D;
     const uint16_t* const kg = kc + kvb;
     const uint16_t* const vg = vc + kvb;
-    char* const vst = smem + w * 2 * VSUB;  // this wave's two V slots
+    char* const slot0 = vs0 + w * VSUB;  // this wave's two V slots
+    char* const slot1 = vs1 + w * VSUB;
 
     // The V sub-tile goes straight from HBM into this wave's LDS slot (no
     // registers): DMA instruction u puts lane l's 16 bytes at byte
@@ -167,7 +155,7 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     // cache, which keeps HBM streaming like a plain copy.  Each wave keeps two
     // sub-tiles in flight: the next one's K loads (registers) and V DMA (the
     // other LDS slot) are issued before the current one is computed.
-    const int we = len;
+    const int we = max(len, 1);  // rows at or past we - 1 re-read row we - 1 (row 0 if empty)
     const int jstep = nwg * DC_NW;
     auto issue = [&](int j, char* slot, bf16x8_t (&kd)[2][KSTEPS]) {
         const int t0 = j * DC_SUB;
@@ -187,19 +175,63 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
         }
     };
 
-    bf16x8_t kf[2][KSTEPS];
+    // Q^T fragments (B operand, N = head): head h0 + lr (zero past the group),
+    // dims 32s + 8lg.  The raw query and this lane's RoPE frequency are loaded
+    // first, then the first sub-tile's cache loads are issued, and the query
+    // is rotated while those are in flight.  All heads share the new token's
+    // position, so each lane forms the cosine and sine of one channel pair
+    // (lane % (D/2)) and the rotation fetches them from the lane holding them.
+    // (unconditional loads, lanes past the group re-read its last head and are
+    // zeroed afterwards, so the compiler can leave the cache loads in flight)
+    u32x4_t xq[KSTEPS];
+    const uint16_t* const qrow = q + (size_t)(b * Hq + h0 + min(lr, GH - 1)) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) xq[s] = *(const u32x4_t*)(qrow + 32 * s);
+    const double freq = fr.f[lane % (D / 2)];  // loaded unconditionally, like the query
+
+    bf16x8_t kA[2][KSTEPS], kB[2][KSTEPS];  // K fragments, double-buffered like V
     int j = chunk + nwg * w;
-    int cur = 0;
-    if (j < n_sub) issue(j, vst, kf);
-    for (; j < n_sub; j += jstep, cur ^= 1) {
-        const int t0 = j * DC_SUB;
-        const bool more = j + jstep < n_sub;
+    // unconditional, like every prefetch below, so the number of loads in
+    // flight is the same on every path (a wave with no sub-tile re-reads a
+    // valid row and never uses it)
+    issue(j, slot0, kA);
+
+    bf16x8_t qf[KSTEPS];
+    float cs_l = 1.f, sn_l = 0.f;
+    if (rope) rope_cos_sin((long long)len - 1, freq, cs_l, sn_l);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+        u32x4_t x = lr < GH ? xq[s] : u32x4_t{0, 0, 0, 0};
+        if (rope) {
+            // word e of x holds channel pair 16s + 4lg + e
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int pr = 16 * s + 4 * lg + e;
+                const float cs = __shfl(cs_l, pr, 64), sn = __shfl(sn_l, pr, 64);
+                float y0, y1;
+                rope_rotate(bf16_lo(x[e]), bf16_hi(x[e]), cs, sn, y0, y1);
+                x[e] = pack_bf16x2(y0, y1);
+            }
+        }
+        qf[s] = __builtin_bit_cast(bf16x8_t, x);
+    }
+
+    // One sub-tile: its V was DMA'd into vcur one step earlier and its K sits
+    // in kf; the next sub-tile's loads go to vnext / kn first.
+    auto body = [&](int jj, const char* vcur, char* vnext, const bf16x8_t (&kf)[2][KSTEPS],
+                    bf16x8_t (&kn)[2][KSTEPS]) __attribute__((always_inline)) {
+        const int t0 = jj * DC_SUB;
+        const bool more = jj + jstep < n_sub;
         // Always prefetch (the last sub-tile re-fetches itself, an L2 hit) so the
         // number of loads in flight is the same on every path and the waits
-        // below can leave the prefetch outstanding.
-        bf16x8_t kn[2][KSTEPS];
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot was read by the previous PV
-        issue(more ? j + jstep : j, vst + (cur ^ 1) * VSUB, kn);
+        // can leave the prefetch outstanding.
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // vnext was read by the previous step's PV
+        issue(more ? jj + jstep : jj, vnext, kn);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the products
+        // this sub-tile's K and V were loaded before the prefetch's
+        // VINST + 2*KSTEPS operations, and vector memory completes in order
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(VINST + 2 * KSTEPS));
+        __builtin_amdgcn_sched_barrier(0);  // ... and the products after the wait
 
         // S^T = K Q^T; lane holds head lr, tokens t0 + 16mt + 4lg + i
         f32x4_t sacc[2] = {f32x4_t{0, 0, 0, 0}, f32x4_t{0, 0, 0, 0}};
@@ -213,12 +245,12 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (t0 + 16 * mt + 4 * lg + i >= we) sacc[mt][i] = -INFINITY;
-                mx = fmaxf(mx, sacc[mt][i]);
+                if (t0 + 16 * mt + 4 * lg + i >= len) sacc[mt][i] = -INFINITY;
+                mx = __builtin_elementwise_maximum(mx, sacc[mt][i]);
             }
-        mx = fmaxf(mx, xor_shfl(mx, 16));
-        mx = fmaxf(mx, xor_shfl(mx, 32));
-        const float mnew = fmaxf(m_run, mx);
+        mx = __builtin_elementwise_maximum(mx, xor_shfl(mx, 16));
+        mx = __builtin_elementwise_maximum(mx, xor_shfl(mx, 32));
+        const float mnew = __builtin_elementwise_maximum(m_run, mx);
         const float mref = (mnew == -INFINITY) ? 0.f : mnew;
         const float alpha = __builtin_amdgcn_exp2f((m_run - mref) * c);
         const float mc = mref * c;
@@ -240,28 +272,28 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
         pw[3] = pack_bf16x2(sacc[1][2], sacc[1][3]);
         const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
 
-        // this sub-tile's V DMA was issued before the prefetch's VINST + 2*KSTEPS
-        // loads, and vector memory operations complete in order
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VINST + 2 * KSTEPS) : "memory");
-        const char* const vcur = vst + cur * VSUB;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
             oacc[dt] = mfma16(v_frag_at<D>(vcur + voff[dt]), pf, oacc[dt] * alpha);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) kf[mt][s] = kn[mt][s];
+    };
+    // Unrolled by two so each step names its V slots and K registers
+    // statically, with no exit between the two steps (the compiler would
+    // otherwise sink the first step's K prefetch past it, next to its use).
+    for (; j + jstep < n_sub; j += 2 * jstep) {
+        body(j, slot0, slot1, kA, kB);
+        body(j + jstep, slot1, slot0, kB, kA);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last (redundant) prefetch landed
+    if (j < n_sub) body(j, slot0, slot1, kA, kB);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the last prefetch landed
 
     // ---- merge the four waves in LDS
     l_run += xor_shfl(l_run, 16);
     l_run += xor_shfl(l_run, 32);
     __syncthreads();  // all V staging reads are done
-    float* const cm = (float*)smem;
-    float* const cl = cm + DC_NW * DC_HEADS;
-    float* const co = cl + DC_NW * DC_HEADS;
-    constexpr int OS = DecodeSmem<D>::kOStride;
+    float* const cm = sstat;
+    float* const cl = sstat + DC_NW * DC_HEADS;
+    float* const co = (float*)vs0;  // [wave][head][D]
+    constexpr int OS = D;
     if (lg == 0) {
         cm[w * DC_HEADS + lr] = m_run;
         cl[w * DC_HEADS + lr] = l_run;
@@ -345,11 +377,11 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     // parallel load, each head's running max / factor / sum are updated there,
     // and every thread folds the o vectors of its items (a head and 4
     // consecutive dims each) with 16-byte loads, MU of them in flight.
-    constexpr int MB = DC_MB, MU = 8, EPI = 4;
+    constexpr int MB = DecodeSmem<D>::kMB, MU = 8, EPI = 4;
     constexpr int NITEM = DC_HEADS * D / EPI / (DC_NW * 64);  // items per thread, at most
-    float* const bm = (float*)smem;        // [DC_HEADS][MB] max, then factor
+    float* const bm = (float*)vs0;         // [DC_HEADS][MB] max, then factor
     float* const bl = bm + DC_HEADS * MB;  // [DC_HEADS][MB] sum
-    float* const run = bl + DC_HEADS * MB;  // [DC_HEADS] running max, [DC_HEADS] alpha, [DC_HEADS] L
+    float* const run = sstat;  // [DC_HEADS] running max, [DC_HEADS] alpha, [DC_HEADS] L
     if (tid < DC_HEADS) {
         run[tid] = -INFINITY;
         run[2 * DC_HEADS + tid] = 0.f;
