@@ -21,6 +21,7 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------------- bf16
 // bf16 -> fp32 is exact: the 16 bits are the top half of a binary32.

@@ -32,6 +32,7 @@
 // writes the output, so one launch does the whole step.  Cache slots at or past a
 // sequence's length never reach the result: loads of rows past it re-read the
 // last valid row (row 0 of an empty sequence) and their scores are masked.
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 
@@ -46,17 +47,15 @@ constexpr int DC_NW = 4;      // waves per split workgroup
 constexpr int DC_SUB = 32;    // tokens per wave sub-tile
 constexpr int DC_HEADS = 16;  // query heads per split workgroup (MFMA N)
 
-#ifndef ATTN_DC_SUBS_PER_WAVE
-#define ATTN_DC_SUBS_PER_WAVE 32
-#endif
-// Sub-tiles one split workgroup covers at most: each of its waves walks about
-// ATTN_DC_SUBS_PER_WAVE sub-tiles, so a sequence of n_sub sub-tiles gets
-// ceil(n_sub / DC_SUBS_PER_WG) workgroups (partials) and no workgroup's work
-// exceeds that bound, whatever the mix of lengths.
-constexpr int DC_SUBS_PER_WG = DC_NW * ATTN_DC_SUBS_PER_WAVE;
+// Sub-tiles one split workgroup covers at most (spwg): a sequence of n_sub
+// sub-tiles gets ceil(n_sub / spwg) workgroups (partials), so no workgroup's
+// work exceeds that bound, whatever the mix of lengths.  DC_SUBS_PER_WG (32
+// per wave) is the default and the smallest value used; workspace sizes are
+// computed with it.
+constexpr int DC_SUBS_PER_WG = DC_NW * 32;
 
-__host__ __device__ inline int decode_partials(int len) {
-    return ceil_div(ceil_div(len, DC_SUB), DC_SUBS_PER_WG);
+__host__ __device__ inline int decode_partials(int len, int spwg) {
+    return ceil_div(ceil_div(len, DC_SUB), spwg);
 }
 
 // Device-coherent (agent-scope) float accesses for the split partials.
@@ -92,7 +91,8 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seqlens, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     unsigned long long* __restrict__ ws_tag, uint16_t* __restrict__ o, int Hq, int Hkv, int S_cap,
-    int max_len, int NC, float c, int n_hchunk, int rope, RopeFreqs fr, unsigned long long tag) {
+    int max_len, int NC, float c, int n_hchunk, int rope, RopeFreqs fr, unsigned long long tag,
+    int spwg) {
     constexpr int KSTEPS = D / 32, DT = D / 16;
     constexpr int ROW = D * 2;                 // bytes per cache row
     constexpr int VSUB = DC_SUB * ROW;         // bytes of one V sub-tile
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     const int n_sub = ceil_div(len, DC_SUB);  // 32-token sub-tiles of this sequence
     // split workgroups of this sequence (an empty one still gets one, which
     // writes its zero rows)
-    const int nwg = max(1, decode_partials(len));
+    const int nwg = max(1, decode_partials(len, spwg));
     if (chunk >= nwg) return;  // uniform across the workgroup
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -463,21 +463,54 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     }
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Sub-tiles per split workgroup for `groups` (sequence, KV head, head slice)
+// groups of up to max_len tokens.  The default leaves every workgroup at most
+// 32 sub-tiles per wave.  When even sequences at max_len would give no more
+// workgroups than compute units (a few long sequences), the workgroups are
+// made longer instead, so that about 70% of the units read the cache: on this
+// part fewer, longer streams read HBM faster than one workgroup per unit, and
+// more workgroups than units would leave some units with two.
+int decode_spwg(long long groups, int max_len) {
+    const long long n_sub = ceil_div((long long)max_len, (long long)DC_SUB);
+    const long long cus = device_cus();
+    if (groups * ceil_div(n_sub, (long long)DC_SUBS_PER_WG) > cus) return DC_SUBS_PER_WG;
+    const long long target = std::max(1ll, cus * 7 / 10);
+    const long long spwg = ceil_div(groups * n_sub, target);
+    return (int)std::min(std::max(spwg, (long long)DC_SUBS_PER_WG), (long long)(1 << 30));
+}
+
 template <int D>
 hipError_t launch_decode_d(void* o, const void* q, const void* k_cache, const void* v_cache, int B,
                            int Hq, int Hkv, int S_cap, const int32_t* seqlens, int max_len, float c,
                            double rope_theta, void* workspace, unsigned long long tag,
                            hipStream_t st) {
-    const int NC = decode_num_chunks(B, Hkv, max_len);
+    const int NC = decode_num_chunks(B, Hkv, max_len);  // partial slots per (sequence, head)
     const int G = Hq / Hkv;
     const int n_hchunk = ceil_div(G, DC_HEADS);
+    const int spwg = decode_spwg((long long)B * Hkv * n_hchunk, max_len);
+    const int nwg_max = max(1, decode_partials(max_len, spwg));  // <= NC
     float* const ws_o = (float*)workspace;
     float* const ws_ml = ws_o + (size_t)B * Hq * NC * D;
     unsigned long long* const ws_tag = (unsigned long long*)(ws_ml + (size_t)B * Hq * NC * 2);
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(NC, Hkv * n_hchunk, B), dim3(DC_NW * 64), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, seqlens,
-                       ws_o, ws_ml, ws_tag, (uint16_t*)o, Hq, Hkv, S_cap, max_len, NC, c, n_hchunk,
-                       rope_theta > 0 ? 1 : 0, rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D), tag);
+    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(nwg_max, Hkv * n_hchunk, B), dim3(DC_NW * 64), 0,
+                       st, (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
+                       seqlens, ws_o, ws_ml, ws_tag, (uint16_t*)o, Hq, Hkv, S_cap, max_len, NC, c,
+                       n_hchunk, rope_theta > 0 ? 1 : 0,
+                       rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D), tag, spwg);
     return hipGetLastError();
 }
 
@@ -498,7 +531,7 @@ unsigned long long next_decode_tag() {
 
 int decode_num_chunks(int B, int Hkv, int max_len) {
     // workspace slots per (sequence, head): the partial count of the longest sequence
-    return max(1, decode_partials(max_len));
+    return max(1, decode_partials(max_len, DC_SUBS_PER_WG));
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int D) {
