@@ -9,12 +9,16 @@
 // With a RoPE theta the split pass first rotates each query head at position
 // len - 1 (the same device code as the stand-alone RoPE kernel, so the fused
 // and unfused paths agree bit for bit), saving a launch per decode step.
-// Split pass: per (sequence, KV head [, 16-head slice]) as many workgroups as
-// the sequence's length needs (each covers at most 4 x 32 sub-tiles of 32
-// tokens).  Sub-tile j goes to workgroup j % nwg and, inside it, to wave
-// (j / nwg) % 4, so the running workgroups always read one contiguous front of
-// the cache (HBM streams as for a plain copy) and ragged batches stay balanced.  Each
-// byte of K and V is read once and serves all G query heads of the group.
+// Split pass: the launch has a fixed budget of workgroups (about two per
+// compute unit when there are many (sequence, KV head [, 16-head slice])
+// groups, fewer and longer streams when there are few).  Every workgroup reads
+// the batch's lengths and derives the same split: each group of n 32-token
+// sub-tiles gets ceil(n / U) workgroups, with U the smallest size (at least
+// 16) that keeps the total within the budget, so ragged batches give
+// workgroups of nearly equal work and all of them run at once.  Sub-tile j of
+// a group goes to its workgroup j % nwg and, inside it, to wave (j / nwg) % 4,
+// so a group's workgroups read one contiguous front of the cache.  Each byte
+// of K and V is read once and serves all G query heads of the group.
 // Per sub-tile:
 //   * K rows are loaded straight from HBM into matrix-core operand registers
 //     (16-byte loads; a wave instruction covers 16 rows x 64 contiguous bytes)
@@ -47,15 +51,51 @@ constexpr int DC_NW = 4;      // waves per split workgroup
 constexpr int DC_SUB = 32;    // tokens per wave sub-tile
 constexpr int DC_HEADS = 16;  // query heads per split workgroup (MFMA N)
 
-// Sub-tiles one split workgroup covers at most (spwg): a sequence of n_sub
-// sub-tiles gets ceil(n_sub / spwg) workgroups (partials), so no workgroup's
-// work exceeds that bound, whatever the mix of lengths.  DC_SUBS_PER_WG (32
-// per wave) is the default and the smallest value used; workspace sizes are
-// computed with it.
-constexpr int DC_SUBS_PER_WG = DC_NW * 32;
+// Smallest number of sub-tiles one split workgroup is given: it bounds the
+// split workgroups (partial results) of a group, ceil(n_sub / DC_UMIN), and so
+// the workspace.
+constexpr int DC_UMIN = 16;
 
-__host__ __device__ inline int decode_partials(int len, int spwg) {
-    return ceil_div(ceil_div(len, DC_SUB), spwg);
+__host__ __device__ inline int decode_max_partials(int max_len) {
+    return max(1, ceil_div(ceil_div(max_len, DC_SUB), DC_UMIN));
+}
+
+// ceil(n / u) for 0 <= n < 2^30, 0 < u, given r ~ 1/u in float: the float
+// quotient is within a few units of the answer, and integer steps settle it.
+__device__ inline int ceil_div_est(int n, int u, float r) {
+    int q = (int)((float)n * r);
+    while ((long long)q * u < n) ++q;
+    while (q > 0 && (long long)(q - 1) * u >= n) --q;
+    return q;
+}
+
+// Wave-wide integer sum and inclusive prefix sum with data-parallel
+// primitives (lane moves inside 16-lane rows, then row swaps or row
+// broadcasts), avoiding the LDS round trips of general shuffles.
+// dpp_add(x, ctrl, rows): x plus the lane value `ctrl` selects, in the rows
+// of the `rows` mask (other rows add nothing).
+template <int CTRL, int ROWS = 0xF>
+__device__ inline int dpp_add(int x) {
+    return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false);
+}
+__device__ inline int wave_sum(int x) {
+    x = dpp_add<0xB1>(x);   // quad permutation: + lane ^ 1
+    x = dpp_add<0x4E>(x);   // quad permutation: + lane ^ 2 (quad totals)
+    x = dpp_add<0x124>(x);  // row rotate by 4: + a neighbouring quad
+    x = dpp_add<0x128>(x);  // row rotate by 8: row totals
+    const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    x = (int)(a[0] + a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return (int)(b[0] + b[1]);
+}
+__device__ inline int wave_inclusive_scan(int x) {
+    x = dpp_add<0x111>(x);  // row shift right by 1, 2, 4, 8: prefix sums within rows
+    x = dpp_add<0x112>(x);
+    x = dpp_add<0x114>(x);
+    x = dpp_add<0x118>(x);
+    x = dpp_add<0x142, 0xA>(x);  // lane 15 of rows 0 and 2 into rows 1 and 3
+    x = dpp_add<0x143, 0xC>(x);  // lane 31 into rows 2 and 3
+    return x;
 }
 
 // Device-coherent (agent-scope) float accesses for the split partials.
@@ -92,7 +132,7 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     const int32_t* __restrict__ seqlens, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     unsigned long long* __restrict__ ws_tag, uint16_t* __restrict__ o, int Hq, int Hkv, int S_cap,
     int max_len, int NC, float c, int n_hchunk, int rope, RopeFreqs fr, unsigned long long tag,
-    int spwg) {
+    int B, int budget) {
     constexpr int KSTEPS = D / 32, DT = D / 16;
     constexpr int ROW = D * 2;                 // bytes per cache row
     constexpr int VSUB = DC_SUB * ROW;         // bytes of one V sub-tile
@@ -105,19 +145,82 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     __shared__ __attribute__((aligned(1024))) char vs1[DecodeSmem<D>::kSlots];
     __shared__ float sstat[2 * DC_NW * DC_HEADS];  // waves' max and sum; then running stats
 
-    const int chunk = blockIdx.x, b = blockIdx.z;
-    const int kvh = (int)blockIdx.y / n_hchunk, hc = (int)blockIdx.y % n_hchunk;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+
+    // ---- this workgroup's (sequence b, group gi, split chunk of nwg).  Groups
+    // are numbered b-major (GPB per sequence), their workgroups consecutively.
+    const int GPB = Hkv * n_hchunk;
+    int b, gi, chunk, nwg, len;
+    if ((long long)B * GPB >= budget) {  // one workgroup per group fills the budget
+        b = (int)blockIdx.x / GPB;
+        gi = (int)blockIdx.x % GPB;
+        chunk = 0;
+        nwg = 1;
+        if (b >= B) return;
+        len = min(max(seqlens[b], 0), max_len);
+    } else {
+        // B < budget: each wave stages the sequences' lengths in its own
+        // second V slot, which only it fills later (an empty sequence still
+        // gets one workgroup, which writes its zero rows)
+        int* const ls = (int*)(vs1 + w * VSUB);
+        for (int i = lane; i < B; i += 64) ls[i] = min(max(seqlens[i], 0), max_len);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        auto ns = [&](int i) { return ceil_div(ls[i], DC_SUB); };
+        // every wave finds the same U, a size whose workgroup count fits the
+        // budget.  With T = GPB * sum(n), count(U) is about T / U + GPB * B / 2
+        // (half a workgroup of rounding per group); start there and grow U
+        // until the count fits (at n_sub_max it is B * GPB < budget).
+        auto count = [&](int U) {
+            const float r = 1.f / (float)U;
+            int n = 0;
+            for (int i = lane; i < B; i += 64) n += max(1, ceil_div_est(ns(i), U, r));
+            return wave_sum(n) * GPB;
+        };
+        int tot = 0;  // the cache holds every counted token, so this fits
+        for (int i = lane; i < B; i += 64) tot += ns(i);
+        const long long T = (long long)wave_sum(tot) * GPB;
+        const int n_sub_max = max(DC_UMIN, ceil_div(max_len, DC_SUB));
+        const long long room = budget - (long long)GPB * B / 2;  // > budget / 2
+        int U = (int)min<long long>(n_sub_max, max<long long>(DC_UMIN, ceil_div(T, room)));
+        while (U < n_sub_max && count(U) > budget) U = min(n_sub_max, U + max(1, U >> 3));
+        // locate this workgroup: prefix sums of the sequences' workgroup counts
+        b = -1;
+        int first = 0;  // first workgroup of sequence b
+        const float rU = 1.f / (float)U;
+        for (int i0 = 0, base = 0; i0 < B; i0 += 64) {
+            const int i = i0 + lane;
+            const int v = i < B ? GPB * max(1, ceil_div_est(ns(i), U, rU)) : 0;
+            const int incl = wave_inclusive_scan(v);
+            const int p = (int)blockIdx.x - base;
+            const unsigned long long hit = __ballot(v > 0 && p >= incl - v && p < incl);
+            if (hit) {
+                const int l = __builtin_ctzll(hit);
+                b = i0 + l;
+                first = base + __builtin_amdgcn_readlane(incl - v, l);
+                break;
+            }
+            base += __builtin_amdgcn_readlane(incl, 63);
+        }
+        if (b < 0) return;  // past the last group's workgroups (uniform)
+        len = ls[b];
+        nwg = max(1, ceil_div_est(ceil_div(len, DC_SUB), U, rU));
+        const int off = (int)blockIdx.x - first;
+        gi = off / nwg;
+        chunk = off % nwg;
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    gi = __builtin_amdgcn_readfirstlane(gi);
+    chunk = __builtin_amdgcn_readfirstlane(chunk);
+    nwg = __builtin_amdgcn_readfirstlane(nwg);
+    len = __builtin_amdgcn_readfirstlane(len);
+    const int kvh = gi / n_hchunk, hc = gi % n_hchunk;
     const int G = Hq / Hkv;
     const int h0 = kvh * G + hc * DC_HEADS;
     const int GH = min(DC_HEADS, G - hc * DC_HEADS);
-    const int len = min(max(seqlens[b], 0), max_len);
     const int n_sub = ceil_div(len, DC_SUB);  // 32-token sub-tiles of this sequence
-    // split workgroups of this sequence (an empty one still gets one, which
-    // writes its zero rows)
-    const int nwg = max(1, decode_partials(len, spwg));
-    if (chunk >= nwg) return;  // uniform across the workgroup
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
 
     const size_t kvb = (size_t)(b * Hkv + kvh) * S_cap * D;
@@ -477,20 +580,23 @@ int device_cus() {
     return n;
 }
 
-// Sub-tiles per split workgroup for `groups` (sequence, KV head, head slice)
-// groups of up to max_len tokens.  The default leaves every workgroup at most
-// 32 sub-tiles per wave.  When even sequences at max_len would give no more
-// workgroups than compute units (a few long sequences), the workgroups are
-// made longer instead, so that about 70% of the units read the cache: on this
-// part fewer, longer streams read HBM faster than one workgroup per unit, and
-// more workgroups than units would leave some units with two.
-int decode_spwg(long long groups, int max_len) {
-    const long long n_sub = ceil_div((long long)max_len, (long long)DC_SUB);
+// Workgroup budget of a launch over `groups` (sequence, KV head, head slice)
+// groups: about two per compute unit when there are many groups; with few
+// groups (a handful of long sequences) about 72% of the units, since on this
+// part fewer, longer streams per cache region read HBM faster.  At most the
+// number of lengths a wave can stage.
+#ifndef DC_MANY_PCT
+#define DC_MANY_PCT 200
+#endif
+#ifndef DC_FEW_PCT
+#define DC_FEW_PCT 72
+#endif
+int decode_budget(long long groups, int D) {
     const long long cus = device_cus();
-    if (groups * ceil_div(n_sub, (long long)DC_SUBS_PER_WG) > cus) return DC_SUBS_PER_WG;
-    const long long target = std::max(1ll, cus * 7 / 10);
-    const long long spwg = ceil_div(groups * n_sub, target);
-    return (int)std::min(std::max(spwg, (long long)DC_SUBS_PER_WG), (long long)(1 << 30));
+    const long long budget = groups * 4 >= cus ? std::max(1ll, cus * DC_MANY_PCT / 100)
+                                               : std::max(1ll, cus * DC_FEW_PCT / 100);
+    const long long cap = (long long)(DC_SUB * D * 2) / 4;  // lengths one V slot holds
+    return (int)std::min(budget, cap);
 }
 
 template <int D>
@@ -501,16 +607,18 @@ hipError_t launch_decode_d(void* o, const void* q, const void* k_cache, const vo
     const int NC = decode_num_chunks(B, Hkv, max_len);  // partial slots per (sequence, head)
     const int G = Hq / Hkv;
     const int n_hchunk = ceil_div(G, DC_HEADS);
-    const int spwg = decode_spwg((long long)B * Hkv * n_hchunk, max_len);
-    const int nwg_max = max(1, decode_partials(max_len, spwg));  // <= NC
+    const long long groups = (long long)B * Hkv * n_hchunk;
+    const int budget = decode_budget(groups, D);
+    const long long nblocks = std::max<long long>(budget, groups);
+    if (nblocks > INT32_MAX) return hipErrorInvalidValue;
     float* const ws_o = (float*)workspace;
     float* const ws_ml = ws_o + (size_t)B * Hq * NC * D;
     unsigned long long* const ws_tag = (unsigned long long*)(ws_ml + (size_t)B * Hq * NC * 2);
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(nwg_max, Hkv * n_hchunk, B), dim3(DC_NW * 64), 0,
-                       st, (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
+    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)nblocks), dim3(DC_NW * 64), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
                        seqlens, ws_o, ws_ml, ws_tag, (uint16_t*)o, Hq, Hkv, S_cap, max_len, NC, c,
                        n_hchunk, rope_theta > 0 ? 1 : 0,
-                       rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D), tag, spwg);
+                       rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D), tag, B, budget);
     return hipGetLastError();
 }
 
@@ -530,8 +638,8 @@ unsigned long long next_decode_tag() {
 }  // namespace
 
 int decode_num_chunks(int B, int Hkv, int max_len) {
-    // workspace slots per (sequence, head): the partial count of the longest sequence
-    return max(1, decode_partials(max_len, DC_SUBS_PER_WG));
+    // workspace slots per (sequence, head): the most split workgroups a group can get
+    return decode_max_partials(max_len);
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int D) {

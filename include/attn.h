@@ -107,9 +107,9 @@ int attn_prefill(void *o, const void *q, const void *k, const void *v, int dtype
  * Bytes of device workspace attn_decode needs for these sizes (0 on invalid
  * sizes).  The workspace holds fp32 partial results (D + 2 floats) per
  * (sequence, query head, split workgroup) and one 64-bit call tag per
- * (sequence, KV head, slice of up to 16 query heads, split workgroup); the
- * number of split workgroups of a sequence depends only on its length, so
- * max_len bounds it.
+ * (sequence, KV head, slice of up to 16 query heads, split workgroup).  A
+ * split workgroup covers at least 16 x 32 cache tokens, so a sequence has at
+ * most ceil(max_len / 512) of them.
  */
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D);
 
@@ -133,8 +133,9 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D);
  * 16-byte aligned; its contents on entry do not matter (each call tags the
  * partial results it writes), and it must not be shared by calls that may
  * overlap.  dtype: BF16 only.  scale > 0 and finite.  One kernel is enqueued:
- * workgroups split each sequence's keys, and one that finds all partial
- * results of its (sequence, KV head) written merges them.
+ * its workgroups read the lengths and split the batch's keys into nearly
+ * equal parts (a sequence's keys go to one or more workgroups), and one that
+ * finds all partial results of its (sequence, KV head) written merges them.
  */
 int attn_decode(void *o, const void *q, const void *k_cache, const void *v_cache, int dtype,
                 int B, int Hq, int Hkv, int S_cap, int D, const int32_t *seqlens,

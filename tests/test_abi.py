@@ -115,10 +115,10 @@ def test_decode_workspace_size(L):
     assert ws(1, 8, 2, 100, 96) == 0           # head dim
     assert ws(0, 8, 2, 100, 128) == 0          # empty
     n = ws(32, 32, 8, 8192, 128)
-    # 8192 tokens = 256 sub-tiles of 32 -> 2 split workgroups per sequence;
-    # (D + 2) floats per (sequence, head, partial) and an 8-byte tag per
-    # (sequence, KV head, partial)
-    assert n == 32 * 32 * 2 * 130 * 4 + 32 * 8 * 2 * 8
+    # 8192 tokens = 256 sub-tiles of 32; a split workgroup takes at least 16
+    # of them -> at most 16 partials per group; (D + 2) floats per (sequence,
+    # head, partial) and an 8-byte tag per (sequence, KV head, partial)
+    assert n == 32 * 32 * 16 * 130 * 4 + 32 * 8 * 16 * 8
     # partials per (sequence, head, chunk): grows with max_len, never shrinks
     sizes = [ws(1, 64, 8, L_, 128) for L_ in (1, 512, 4096, 131072)]
     assert sizes == sorted(sizes) and sizes[0] > 0
