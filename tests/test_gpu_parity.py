@@ -401,6 +401,12 @@ DECODE_CASES = [  # B, Hq, Hkv, S_cap, D, lengths
     (3, 16, 2, 20000, 64, [20000, 4097, 1]),
     (2, 64, 2, 9000, 128, [9000, 8193]),          # two head slices, 3 partials each
     (1, 2, 1, 1100000, 64, [1100000]),            # > 256 partials: blocked final merge
+    # more (sequence, KV head) groups than the launch budget (two workgroups
+    # per compute unit): one workgroup per group
+    (70, 8, 8, 200, 64, [(37 * i) % 201 for i in range(70)]),
+    # over 64 ragged sequences under the budget: the split's prefix sums span
+    # several 64-sequence passes
+    (100, 4, 1, 3000, 64, [(997 * i) % 3001 for i in range(100)]),
 ]
 
 
