@@ -17,10 +17,12 @@
 //  * Scores are formed transposed, S^T = K Q^T, with the 16x16x32 bf16 matrix
 //    core: each lane ends up holding one query and 4 keys per 16x16 tile, so the
 //    softmax row statistics are per-lane scalars (plus a 4-lane reduction).
-//  * Online softmax in fp32 in the exp2 domain (scale * log2 e folded into one
-//    FMA per score).  The reference max moves only when a tile raises it by
-//    more than 2^8, so almost every tile skips rescaling O (the normalisation
-//    at the end is exact for any reference).  P is rounded to bf16 and fed
+//  * Online softmax in fp32 in the exp2 domain.  Q is pre-scaled by
+//    scale * log2 e, and the score products start from the negated running
+//    reference instead of zero, so they produce the exponent itself: one exp2
+//    per score and no other arithmetic before it.  The reference moves only
+//    when a tile raises it by more than 2^8, so almost every tile skips
+//    rescaling O (the normalisation at the end is exact for any reference).  P is rounded to bf16 and fed
 //    straight from registers as the
 //    B operand of O^T = V^T P^T.  The A operand (V^T) comes from the row-major
 //    V tile through the LDS transpose read, so V is never transposed in memory.
@@ -148,6 +150,10 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                     x[e] = pack_bf16x2(y0, y1);
                 }
             }
+            // pre-scale by c = scale * log2(e) (rounded to bf16 once more), so
+            // the products are scores in the exp2 domain
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = pack_bf16x2(bf16_lo(x[e]) * c, bf16_hi(x[e]) * c);
             qf[n][s] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
@@ -193,7 +199,11 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     f32x4_t oacc[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt][0] = oacc[dt][1] = f32x4_t{0, 0, 0, 0};
+    // Running reference of each row in the exp2 domain (-inf before the first
+    // tile), and its negation as a 16x16 accumulator: the score products start
+    // from it, so they yield c * s - reference with no vector instruction.
     float m_run[2] = {-INFINITY, -INFINITY};
+    f32x4_t negm[2] = {f32x4_t{0, 0, 0, 0}, f32x4_t{0, 0, 0, 0}};
     // Row sums of P: with D = 64 the softmax, not the matrix core, bounds the
     // tile, so the sums move to the matrix core (4 more products per tile, 32
     // fewer vector adds); with D = 128 they stay vector adds per lane, reduced
@@ -208,14 +218,12 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         // ---- S^T = K Q^T : tile mt covers keys kv0 + 16mt .. +15
         f32x4_t sacc[4][2];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) sacc[mt][0] = sacc[mt][1] = f32x4_t{0, 0, 0, 0};
-#pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 const bf16x8_t a = *(const bf16x8_t*)(ks + koff[s] + 16 * mt * ROW);
-                sacc[mt][0] = mfma16(a, qf[0][s], sacc[mt][0]);
-                sacc[mt][1] = mfma16(a, qf[1][s], sacc[mt][1]);
+                sacc[mt][0] = mfma16(a, qf[0][s], s == 0 ? negm[0] : sacc[mt][0]);
+                sacc[mt][1] = mfma16(a, qf[1][s], s == 0 ? negm[1] : sacc[mt][1]);
             }
         }
 
@@ -231,35 +239,53 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                         if (16 * mt + i > lim) sacc[mt][n][i] = -INFINITY;
             }
         }
-        bf16x8_t pf[2][2];
-        float mold[2], lpart[2];
+        // ---- sacc = c * s - reference.  The reference moves to the row's tile
+        // maximum on the first tile and whenever a tile exceeds it by more
+        // than PF_RESCALE_LOG2; then O and the sums are rescaled and this
+        // tile's values shifted (wave-uniform branch, taken on few tiles).
+        float mx[2];
         bool rescale = false;
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             // NaN-propagating maximum: one 3-input instruction per pair, no
             // operand canonicalisation (scores are finite or -inf)
-            float mx = sacc[0][n][0];
+            float m = sacc[0][n][0];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_maximum(mx, sacc[mt][n][i]);
-            mx = group4_max(mx);
-            // move the reference max only when the tile's max is well above it
-            const bool up = (mx - m_run[n]) * c > PF_RESCALE_LOG2;
-            mold[n] = m_run[n];
-            rescale |= up;
-            if (up) m_run[n] = mx;
-            const float mc = (m_run[n] == -INFINITY) ? 0.f : m_run[n] * c;
+                for (int i = 0; i < 4; ++i) m = __builtin_elementwise_maximum(m, sacc[mt][n][i]);
+            mx[n] = group4_max(m);
+            rescale |= (mx[n] > -INFINITY) & ((m_run[n] == -INFINITY) | (mx[n] > PF_RESCALE_LOG2));
+        }
+        if (__any(rescale)) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const bool up = (mx[n] > -INFINITY) & ((m_run[n] == -INFINITY) | (mx[n] > PF_RESCALE_LOG2));
+                const float d = up ? mx[n] : 0.f;  // the shift of the reference
+                // nothing is accumulated before the first tile
+                const float alpha = (m_run[n] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(-d);
+                if (up) m_run[n] = (m_run[n] == -INFINITY ? 0.f : m_run[n]) + d;
+                negm[n] = f32x4_t{-m_run[n], -m_run[n], -m_run[n], -m_run[n]};
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) sacc[mt][n] -= d;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) oacc[dt][n] *= alpha;
+                lacc[n] *= alpha;
+            }
+        }
+        bf16x8_t pf[2][2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
             float ls = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][i], c, -mc));
+                    const float p = __builtin_amdgcn_exp2f(sacc[mt][n][i]);
                     sacc[mt][n][i] = p;
                     if constexpr (!kMatrixSums) ls += p;
                 }
-            if constexpr (!kMatrixSums) lpart[n] = ls;
+            if constexpr (!kMatrixSums) lacc[n][0] += ls;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 u32x4_t pw;
@@ -269,22 +295,6 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                 pw[3] = pack_bf16x2(sacc[2 * kk + 1][n][2], sacc[2 * kk + 1][n][3]);
                 pf[n][kk] = __builtin_bit_cast(bf16x8_t, pw);
             }
-        }
-        if (__any(rescale)) {  // wave-uniform: most tiles keep the reference max
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                // the old reference is -inf only before the first tile (nothing accumulated)
-                const float alpha = (mold[n] == -INFINITY)
-                                        ? 0.f
-                                        : __builtin_amdgcn_exp2f((mold[n] - m_run[n]) * c);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) oacc[dt][n] *= alpha;
-                lacc[n] *= alpha;
-            }
-        }
-        if constexpr (!kMatrixSums) {
-            lacc[0][0] += lpart[0];
-            lacc[1][0] += lpart[1];
         }
 
         // ---- row sums of the bf16 probabilities on the matrix core: a tile of
