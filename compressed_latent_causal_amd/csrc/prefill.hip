@@ -60,11 +60,12 @@ constexpr int PF_QW = 32;                 // queries per wave
 constexpr int PF_NW = ATTN_PF_WAVES;      // waves per workgroup
 constexpr int PF_THREADS = PF_NW * 64;
 
-// Online-softmax running max is only moved when a tile's max exceeds it by more
-// than this many log2 units; until then the stale max is used as the reference
-// (probabilities up to 2^8, exact in the final normalisation) and the wave
-// skips rescaling O.
-constexpr float PF_RESCALE_LOG2 = 8.f;
+// The online softmax keeps a per-row reference (a past tile maximum) and only
+// moves it when a tile's probabilities relative to it sum to more than this:
+// every accumulated probability is then at most 2^16 (exact in the final
+// normalisation, far from fp32 and bf16 overflow), and most tiles need neither
+// a maximum nor a rescale of O.
+constexpr float PF_SUM_LIMIT = 65536.f;
 
 template <int D, int HPW>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
@@ -204,12 +205,12 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     // from it, so they yield c * s - reference with no vector instruction.
     float m_run[2] = {-INFINITY, -INFINITY};
     f32x4_t negm[2] = {f32x4_t{0, 0, 0, 0}, f32x4_t{0, 0, 0, 0}};
-    // Row sums of P: with D = 64 the softmax, not the matrix core, bounds the
-    // tile, so the sums move to the matrix core (4 more products per tile, 32
-    // fewer vector adds); with D = 128 they stay vector adds per lane, reduced
-    // over the lane group at the end.
-    constexpr bool kMatrixSums = (D == 64);
-    f32x4_t lacc[2] = {f32x4_t{0, 0, 0, 0}, f32x4_t{0, 0, 0, 0}};  // element 0 = row sum
+    // Row sums of P, formed on the matrix core: a tile of ones times P^T puts
+    // each query's sum over the tile's keys in every element of its lane (no
+    // lane reduction), and it sums exactly the bf16 values the P V product
+    // weights.  Four products per tile cost less than 32 vector adds, since
+    // vector and matrix instructions share a SIMD's issue.
+    float lacc[2] = {0.f, 0.f};
     const bf16x8_t kOnes = __builtin_bit_cast(
         bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});  // bf16 1.0
 
@@ -239,29 +240,48 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                         if (16 * mt + i > lim) sacc[mt][n][i] = -INFINITY;
             }
         }
-        // ---- sacc = c * s - reference.  The reference moves to the row's tile
-        // maximum on the first tile and whenever a tile exceeds it by more
-        // than PF_RESCALE_LOG2; then O and the sums are rescaled and this
-        // tile's values shifted (wave-uniform branch, taken on few tiles).
-        float mx[2];
-        bool rescale = false;
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            // NaN-propagating maximum: one 3-input instruction per pair, no
-            // operand canonicalisation (scores are finite or -inf)
-            float m = sacc[0][n][0];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) m = __builtin_elementwise_maximum(m, sacc[mt][n][i]);
-            mx[n] = group4_max(m);
-            rescale |= (mx[n] > -INFINITY) & ((m_run[n] == -INFINITY) | (mx[n] > PF_RESCALE_LOG2));
-        }
-        if (__any(rescale)) {
+        // ---- sacc = c * s - reference.  P = exp2(sacc) as bf16 fragments and
+        // its row sums lt for this tile.
+        bf16x8_t pf[2][2];
+        f32x4_t lt[2];
+        auto exp_pack = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
-                const bool up = (mx[n] > -INFINITY) & ((m_run[n] == -INFINITY) | (mx[n] > PF_RESCALE_LOG2));
-                const float d = up ? mx[n] : 0.f;  // the shift of the reference
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    u32x4_t pw;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const f32x4_t& x = sacc[2 * kk + h][n];
+                        pw[2 * h] = pack_bf16x2(__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]));
+                        pw[2 * h + 1] = pack_bf16x2(__builtin_amdgcn_exp2f(x[2]), __builtin_amdgcn_exp2f(x[3]));
+                    }
+                    pf[n][kk] = __builtin_bit_cast(bf16x8_t, pw);
+                }
+                lt[n] = mfma16(kOnes, pf[n][0], f32x4_t{0, 0, 0, 0});
+                lt[n] = mfma16(kOnes, pf[n][1], lt[n]);
+            }
+        };
+        exp_pack();
+        // The reference moves to the row's tile maximum on the row's first
+        // tile, and when the tile's sum exceeds PF_SUM_LIMIT (or is not
+        // finite); then O and the sums are rescaled and the tile is redone
+        // (wave-uniform branch, taken on few tiles).
+        bool redo = false;
+#pragma unroll
+        for (int n = 0; n < 2; ++n) redo |= (m_run[n] == -INFINITY) | !(lt[n][0] <= PF_SUM_LIMIT);
+        if (__any(redo)) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                // NaN-propagating maximum: one 3-input instruction per pair
+                float m = sacc[0][n][0];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m = __builtin_elementwise_maximum(m, sacc[mt][n][i]);
+                const float mx = group4_max(m);
+                const bool up = (mx > -INFINITY) & ((m_run[n] == -INFINITY) | !(lt[n][0] <= PF_SUM_LIMIT));
+                const float d = up ? mx : 0.f;  // the shift of the reference
                 // nothing is accumulated before the first tile
                 const float alpha = (m_run[n] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(-d);
                 if (up) m_run[n] = (m_run[n] == -INFINITY ? 0.f : m_run[n]) + d;
@@ -272,42 +292,10 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                 for (int dt = 0; dt < DT; ++dt) oacc[dt][n] *= alpha;
                 lacc[n] *= alpha;
             }
+            exp_pack();
         }
-        bf16x8_t pf[2][2];
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            float ls = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(sacc[mt][n][i]);
-                    sacc[mt][n][i] = p;
-                    if constexpr (!kMatrixSums) ls += p;
-                }
-            if constexpr (!kMatrixSums) lacc[n][0] += ls;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                u32x4_t pw;
-                pw[0] = pack_bf16x2(sacc[2 * kk][n][0], sacc[2 * kk][n][1]);
-                pw[1] = pack_bf16x2(sacc[2 * kk][n][2], sacc[2 * kk][n][3]);
-                pw[2] = pack_bf16x2(sacc[2 * kk + 1][n][0], sacc[2 * kk + 1][n][1]);
-                pw[3] = pack_bf16x2(sacc[2 * kk + 1][n][2], sacc[2 * kk + 1][n][3]);
-                pf[n][kk] = __builtin_bit_cast(bf16x8_t, pw);
-            }
-        }
-
-        // ---- row sums of the bf16 probabilities on the matrix core: a tile of
-        // ones times P^T puts each query's sum over the tile's keys in every
-        // element of its lane (no lane reduction), and it sums exactly the
-        // values the P V product weights.
-        if constexpr (kMatrixSums) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                lacc[0] = mfma16(kOnes, pf[0][kk], lacc[0]);
-                lacc[1] = mfma16(kOnes, pf[1][kk], lacc[1]);
-            }
-        }
+        lacc[0] += lt[0][0];
+        lacc[1] += lt[1][0];
 
         // ---- O^T += V^T P^T
 #pragma unroll
@@ -344,7 +332,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     // ---- epilogue: O = O^T / l, lane holds query qw0 + 16n + lr, dims 16dt + 4lg .. +3
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-        const float lt = kMatrixSums ? lacc[n][0] : group4_sum(lacc[n][0]);
+        const float lt = lacc[n];
         const int qi = qw0 + 16 * n + lr;
         if (qi >= S) continue;
         const float inv = 1.f / lt;

@@ -311,6 +311,25 @@ def test_prefill_scale_and_errors():
         attn.prefill(dev(q), dev(k).float(), dev(v))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_scores_growing_along_the_keys(D):
+    """Keys scaled up along the sequence (and queries aligned with them), so
+    later tiles keep exceeding the row's reference by many exp2 units: the
+    kernel's rescale path runs on most tiles, and some tiles' probabilities
+    relative to a stale reference would overflow."""
+    B, Hq, Hkv, S = 1, 4, 2, 700
+    g = torch.Generator().manual_seed(77 + D)
+    base = torch.randn(D, generator=g)
+    q = (base + 0.3 * torch.randn(B, Hq, S, D, generator=g)).to(torch.bfloat16)
+    growth = torch.linspace(0.2, 3.0, S).reshape(1, 1, S, 1)
+    k = ((base + 0.3 * torch.randn(B, Hkv, S, D, generator=g)) * growth).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, S, D, generator=g).to(torch.bfloat16)
+    say(f"prefill growing scores D={D}")
+    o = attn.prefill(dev(q), dev(k), dev(v))
+    assert_close(host_f64(o), oracle.prefill(bits(q), bits(k), bits(v)), BF16_MAX, BF16_MEAN,
+                 what=f"growing scores D={D}")
+
+
 def _sample_rows(B, Hq, S, n_random, seed):
     """Row indices (b*Hq + h)*S + i: both ends of every head, tile edges and
     random interior rows."""
