@@ -59,6 +59,10 @@ constexpr int PF_BN = 64;                 // keys per K/V tile
 constexpr int PF_QW = 32;                 // queries per wave
 constexpr int PF_NW = ATTN_PF_WAVES;      // waves per workgroup
 constexpr int PF_THREADS = PF_NW * 64;
+// LDS operand fragments read ahead of the products that use them
+#ifndef PF_PD
+#define PF_PD 2
+#endif
 
 // The online softmax keeps a per-row reference (a past tile maximum) and only
 // moves it when a tile's probabilities relative to it sum to more than this:
@@ -216,16 +220,25 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
 
     auto compute = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
         const int kv0 = t * PF_BN;
-        // ---- S^T = K Q^T : tile mt covers keys kv0 + 16mt .. +15
+        // ---- S^T = K Q^T : tile mt covers keys kv0 + 16mt .. +15.  Operand f
+        // (k-step f / 4, key tile f % 4) is read PF_PD operands ahead of its
+        // products, so the LDS latency hides behind them.
+        constexpr int NKF = 4 * KSTEPS;
+        auto kfrag = [&](int f) __attribute__((always_inline)) {
+            return *(const bf16x8_t*)(ks + koff[f / 4] + 16 * (f % 4) * ROW);
+        };
         f32x4_t sacc[4][2];
+        bf16x8_t kf[NKF];
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
+        for (int f = 0; f < PF_PD && f < NKF; ++f) kf[f] = kfrag(f);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8_t a = *(const bf16x8_t*)(ks + koff[s] + 16 * mt * ROW);
-                sacc[mt][0] = mfma16(a, qf[0][s], s == 0 ? negm[0] : sacc[mt][0]);
-                sacc[mt][1] = mfma16(a, qf[1][s], s == 0 ? negm[1] : sacc[mt][1]);
-            }
+        for (int f = 0; f < NKF; ++f) {
+            if (f + PF_PD < NKF) kf[f + PF_PD] = kfrag(f + PF_PD);
+            __builtin_amdgcn_sched_barrier(0);
+            const int s = f / 4, mt = f % 4;
+            sacc[mt][0] = mfma16(kf[f], qf[0][s], s == 0 ? negm[0] : sacc[mt][0]);
+            sacc[mt][1] = mfma16(kf[f], qf[1][s], s == 0 ? negm[1] : sacc[mt][1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // ---- online softmax; lane holds query qw0 + 16n + lr and keys kv0 + 16mt + 4lg + i
@@ -297,15 +310,23 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         lacc[0] += lt[0][0];
         lacc[1] += lt[1][0];
 
-        // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T, operand f = (d tile f / 2, key half f % 2) read
+        // PF_PD operands ahead
+        constexpr int NVF = 2 * DT;
+        auto vfrag = [&](int f) __attribute__((always_inline)) {
+            return v_frag_at<D>(vs + voff[f / 2] + 32 * (f % 2) * ROW);
+        };
+        bf16x8_t vf[NVF];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+        for (int f = 0; f < PF_PD && f < NVF; ++f) vf[f] = vfrag(f);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8_t a = v_frag_at<D>(vs + voff[dt] + 32 * kk * ROW);
-                oacc[dt][0] = mfma16(a, pf[0][kk], oacc[dt][0]);
-                oacc[dt][1] = mfma16(a, pf[1][kk], oacc[dt][1]);
-            }
+        for (int f = 0; f < NVF; ++f) {
+            if (f + PF_PD < NVF) vf[f + PF_PD] = vfrag(f + PF_PD);
+            __builtin_amdgcn_sched_barrier(0);
+            const int dt = f / 2, kk = f % 2;
+            oacc[dt][0] = mfma16(vf[f], pf[0][kk], oacc[dt][0]);
+            oacc[dt][1] = mfma16(vf[f], pf[1][kk], oacc[dt][1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
