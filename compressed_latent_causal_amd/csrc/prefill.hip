@@ -9,8 +9,10 @@
 // bf16 kernel design (flash-style, exact up to rounding):
 //  * One workgroup = 4 waves = HPW query heads of one KV group x a block of
 //    queries.  Each wave owns one head and 32 consecutive queries; two
-//    workgroups share a CU, and their independent barriers let one
-//    workgroup's matrix-core phase overlap the other's softmax.  The K and V
+//    workgroups share a CU, so while one waits on its barrier, its tile loads
+//    or LDS, the other issues.  (A SIMD issues matrix and vector
+//    instructions one after the other: vector work is never hidden behind
+//    the matrix core, so the softmax is kept to the exponentials.)  The K and V
 //    tile (64 keys x D) is loaded once into LDS and serves every head of the
 //    workgroup, so a KV group's key/value bytes are fetched once per query block
 //    rather than once per query head.
