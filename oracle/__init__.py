@@ -72,6 +72,9 @@ def _load():
             lib.oracle_decode.argtypes = [P, P, P, P, i, i, i, i, i, i, P,
                                           ctypes.c_double]
             lib.oracle_decode.restype = i
+            lib.oracle_decode_paged.argtypes = [P, P, P, P, i, i, i, i, i, i, i, P, i, P, i,
+                                                ctypes.c_double]
+            lib.oracle_decode_paged.restype = i
             lib.oracle_round_bf16.argtypes = [P, P, ctypes.c_size_t]
             lib.oracle_round_bf16.restype = None
             lib.oracle_round_f32.argtypes = [P, P, ctypes.c_size_t]
@@ -210,6 +213,38 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, seqlens,
                                float(scale))
     if rc:
         raise RuntimeError(f"oracle_decode failed ({rc})")
+    return out
+
+
+def decode_paged(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_table,
+                 seqlens, window: int = 0, scale: float | None = None) -> np.ndarray:
+    """One new query token per sequence over a paged cache ("GQA y técnicas
+    relacionadas": PagedAttention, sliding-window attention).  q [B,Hq,D],
+    pages [num_pages,Hkv,page_size,D], block_table int [B,max_pages] (token t
+    of sequence b is row t % page_size of page block_table[b, t // page_size]),
+    seqlens int [B]; window > 0 limits the query to the last `window` tokens.
+    Returns fp64 [B,Hq,D]."""
+    dt = _dtype_of(q)
+    q, k_pages, v_pages = (_as_input(t, dt) for t in (q, k_pages, v_pages))
+    B, Hq, D = q.shape
+    num_pages, Hkv, page_size, _ = k_pages.shape
+    if k_pages.shape != (num_pages, Hkv, page_size, D) or v_pages.shape != k_pages.shape or Hq % Hkv:
+        raise ValueError("bad shapes")
+    table = np.ascontiguousarray(block_table, dtype=np.int32)
+    if table.ndim != 2 or table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    lens = np.ascontiguousarray(seqlens, dtype=np.int32)
+    if lens.shape != (B,):
+        raise ValueError("seqlens must be [B]")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    rc = _load().oracle_decode_paged(_ptr(out), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                     _DT_CODE[dt], B, Hq, Hkv, page_size, D, num_pages,
+                                     _ptr(table), table.shape[1], _ptr(lens), int(window),
+                                     float(scale))
+    if rc:
+        raise RuntimeError(f"oracle_decode_paged failed ({rc})")
     return out
 
 

@@ -265,3 +265,92 @@ int oracle_decode(double *out, const void *q, const void *k_cache, const void *v
     }
     return bad;
 }
+
+/* Single-token decode over a paged cache, optionally limited to a sliding
+ * window.  "Grouped Query Attention (GQA)" glossary, section "GQA y técnicas
+ * relacionadas": PagedAttention keeps the cache in fixed-size blocks, and
+ * sliding-window attention bounds the cached tokens a query sees.  The pages
+ * name both without further detail; this follows the plain reading:
+ *  - k_pages, v_pages: [num_pages, Hkv, page_size, D];  block_table:
+ *    [B, max_pages] page indices;  token t of sequence b is row t % page_size
+ *    of page block_table[b][t / page_size];
+ *  - window > 0: the query of sequence b sees tokens max(0, len_b - window)
+ *    .. len_b - 1;  window <= 0: all len_b tokens.
+ * Otherwise as oracle_decode: out [B, Hq, D], a sequence that sees no token
+ * gets a zero row.  Returns 3 if a needed table entry is outside
+ * [0, num_pages) or a length exceeds max_pages * page_size. */
+int oracle_decode_paged(double *out, const void *q, const void *k_pages, const void *v_pages,
+                        int dt, int B, int Hq, int Hkv, int page_size, int D, int num_pages,
+                        const int32_t *block_table, int max_pages, const int32_t *seqlens,
+                        int window, double scale)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || page_size <= 0 || D <= 0 || num_pages <= 0 ||
+        max_pages <= 0 || Hq % Hkv != 0)
+        return 1;
+    for (int b = 0; b < B; ++b) {
+        const int len = seqlens[b];
+        if (len < 0 || (int64_t)len > (int64_t)max_pages * page_size)
+            return 3;
+        const int lo = (window > 0 && len > window) ? len - window : 0;
+        for (int t = lo; t < len; ++t) {
+            int pg = block_table[(size_t)b * max_pages + t / page_size];
+            if (pg < 0 || pg >= num_pages)
+                return 3;
+        }
+    }
+    int G = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        size_t cap = (size_t)max_pages * page_size;
+        double *w = (double *)malloc(sizeof(double) * cap);
+        size_t *rowb = (size_t *)malloc(sizeof(size_t) * cap);
+        if (!w || !rowb) {
+#pragma omp atomic write
+            bad = 2;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < (int64_t)B * Hq; ++r) {
+                int h = (int)(r % Hq);
+                int b = (int)(r / Hq);
+                int j = h / G;
+                const int len = seqlens[b];
+                const int lo = (window > 0 && len > window) ? len - window : 0;
+                double *o = out + (size_t)r * D;
+                for (int d = 0; d < D; ++d)
+                    o[d] = 0.0;
+                if (len <= lo)
+                    continue;
+                /* element offset of every visible token's row */
+                for (int t = lo; t < len; ++t) {
+                    size_t pg = (size_t)block_table[(size_t)b * max_pages + t / page_size];
+                    rowb[t - lo] = ((pg * Hkv + j) * page_size + (size_t)(t % page_size)) * D;
+                }
+                const int cnt = len - lo;
+                double m = -INFINITY;
+                for (int t = 0; t < cnt; ++t) {
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dot += load(q, (size_t)r * D + d, dt) * load(k_pages, rowb[t] + d, dt);
+                    w[t] = dot * scale;
+                    if (w[t] > m)
+                        m = w[t];
+                }
+                double l = 0.0;
+                for (int t = 0; t < cnt; ++t) {
+                    w[t] = exp(w[t] - m);
+                    l += w[t];
+                }
+                for (int t = 0; t < cnt; ++t)
+                    for (int d = 0; d < D; ++d)
+                        o[d] += w[t] * load(v_pages, rowb[t] + d, dt);
+                for (int d = 0; d < D; ++d)
+                    o[d] = o[d] / l;
+            }
+        }
+        free(w);
+        free(rowb);
+    }
+    return bad;
+}
+

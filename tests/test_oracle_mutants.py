@@ -32,6 +32,13 @@ MUTANTS = {
     "decode_length_short": ("int n = seqlens[b];", "int n = seqlens[b] > 0 ? seqlens[b] - 1 : 0;"),
     "bf16_truncates": ("double r = rint(ldexp(x, -k));", "double r = trunc(ldexp(x, -k));"),
     "missing_normalisation": ("o[d] /= l;", "o[d] /= 1.0;"),
+    "paged_ignores_table": ("size_t pg = (size_t)block_table[(size_t)b * max_pages + t / page_size];",
+                            "size_t pg = (size_t)b * max_pages + t / page_size;"),
+    "paged_row_in_page": ("(size_t)(t % page_size)) * D;", "(size_t)(t / page_size)) * D;"),
+    "paged_head_major_pages": ("((pg * Hkv + j) * page_size", "((j * num_pages + pg) * page_size"),
+    "window_off_by_one": ("? len - window : 0;\n                double *o",
+                          "? len - window + 1 : 0;\n                double *o"),
+    "paged_normalisation": ("o[d] = o[d] / l;", "o[d] = o[d];"),
 }
 
 

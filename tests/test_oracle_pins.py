@@ -283,6 +283,98 @@ def test_decode_ragged_lengths_match_sdpa_and_empty_is_zero():
 
 
 # ---------------------------------------------------------------------------
+# Paged cache and sliding window ("GQA y técnicas relacionadas")
+# ---------------------------------------------------------------------------
+def _paged(kc, vc, P, seed=None):
+    """Split a contiguous cache [B,Hkv,cap,D] (cap % P == 0) into pages
+    [B*cap/P, Hkv, P, D]; with a seed the physical page order is shuffled.
+    Returns (k_pages, v_pages, block_table)."""
+    B, Hkv, cap, D = kc.shape
+    n = cap // P
+    perm = np.arange(B * n) if seed is None else np.random.default_rng(seed).permutation(B * n)
+    kp = np.empty((B * n, Hkv, P, D), kc.dtype)
+    vp = np.empty_like(kp)
+    table = np.empty((B, n), np.int32)
+    for b in range(B):
+        for i in range(n):
+            pg = perm[b * n + i]
+            kp[pg] = kc[b, :, i * P:(i + 1) * P]
+            vp[pg] = vc[b, :, i * P:(i + 1) * P]
+            table[b, i] = pg
+    return kp, vp, table
+
+
+def _cache(seed, B=3, Hq=8, Hkv=2, cap=48, D=16):
+    return (_rand((B, Hq, D), seed), _rand((B, Hkv, cap, D), seed + 1),
+            _rand((B, Hkv, cap, D), seed + 2))
+
+
+def test_decode_paged_with_pages_in_order_equals_contiguous_decode():
+    q, kc, vc = _cache(60)
+    lens = [48, 17, 1]
+    for P in (1, 8, 16, 48):
+        kp, vp, table = _paged(kc, vc, P)
+        got = oracle.decode_paged(q, kp, vp, table, lens)
+        assert np.max(np.abs(got - oracle.decode(q, kc, vc, lens))) < 1e-13
+
+
+def test_decode_paged_page_order_does_not_matter():
+    q, kc, vc = _cache(61)
+    lens = [40, 9, 33]
+    ref = oracle.decode_paged(q, *_paged(kc, vc, 8), lens)
+    for seed in (1, 2):
+        got = oracle.decode_paged(q, *_paged(kc, vc, 8, seed=seed), lens)
+        assert np.max(np.abs(got - ref)) < 1e-13
+
+
+def test_decode_paged_window_of_one_returns_the_last_value():
+    q, kc, vc = _cache(62)
+    lens = [48, 17, 1]
+    got = oracle.decode_paged(q, *_paged(kc, vc, 16, seed=3), lens, window=1)
+    G = q.shape[1] // kc.shape[1]
+    for b, n in enumerate(lens):
+        for h in range(q.shape[1]):
+            assert np.array_equal(got[b, h], vc[b, h // G, n - 1])
+
+
+def test_decode_paged_window_of_two_is_a_logistic_blend():
+    q, kc, vc = _cache(63)
+    lens = [48, 17, 2]
+    D = q.shape[2]
+    got = oracle.decode_paged(q, *_paged(kc, vc, 16, seed=4), lens, window=2)
+    G = q.shape[1] // kc.shape[1]
+    for b, n in enumerate(lens):
+        for h in range(q.shape[1]):
+            j = h // G
+            s0 = q[b, h] @ kc[b, j, n - 2] / math.sqrt(D)
+            s1 = q[b, h] @ kc[b, j, n - 1] / math.sqrt(D)
+            a = 1.0 / (1.0 + math.exp(s1 - s0))  # weight of the older token
+            ref = a * vc[b, j, n - 2] + (1 - a) * vc[b, j, n - 1]
+            assert np.max(np.abs(got[b, h] - ref)) < 1e-12
+
+
+def test_decode_paged_window_sees_exactly_the_last_tokens():
+    q, kc, vc = _cache(64)
+    lens = [48, 30, 5]
+    W = 12
+    got = oracle.decode_paged(q, *_paged(kc, vc, 8, seed=5), lens, window=W)
+    for b, n in enumerate(lens):
+        lo = max(0, n - W)
+        sl = lambda c: np.ascontiguousarray(c[b:b + 1, :, lo:n])
+        ref = oracle.decode(q[b:b + 1], sl(kc), sl(vc), [n - lo])
+        assert np.max(np.abs(got[b] - ref[0])) < 1e-13
+    # a window at least as long as the sequence changes nothing
+    full = oracle.decode_paged(q, *_paged(kc, vc, 8, seed=5), lens)
+    assert np.array_equal(oracle.decode_paged(q, *_paged(kc, vc, 8, seed=5), lens, window=48), full)
+
+
+def test_decode_paged_empty_sequence_is_zero():
+    q, kc, vc = _cache(65)
+    got = oracle.decode_paged(q, *_paged(kc, vc, 16, seed=6), [0, 3, 0], window=4)
+    assert np.array_equal(got[0], np.zeros_like(got[0])) and np.array_equal(got[2], got[0])
+
+
+# ---------------------------------------------------------------------------
 # RoPE
 # ---------------------------------------------------------------------------
 def test_rope_position_zero_is_identity():
