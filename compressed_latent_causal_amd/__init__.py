@@ -22,7 +22,7 @@ from ._lib import (  # noqa: F401
     AttnError, lib, lib_path, DTYPE_CODES, STATUS,
 )
 
-__all__ = ["rope", "prefill", "decode", "decode_workspace_size", "AttnError", "lib_path"]
+__all__ = ["rope", "prefill", "decode", "decode_paged", "decode_workspace_size", "AttnError", "lib_path"]
 
 
 def _torch():
@@ -139,5 +139,48 @@ def decode(q, k_cache, v_cache, seqlens, max_len: int | None = None, scale: floa
     _call(lib().attn_decode, out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
           v_cache.data_ptr(), _dtype_code(q), B, Hq, Hkv, S_cap, D, seqlens.data_ptr(),
           int(max_len), float(scale), float(rope_theta), workspace.data_ptr(),
+          workspace.numel() * workspace.element_size(), _stream(q))
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, max_len: int | None = None,
+                 window: int = 0, scale: float | None = None, rope_theta: float = 0.0,
+                 out=None, workspace=None):
+    """One query token per sequence over a paged cache.
+
+    q [B,Hq,D]; pages [num_pages,Hkv,page_size,D] (page_size a multiple of
+    32); block_table device int32 [B,max_pages]: token t of sequence b is row
+    t % page_size of page block_table[b, t // page_size]; seqlens device int32
+    [B] with 0 <= seqlens[b] <= max_len <= max_pages*page_size (max_len
+    defaults to that product).  window > 0 limits each query to its
+    sequence's last `window` tokens.  rope_theta as for decode.
+    Returns [B,Hq,D]."""
+    torch = _torch()
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("q must be [B,Hq,D] and pages [num_pages,Hkv,page_size,D]")
+    B, Hq, D = q.shape
+    num_pages, Hkv, page_size, _ = k_pages.shape
+    if k_pages.shape[3] != D:
+        raise ValueError("pages must have q's head dim")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    if seqlens.dtype != torch.int32 or seqlens.shape != (B,):
+        raise ValueError("seqlens must be int32 [B]")
+    max_pages = block_table.shape[1]
+    if max_len is None:
+        max_len = max_pages * page_size
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_size(B, Hq, Hkv, max_len, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    block_table = block_table.contiguous()
+    _check_dev(q, k_pages, v_pages, block_table, seqlens, out, workspace)
+    _call(lib().attn_decode_paged, out.data_ptr(), q.data_ptr(), k_pages.data_ptr(),
+          v_pages.data_ptr(), _dtype_code(q), B, Hq, Hkv, page_size, D, num_pages,
+          block_table.data_ptr(), max_pages, seqlens.data_ptr(), int(max_len), int(window),
+          float(scale), float(rope_theta), workspace.data_ptr(),
           workspace.numel() * workspace.element_size(), _stream(q))
     return out

@@ -27,6 +27,7 @@ SIGNATURES = {
     "attn_prefill": (I, [P, P, P, P, I, I, I, I, I, I, F, D, P]),
     "attn_decode_workspace_size": (SZ, [I, I, I, I, I]),
     "attn_decode": (I, [P, P, P, P, I, I, I, I, I, I, P, I, F, D, P, SZ, P]),
+    "attn_decode_paged": (I, [P, P, P, P, I, I, I, I, I, I, I, P, I, P, I, I, F, D, P, SZ, P]),
     "attn_status_string": (ctypes.c_char_p, [I]),
 }
 

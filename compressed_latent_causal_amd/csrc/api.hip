@@ -79,6 +79,33 @@ ATTN_API int attn_decode(void* o, const void* q, const void* k_cache, const void
                                           (hipStream_t)stream));
 }
 
+ATTN_API int attn_decode_paged(void* o, const void* q, const void* k_pages, const void* v_pages,
+                               int dtype, int B, int Hq, int Hkv, int page_size, int D,
+                               int num_pages, const int32_t* block_table, int max_pages,
+                               const int32_t* seqlens, int max_len, int window, float scale,
+                               double rope_theta, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || page_size < 32 || page_size % 32 != 0 ||
+        num_pages < 1 || max_pages < 1 || max_len < 0 ||
+        (long long)max_len > (long long)max_pages * page_size)
+        return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_BF16 || !supported_dim(D) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
+    if (!(rope_theta >= 0.0) || !isfinite(rope_theta)) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * max_pages > INT32_MAX) return ATTN_ERR_SHAPE;
+    if (B == 0) return ATTN_OK;
+    if (!o || !q || !k_pages || !v_pages || !block_table || !seqlens) return ATTN_ERR_NULL;
+    if (!aligned16(o) || !aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) ||
+        ((uintptr_t)block_table & 3u) || ((uintptr_t)seqlens & 3u))
+        return ATTN_ERR_ALIGN;
+    const size_t need = attn::decode_workspace_bytes(B, Hq, Hkv, max_len, D);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+    return hip_status(attn::launch_decode_paged(o, q, k_pages, v_pages, B, Hq, Hkv, page_size, D,
+                                                num_pages, block_table, max_pages, seqlens, max_len,
+                                                window, scale, rope_theta, workspace,
+                                                (hipStream_t)stream));
+}
+
 ATTN_API const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";

@@ -122,17 +122,39 @@ struct DecodeSmem {
     static constexpr int kMB = kSlots / (2 * DC_HEADS * 4);
 };
 
+// Where the cached keys/values live.  Contiguous: k, v [B, Hkv, S_cap, D].
+// Paged: k, v [num_pages, Hkv, page, D], and token t of sequence b is row
+// t % page of page table[b * max_pages + t / page] ("GQA y técnicas
+// relacionadas": PagedAttention's fixed-size blocks).  window > 0 limits each
+// query to the last `window` tokens (sliding-window attention, same section).
+struct DecodeCache {
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* table;
+    int S_cap;
+    int page, max_pages, num_pages;
+    int window;
+};
+
+// First token a query of a sequence of len tokens sees, and the number of
+// 32-token sub-tiles from the one holding it to the end.
+__device__ inline int decode_first_token(int len, int window) {
+    return window > 0 ? max(0, len - window) : 0;
+}
+__device__ inline int decode_subtiles(int len, int window) {
+    return ceil_div(len, DC_SUB) - decode_first_token(len, window) / DC_SUB;
+}
+
 // s_waitcnt immediates: vmcnt(n) alone, and lgkmcnt(0) alone
 constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 constexpr int kWaitLgkm0 = 0xC07F;
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ seqlens, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    unsigned long long* __restrict__ ws_tag, uint16_t* __restrict__ o, int Hq, int Hkv, int S_cap,
-    int max_len, int NC, float c, int n_hchunk, int rope, RopeFreqs fr, unsigned long long tag,
-    int B, int budget) {
+    const uint16_t* __restrict__ q, DecodeCache cache, const int32_t* __restrict__ seqlens,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, unsigned long long* __restrict__ ws_tag,
+    uint16_t* __restrict__ o, int Hq, int Hkv, int max_len, int NC, float c, int n_hchunk,
+    int rope, RopeFreqs fr, unsigned long long tag, int B, int budget) {
     constexpr int KSTEPS = D / 32, DT = D / 16;
     constexpr int ROW = D * 2;                 // bytes per cache row
     constexpr int VSUB = DC_SUB * ROW;         // bytes of one V sub-tile
@@ -146,6 +168,7 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     __shared__ float sstat[2 * DC_NW * DC_HEADS];  // waves' max and sum; then running stats
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int window = PAGED ? cache.window : 0;  // the contiguous entry point has none
 
     // ---- this workgroup's (sequence b, group gi, split chunk of nwg).  Groups
     // are numbered b-major (GPB per sequence), their workgroups consecutively.
@@ -167,7 +190,7 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        auto ns = [&](int i) { return ceil_div(ls[i], DC_SUB); };
+        auto ns = [&](int i) { return decode_subtiles(ls[i], window); };
         // every wave finds the same U, a size whose workgroup count fits the
         // budget.  With T = GPB * sum(n), count(U) is about T / U + GPB * B / 2
         // (half a workgroup of rounding per group); start there and grow U
@@ -205,7 +228,7 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
         }
         if (b < 0) return;  // past the last group's workgroups (uniform)
         len = ls[b];
-        nwg = max(1, ceil_div_est(ceil_div(len, DC_SUB), U, rU));
+        nwg = max(1, ceil_div_est(decode_subtiles(len, window), U, rU));
         const int off = (int)blockIdx.x - first;
         gi = off / nwg;
         chunk = off % nwg;
@@ -220,12 +243,14 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     const int h0 = kvh * G + hc * DC_HEADS;
     const int GH = min(DC_HEADS, G - hc * DC_HEADS);
     const int n_sub = ceil_div(len, DC_SUB);  // 32-token sub-tiles of this sequence
+    const int w0 = decode_first_token(len, window);  // first token the query sees
+    const int s0 = w0 / DC_SUB;                             // and its sub-tile
 
     const int lr = lane & 15, lg = lane >> 4;
 
-    const size_t kvb = (size_t)(b * Hkv + kvh) * S_cap * D;
-    const uint16_t* const kg = kc + kvb;
-    const uint16_t* const vg = vc + kvb;
+    const size_t kvb = PAGED ? 0 : (size_t)(b * Hkv + kvh) * cache.S_cap * D;
+    const uint16_t* const kg = cache.k + kvb;
+    const uint16_t* const vg = cache.v + kvb;
     char* const slot0 = vs0 + w * VSUB;  // this wave's two V slots
     char* const slot1 = vs1 + w * VSUB;
 
@@ -260,12 +285,33 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     // other LDS slot) are issued before the current one is computed.
     const int we = max(len, 1);  // rows at or past we - 1 re-read row we - 1 (row 0 if empty)
     const int jstep = nwg * DC_NW;
-    auto issue = [&](int j, char* slot, bf16x8_t (&kd)[2][KSTEPS]) {
+    // Page holding sub-tile j (paged cache).  A page holds whole sub-tiles,
+    // and rows past the length re-read row we - 1 of the same sub-tile, so one
+    // page serves a sub-tile.  Out-of-range table entries are clamped so that
+    // no read leaves the page pool.  Each wave looks up the page of the
+    // sub-tile after next while the current one streams, so the table read
+    // never delays a prefetch.
+    auto page_of = [&](int j) __attribute__((always_inline)) {
+        if constexpr (!PAGED) return 0;
+        const int pi = min(j * DC_SUB, we - 1) / cache.page;
+        return min(max(cache.table[(size_t)b * cache.max_pages + pi], 0), cache.num_pages - 1);
+    };
+    auto issue = [&](int j, int pg, char* slot, bf16x8_t (&kd)[2][KSTEPS]) {
         const int t0 = j * DC_SUB;
+        // rows of this sub-tile: token tok sits at base + (tok - r0) * D
+        const uint16_t* kb = kg;
+        const uint16_t* vb = vg;
+        int r0 = 0;
+        if constexpr (PAGED) {
+            const size_t off = ((size_t)pg * Hkv + kvh) * (size_t)cache.page * D;
+            kb += off;
+            vb += off;
+            r0 = min(t0, we - 1) / cache.page * cache.page;
+        }
 #pragma unroll
         for (int u = 0; u < VINST; ++u) {
             const int tok = min(t0 + vrow[u], we - 1);
-            __builtin_amdgcn_global_load_lds((const void*)(vg + (size_t)tok * D + vcol[u] * 8),
+            __builtin_amdgcn_global_load_lds((const void*)(vb + (size_t)(tok - r0) * D + vcol[u] * 8),
                                              (__attribute__((address_space(3))) void*)(slot + u * 1024),
                                              16, 0, 0);
         }
@@ -274,7 +320,7 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
             const int tok = min(t0 + 16 * mt + lr, we - 1);
 #pragma unroll
             for (int s = 0; s < KSTEPS; ++s)
-                kd[mt][s] = *(const bf16x8_t*)(kg + (size_t)tok * D + 32 * s + 8 * lg);
+                kd[mt][s] = *(const bf16x8_t*)(kb + (size_t)(tok - r0) * D + 32 * s + 8 * lg);
         }
     };
 
@@ -293,11 +339,12 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     const double freq = fr.f[lane % (D / 2)];  // loaded unconditionally, like the query
 
     bf16x8_t kA[2][KSTEPS], kB[2][KSTEPS];  // K fragments, double-buffered like V
-    int j = chunk + nwg * w;
+    int j = s0 + chunk + nwg * w;
     // unconditional, like every prefetch below, so the number of loads in
     // flight is the same on every path (a wave with no sub-tile re-reads a
     // valid row and never uses it)
-    issue(j, slot0, kA);
+    int pg_this = page_of(j), pg_next = page_of(j + jstep);  // pages of sub-tiles j, j + jstep
+    issue(j, pg_this, slot0, kA);
 
     bf16x8_t qf[KSTEPS];
     float cs_l = 1.f, sn_l = 0.f;
@@ -329,7 +376,11 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
         // number of loads in flight is the same on every path and the waits
         // can leave the prefetch outstanding.
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // vnext was read by the previous step's PV
-        issue(more ? jj + jstep : jj, vnext, kn);
+        issue(more ? jj + jstep : jj, more ? pg_next : pg_this, vnext, kn);
+        if (PAGED) {  // the next step's sub-tile and the one after it
+            pg_this = more ? pg_next : pg_this;
+            pg_next = page_of(jj + 2 * jstep);
+        }
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the products
         // this sub-tile's K and V were loaded before the prefetch's
         // VINST + 2*KSTEPS operations, and vector memory completes in order
@@ -348,7 +399,8 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (t0 + 16 * mt + 4 * lg + i >= len) sacc[mt][i] = -INFINITY;
+                const int tk = t0 + 16 * mt + 4 * lg + i;
+                if (tk >= len || (PAGED && tk < w0)) sacc[mt][i] = -INFINITY;
                 mx = __builtin_elementwise_maximum(mx, sacc[mt][i]);
             }
         mx = __builtin_elementwise_maximum(mx, xor_shfl(mx, 16));
@@ -599,11 +651,12 @@ int decode_budget(long long groups, int D) {
     return (int)std::min(budget, cap);
 }
 
-template <int D>
-hipError_t launch_decode_d(void* o, const void* q, const void* k_cache, const void* v_cache, int B,
-                           int Hq, int Hkv, int S_cap, const int32_t* seqlens, int max_len, float c,
-                           double rope_theta, void* workspace, unsigned long long tag,
-                           hipStream_t st) {
+unsigned long long next_decode_tag();
+
+template <int D, bool PAGED>
+hipError_t launch_decode_d(void* o, const void* q, const DecodeCache& cache, int B, int Hq, int Hkv,
+                           const int32_t* seqlens, int max_len, float c, double rope_theta,
+                           void* workspace, unsigned long long tag, hipStream_t st) {
     const int NC = decode_num_chunks(B, Hkv, max_len);  // partial slots per (sequence, head)
     const int G = Hq / Hkv;
     const int n_hchunk = ceil_div(G, DC_HEADS);
@@ -614,12 +667,23 @@ hipError_t launch_decode_d(void* o, const void* q, const void* k_cache, const vo
     float* const ws_o = (float*)workspace;
     float* const ws_ml = ws_o + (size_t)B * Hq * NC * D;
     unsigned long long* const ws_tag = (unsigned long long*)(ws_ml + (size_t)B * Hq * NC * 2);
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)nblocks), dim3(DC_NW * 64), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
-                       seqlens, ws_o, ws_ml, ws_tag, (uint16_t*)o, Hq, Hkv, S_cap, max_len, NC, c,
-                       n_hchunk, rope_theta > 0 ? 1 : 0,
+    hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)nblocks), dim3(DC_NW * 64), 0,
+                       st, (const uint16_t*)q, cache, seqlens, ws_o, ws_ml, ws_tag, (uint16_t*)o, Hq,
+                       Hkv, max_len, NC, c, n_hchunk, rope_theta > 0 ? 1 : 0,
                        rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D), tag, B, budget);
     return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t launch_decode_any(void* o, const void* q, const DecodeCache& cache, int B, int Hq,
+                             int Hkv, int D, const int32_t* seqlens, int max_len, float scale,
+                             double rope_theta, void* workspace, hipStream_t st) {
+    const float c = scale * kLog2e;
+    const unsigned long long tag = next_decode_tag();
+    return D == 64 ? launch_decode_d<64, PAGED>(o, q, cache, B, Hq, Hkv, seqlens, max_len, c,
+                                                rope_theta, workspace, tag, st)
+                   : launch_decode_d<128, PAGED>(o, q, cache, B, Hq, Hkv, seqlens, max_len, c,
+                                                 rope_theta, workspace, tag, st);
 }
 
 // Call tags for the partial slots: distinct for every call in the process
@@ -654,12 +718,20 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int D) {
 hipError_t launch_decode(void* o, const void* q, const void* k_cache, const void* v_cache, int B,
                          int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens, int max_len,
                          float scale, double rope_theta, void* workspace, hipStream_t st) {
-    const float c = scale * kLog2e;
-    const unsigned long long tag = next_decode_tag();
-    return D == 64 ? launch_decode_d<64>(o, q, k_cache, v_cache, B, Hq, Hkv, S_cap, seqlens, max_len,
-                                         c, rope_theta, workspace, tag, st)
-                   : launch_decode_d<128>(o, q, k_cache, v_cache, B, Hq, Hkv, S_cap, seqlens, max_len,
-                                          c, rope_theta, workspace, tag, st);
+    const DecodeCache cache{(const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr, S_cap, 0, 0, 0, 0};
+    return launch_decode_any<false>(o, q, cache, B, Hq, Hkv, D, seqlens, max_len, scale, rope_theta,
+                                    workspace, st);
+}
+
+hipError_t launch_decode_paged(void* o, const void* q, const void* k_pages, const void* v_pages,
+                               int B, int Hq, int Hkv, int page_size, int D, int num_pages,
+                               const int32_t* block_table, int max_pages, const int32_t* seqlens,
+                               int max_len, int window, float scale, double rope_theta,
+                               void* workspace, hipStream_t st) {
+    const DecodeCache cache{(const uint16_t*)k_pages, (const uint16_t*)v_pages, block_table, 0,
+                            page_size, max_pages, num_pages, window};
+    return launch_decode_any<true>(o, q, cache, B, Hq, Hkv, D, seqlens, max_len, scale, rope_theta,
+                                   workspace, st);
 }
 
 }  // namespace attn

@@ -36,4 +36,13 @@ hipError_t launch_decode(void* o, const void* q, const void* k_cache, const void
                          int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens, int max_len,
                          float scale, double rope_theta, void* workspace, hipStream_t st);
 
+// Decode over a paged cache (pages [num_pages, Hkv, page_size, D], page_size a
+// multiple of 32, block_table [B, max_pages]); window > 0 limits each query to
+// its sequence's last `window` tokens.
+hipError_t launch_decode_paged(void* o, const void* q, const void* k_pages, const void* v_pages,
+                               int B, int Hq, int Hkv, int page_size, int D, int num_pages,
+                               const int32_t* block_table, int max_pages, const int32_t* seqlens,
+                               int max_len, int window, float scale, double rope_theta,
+                               void* workspace, hipStream_t st);
+
 }  // namespace attn

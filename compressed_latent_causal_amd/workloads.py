@@ -112,6 +112,38 @@ def poison_cache_tail(cache: torch.Tensor, lens: torch.Tensor) -> None:
             cache[b, :, n:, :] = float("nan")
 
 
+def to_pages(k: torch.Tensor, v: torch.Tensor, lens: torch.Tensor, page_size: int, seed: int = 0,
+             spare_pages: int = 3):
+    """Lay a contiguous cache [B,Hkv,S,D] out as a paged one (CPU).
+
+    Returns (k_pages, v_pages, block_table): pages [num_pages,Hkv,page_size,D]
+    and table int32 [B, ceil(S/page_size)], where token t of sequence b is row
+    t % page_size of page table[b, t // page_size].  Only the pages holding a
+    sequence's first lens[b] tokens are kept, in a seeded random physical
+    order, mixed with `spare_pages` NaN pages that no table entry names; table
+    entries past a sequence's pages are -1.  Rows past a length inside its
+    last page keep the contiguous cache's values."""
+    B, Hkv, S, D = k.shape
+    mp = -(-S // page_size)
+    need = [-(-int(n) // page_size) for n in lens]
+    total = sum(need) + spare_pages
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(total, generator=g)
+    kp = torch.full((total, Hkv, page_size, D), float("nan"), dtype=k.dtype)
+    vp = torch.full_like(kp, float("nan"))
+    table = torch.full((B, mp), -1, dtype=torch.int32)
+    slot = 0
+    for b in range(B):
+        for i in range(need[b]):
+            pg = int(perm[slot])
+            slot += 1
+            lo, hi = i * page_size, min(S, (i + 1) * page_size)
+            kp[pg, :, :hi - lo] = k[b, :, lo:hi]
+            vp[pg, :, :hi - lo] = v[b, :, lo:hi]
+            table[b, i] = pg
+    return kp, vp, table
+
+
 def custom(kind: str, dtype: str, B: int, Hq: int, Hkv: int, D: int, S: int,
            theta: float = 1e4, len_lo: int = 0, len_hi: int = 0) -> Workload:
     """An ad-hoc workload (tests sweep shapes and edge cases with it)."""

@@ -1,7 +1,7 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) causal grouped-query attention
  * library: rotary position embedding, causal prefill and single-token decode
- * over a contiguous KV cache.
+ * over a contiguous or a paged KV cache.
  *
  * What is computed (pages cited by title and section):
  *  - "Grouped Query Attention (GQA)" glossary, section "Cómo funciona GQA":
@@ -141,6 +141,38 @@ int attn_decode(void *o, const void *q, const void *k_cache, const void *v_cache
                 int B, int Hq, int Hkv, int S_cap, int D, const int32_t *seqlens,
                 int max_len, float scale, double rope_theta, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/*
+ * Decode over a paged KV cache, optionally limited to a sliding window.
+ * "Grouped Query Attention (GQA)" glossary, section "GQA y técnicas
+ * relacionadas": PagedAttention keeps the cache in fixed-size blocks, whatever
+ * the number of heads, and sliding-window attention bounds the cached tokens
+ * each query sees (Mistral 7B pairs it with GQA).
+ *
+ *   q, o: [B, Hq, D];  k_pages, v_pages: [num_pages, Hkv, page_size, D];
+ *   block_table: device int32 [B, max_pages];  seqlens: device int32 [B].
+ *   Token t of sequence b is row t % page_size of page
+ *   block_table[b * max_pages + t / page_size].
+ *   window > 0: the query of sequence b sees tokens max(0, len_b - window) ..
+ *   len_b - 1;  window <= 0: all len_b tokens.
+ *   o[b,h,:] = sum_{t seen} softmax_t(scale * <q[b,h,:], k_t>) v_t, with
+ *   k_t, v_t the rows of head h / G.
+ *
+ * page_size: a positive multiple of 32.  0 <= seqlens[b] <= max_len <=
+ * max_pages * page_size (lengths are clamped to [0, max_len] on the device).
+ * Table entries of the pages a query sees must lie in [0, num_pages); the
+ * kernel clamps any other entry it reads into that range, so no read leaves
+ * the page pool (the result is then unspecified).  Pages and rows that no
+ * query sees are never read into a result.  A sequence that sees no token gets
+ * a zero row.  rope_theta, scale, dtype (BF16 only) and the workspace are as
+ * for attn_decode, with the same attn_decode_workspace_size(B, Hq, Hkv,
+ * max_len, D).  One kernel is enqueued.
+ */
+int attn_decode_paged(void *o, const void *q, const void *k_pages, const void *v_pages,
+                      int dtype, int B, int Hq, int Hkv, int page_size, int D, int num_pages,
+                      const int32_t *block_table, int max_pages, const int32_t *seqlens,
+                      int max_len, int window, float scale, double rope_theta,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *attn_status_string(int status);

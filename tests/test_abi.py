@@ -158,6 +158,41 @@ def test_decode_validation(L):
     assert d(*args(o=None, q=None, kc=None, vc=None, lens=None, ws=None, B=0)) == OK
 
 
+def test_decode_paged_validation(L):
+    d = L.attn_decode_paged
+    big = 1 << 40
+
+    def args(**kw):
+        return [kw.get("o", FAKE), kw.get("q", FAKE), kw.get("kp", FAKE), kw.get("vp", FAKE),
+                kw.get("dt", BF16), kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 2),
+                kw.get("page", 64), kw.get("D", 128), kw.get("npages", 10), kw.get("table", FAKE),
+                kw.get("max_pages", 4), kw.get("lens", FAKE), kw.get("max_len", 256),
+                kw.get("window", 0), kw.get("scale", 0.088), kw.get("theta", 0.0),
+                kw.get("ws", FAKE), kw.get("ws_bytes", big), None]
+
+    assert d(*args(Hkv=3)) == ESHAPE
+    for page in (0, 16, 48, -32):
+        assert d(*args(page=page)) == ESHAPE            # a positive multiple of 32
+    assert d(*args(npages=0)) == ESHAPE
+    assert d(*args(max_pages=0)) == ESHAPE
+    assert d(*args(max_len=257)) == ESHAPE               # beyond max_pages * page_size
+    assert d(*args(max_len=-1)) == ESHAPE
+    assert d(*args(dt=F32)) == EUNSUP
+    assert d(*args(D=96)) == EUNSUP
+    assert d(*args(scale=float("inf"))) == EUNSUP
+    assert d(*args(theta=float("inf"))) == EUNSUP
+    for name in ("o", "q", "kp", "vp", "table", "lens"):
+        assert d(*args(**{name: None})) == ENULL
+    for name in ("o", "q", "kp", "vp"):
+        assert d(*args(**{name: FAKE + 8})) == EALIGN
+    for name in ("table", "lens"):
+        assert d(*args(**{name: FAKE + 2})) == EALIGN
+    assert d(*args(ws=None)) == EWS
+    need = L.attn_decode_workspace_size(2, 8, 2, 256, 128)
+    assert d(*args(ws_bytes=need - 1)) == EWS
+    assert d(*args(B=0, o=None, q=None, kp=None, vp=None, table=None, lens=None, ws=None)) == OK
+
+
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "_HERE", str(tmp_path))

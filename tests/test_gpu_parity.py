@@ -449,6 +449,79 @@ def test_decode_edge_cases(case):
             assert (got[b] == 0).all()
 
 
+PAGED_CASES = [  # B, Hq, Hkv, S_cap, D, page_size, lengths, window
+    (9, 8, 2, 1100, 128, 64, [0, 1, 31, 32, 33, 511, 512, 513, 1100], 0),
+    (9, 8, 2, 1100, 128, 32, [0, 1, 31, 32, 33, 511, 512, 513, 1100], 0),
+    (4, 8, 8, 300, 64, 256, [300, 1, 129, 64], 0),
+    (3, 16, 2, 20000, 64, 128, [20000, 4097, 1], 0),   # several split workgroups
+    (2, 64, 2, 9000, 128, 512, [9000, 8193], 0),       # two head slices
+    (5, 8, 2, 3000, 128, 64, [3000, 1000, 64, 2, 0], 1),
+    (5, 8, 2, 3000, 128, 64, [3000, 1000, 64, 2, 0], 31),
+    (5, 8, 2, 3000, 128, 64, [3000, 1000, 64, 33, 0], 32),
+    (5, 8, 2, 3000, 64, 32, [3000, 1000, 64, 33, 0], 33),
+    (5, 8, 2, 3000, 128, 256, [3000, 1000, 64, 33, 0], 1024),
+    (2, 16, 2, 20000, 128, 256, [20000, 12000], 4096),  # windows split over workgroups
+    (70, 8, 8, 200, 64, 32, [(37 * i) % 201 for i in range(70)], 50),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES)
+def test_decode_paged_matches_oracle(case):
+    """Paged cache in shuffled page order with unreferenced NaN pages, table
+    entries past each sequence set to -1, and an optional sliding window."""
+    B, Hq, Hkv, S_cap, D, P, lens, window = case
+    g = torch.Generator().manual_seed(B * 100 + P + window)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kc = torch.randn(B, Hkv, S_cap, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Hkv, S_cap, D, generator=g).to(torch.bfloat16)
+    lt = torch.tensor(lens, dtype=torch.int32)
+    kp, vp, table = wl.to_pages(kc, vc, lt, P, seed=B + P)
+    say(f"decode paged B={B} Hq={Hq} Hkv={Hkv} S_cap={S_cap} D={D} page={P} window={window} "
+        f"lens={lens if len(lens) < 12 else str(len(lens)) + ' ragged'}")
+    o = attn.decode_paged(dev(q), dev(kp), dev(vp), dev(table), dev(lt), max_len=max(lens),
+                          window=window)
+    ref = oracle.decode_paged(bits(q), bits(kp), bits(vp),
+                              np.maximum(table.numpy(), 0), lt.numpy(), window=window)
+    got = host_f64(o)
+    assert_close(got, ref, BF16_MAX, BF16_MEAN, what=f"decode paged {case[:6]} window {window}")
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert (got[b] == 0).all()
+
+
+def test_decode_paged_in_order_equals_contiguous_decode_bitwise():
+    """The gqa_decode workload laid out as 256-token pages in order: the
+    paged path reads the same rows in the same split, so it agrees bitwise."""
+    w = wl.WORKLOADS["gqa_decode"]
+    q, kc, vc, lens = wl.make_decode(w, seed=0)
+    B, Hkv, S, D = kc.shape
+    P = 256
+    kp = kc.reshape(B, Hkv, S // P, P, D).permute(0, 2, 1, 3, 4).contiguous().reshape(-1, Hkv, P, D)
+    vp = vc.reshape(B, Hkv, S // P, P, D).permute(0, 2, 1, 3, 4).contiguous().reshape(-1, Hkv, P, D)
+    table = torch.arange(B * (S // P), dtype=torch.int32).reshape(B, S // P)
+    say("decode paged in order vs contiguous, gqa_decode")
+    ld = dev(lens)
+    cont = attn.decode(dev(q), dev(kc), dev(vc), ld, rope_theta=w.theta)
+    paged = attn.decode_paged(dev(q), dev(kp), dev(vp), dev(table), ld, rope_theta=w.theta)
+    assert torch.equal(cont, paged)
+
+
+def test_decode_paged_fused_rope_equals_separate_rope():
+    B, Hq, Hkv, S_cap, D, P = 3, 16, 2, 700, 128, 64
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kc = torch.randn(B, Hkv, S_cap, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Hkv, S_cap, D, generator=g).to(torch.bfloat16)
+    lt = torch.tensor([700, 65, 1], dtype=torch.int32)
+    kp, vp, table = wl.to_pages(kc, vc, lt, P, seed=9)
+    ld, tb = dev(lt), dev(table)
+    say("decode paged fused RoPE vs separate, window 100")
+    qr = attn.rope(dev(q).unsqueeze(2), 5e5, ld, pos_shift=-1).squeeze(2)
+    sep = attn.decode_paged(qr, dev(kp), dev(vp), tb, ld, window=100)
+    fused = attn.decode_paged(dev(q), dev(kp), dev(vp), tb, ld, window=100, rope_theta=5e5)
+    assert torch.equal(sep, fused)
+
+
 def test_decode_ignores_workspace_contents_and_default_max_len():
     B, Hq, Hkv, S_cap, D = 3, 8, 2, 600, 128
     q, kc, vc = rand_bf16((B, Hq, D), 20), rand_bf16((B, Hkv, S_cap, D), 21), rand_bf16((B, Hkv, S_cap, D), 22)
