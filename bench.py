@@ -150,18 +150,23 @@ def bench_prefill(w, steps, warmup):
     return wall * 1e3 / steps, sum(kern_ms) / len(kern_ms), sorted(kern_ms)
 
 
-def bench_decode(w, iters, warmup, layers):
+def bench_decode(w, iters, warmup, layers, page_size=0):
     """One decode step of a `layers`-layer model: the same call on `layers`
     distinct KV caches back to back (as a serving step walks its layers), the
     whole group timed with HIP events.  Together the caches far exceed the
     L2 and memory-side caches, and a 1 GiB read before every timed group evicts
-    them too, so every layer reads its cache from HBM."""
+    them too, so every layer reads its cache from HBM.  page_size > 0 lays each
+    cache out as pages of that many tokens in a shuffled physical order and
+    runs the paged entry point."""
     import torch
     import compressed_latent_causal_amd as attn
     from compressed_latent_causal_amd import workloads as wl
 
     q, kc, vc, lens = wl.make_decode(w, seed=0)
     qd, ld = q.cuda(), lens.cuda()
+    if page_size:
+        kc, vc, table = wl.to_pages(kc, vc, lens, page_size, seed=1, spare_pages=0)
+        tb = table.cuda()
     kcs = [kc.cuda() for _ in range(layers)]  # same values, distinct memory
     vcs = [vc.cuda() for _ in range(layers)]
     del kc, vc
@@ -175,8 +180,12 @@ def bench_decode(w, iters, warmup, layers):
 
     def step():  # RoPE of the new query is fused into the decode kernel
         for l in range(layers):
-            attn.decode(qd, kcs[l], vcs[l], ld, max_len=w.S, scale=w.scale, rope_theta=w.theta,
-                        out=o, workspace=ws)
+            if page_size:
+                attn.decode_paged(qd, kcs[l], vcs[l], tb, ld, max_len=w.S, scale=w.scale,
+                                  rope_theta=w.theta, out=o, workspace=ws)
+            else:
+                attn.decode(qd, kcs[l], vcs[l], ld, max_len=w.S, scale=w.scale,
+                            rope_theta=w.theta, out=o, workspace=ws)
 
     settle(step, 0.5)
     for _ in range(warmup):
@@ -196,7 +205,9 @@ def bench_decode(w, iters, warmup, layers):
     nbytes = decode_bytes(lens.tolist(), w.Hkv, w.D)
     gbs = nbytes / (med * 1e-3) / 1e9
     return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
-            "head_dim": w.D, "cache_capacity": w.S, "sum_len": int(lens.sum()),
+            "head_dim": w.D, "cache_capacity": w.S,
+            "cache": f"paged, {page_size}-token pages in shuffled order" if page_size else "contiguous",
+            "sum_len": int(lens.sum()),
             "kv_bytes_per_layer": nbytes, "layers": layers, "ms_per_layer_median": round(med, 5),
             "ms_per_layer_min": round(ms[0], 5), "GB_per_s": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "iters": iters,
@@ -204,6 +215,10 @@ def bench_decode(w, iters, warmup, layers):
 
 
 DECODE_LAYERS = {"gqa_decode": 4, "long_decode": 8}  # 4 GiB of caches either way
+# (reported name, workload, page size): the paged line reads the gqa workload's
+# cache through 256-token pages
+DECODE_LINES = [("gqa_decode", "gqa_decode", 0), ("long_decode", "long_decode", 0),
+                ("gqa_decode_paged256", "gqa_decode", 256)]
 
 
 def cpu_baseline(w, budget_s=15.0):
@@ -253,7 +268,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "gqa_decode", "long_decode", "ccgqa_prefill", "copy"],
+    ap.add_argument("--only", choices=["prefill", "gqa_decode", "long_decode", "gqa_decode_paged256",
+                                       "ccgqa_prefill", "copy"],
                     help="time one workload alone and print its line (profiling runs; `copy` is "
                          "the plain copy that calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -273,9 +289,11 @@ def main():
     if args.only == "copy":
         print(json.dumps(bench_copy()), flush=True)
         return
-    if args.only in ("gqa_decode", "long_decode"):
-        d = bench_decode(wl.WORKLOADS[args.only], args.decode_iters, args.warmup,
-                         DECODE_LAYERS[args.only])
+    lines = {name: (wname, page) for name, wname, page in DECODE_LINES}
+    if args.only in lines:
+        wname, page = lines[args.only]
+        d = bench_decode(wl.WORKLOADS[wname], args.decode_iters, args.warmup,
+                         DECODE_LAYERS[wname], page)
         print(json.dumps(d), flush=True)
         return
     w = wl.WORKLOADS["ccgqa_prefill" if args.only == "ccgqa_prefill" else "llama8b_prefill"]
@@ -312,8 +330,8 @@ def main():
         return
     if not args.no_decode:
         dec = {}
-        for name in ("gqa_decode", "long_decode"):
-            d = bench_decode(wl.WORKLOADS[name], args.decode_iters, 3, DECODE_LAYERS[name])
+        for name, wname, page in DECODE_LINES:
+            d = bench_decode(wl.WORKLOADS[wname], args.decode_iters, 3, DECODE_LAYERS[wname], page)
             log(f"decode {name}: {d['ms_per_layer_median']:.4f} ms per layer, {d['GB_per_s']:.0f} GB/s")
             dec[name] = d
         result["decode"] = dec

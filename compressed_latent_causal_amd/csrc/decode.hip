@@ -1,4 +1,5 @@
-// Single-token grouped-query decode over a contiguous KV cache, for gfx950.
+// Single-token grouped-query decode over a contiguous or paged KV cache, for
+// gfx950.
 //
 // What is computed ("Grouped Query Attention (GQA)" glossary, sections "Cómo
 // funciona GQA" and "Por qué GQA reduce la caché KV"): each sequence's new
@@ -36,6 +37,16 @@
 // writes the output, so one launch does the whole step.  Cache slots at or past a
 // sequence's length never reach the result: loads of rows past it re-read the
 // last valid row (row 0 of an empty sequence) and their scores are masked.
+//
+// Paged caches (same glossary, section "GQA y técnicas relacionadas":
+// PagedAttention's fixed-size blocks, and sliding-window attention) use the
+// same kernel, instantiated with PAGED: a sub-tile's 32 rows never straddle a
+// page (page sizes are multiples of 32), so only the row base changes, taken
+// from the sequence's block-table entry, which each wave fetches one sub-tile
+// ahead so the lookup's latency stays off the load path.  A window of w tokens
+// starts the sequence's sub-tiles at the one holding token len - w and masks
+// the keys before it; the split counts only the sub-tiles a query sees.  The
+// contiguous instantiation compiles all of this out.
 #include <algorithm>
 #include <atomic>
 #include <chrono>

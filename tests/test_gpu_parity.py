@@ -462,6 +462,8 @@ PAGED_CASES = [  # B, Hq, Hkv, S_cap, D, page_size, lengths, window
     (5, 8, 2, 3000, 128, 256, [3000, 1000, 64, 33, 0], 1024),
     (2, 16, 2, 20000, 128, 256, [20000, 12000], 4096),  # windows split over workgroups
     (70, 8, 8, 200, 64, 32, [(37 * i) % 201 for i in range(70)], 50),
+    (3, 16, 1, 2000, 128, 64, [2000, 777, 5], 100),     # MQA
+    (3, 8, 2, 500, 64, 64, [500, 100, 1], 4096),        # window wider than every length
 ]
 
 
