@@ -75,6 +75,13 @@ def _load():
             lib.oracle_decode_paged.argtypes = [P, P, P, P, i, i, i, i, i, i, i, P, i, P, i,
                                                 ctypes.c_double]
             lib.oracle_decode_paged.restype = i
+            lib.oracle_prefill_lse.argtypes = [P, P, P, i, i, i, i, i, i, ctypes.c_double, P,
+                                               ctypes.c_int64]
+            lib.oracle_prefill_lse.restype = i
+            lib.oracle_prefill_backward.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i,
+                                                    ctypes.c_double, P, ctypes.c_int64, P,
+                                                    ctypes.c_int64]
+            lib.oracle_prefill_backward.restype = i
             lib.oracle_round_bf16.argtypes = [P, P, ctypes.c_size_t]
             lib.oracle_round_bf16.restype = None
             lib.oracle_round_f32.argtypes = [P, P, ctypes.c_size_t]
@@ -259,3 +266,76 @@ def kv_values_per_token(n_kv_heads: int, head_dim: int, n_layers: int = 1) -> in
 def kv_cache_bytes(n_kv_heads: int, head_dim: int, n_tokens: int, n_layers: int = 1,
                    bytes_per_value: int = 2) -> int:
     return kv_values_per_token(n_kv_heads, head_dim, n_layers) * n_tokens * bytes_per_value
+
+
+# ---------------------------------------------------------------------------
+# training: log-normaliser and backward pass
+# ---------------------------------------------------------------------------
+def prefill_lse(q: np.ndarray, k: np.ndarray, scale: float | None = None,
+                rows: np.ndarray | None = None) -> np.ndarray:
+    """Log-normaliser of causal prefill rows, log sum_{t<=i} exp(scale <q_i, k_t>)
+    (natural log).  rows=None: fp64 [B,Hq,S]; else fp64 [len(rows)] for flat
+    row indices (b*Hq+h)*S+i."""
+    dt = _dtype_of(q)
+    q, k = (_as_input(t, dt) for t in (q, k))
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or Hq % Hkv:
+        raise ValueError("bad shapes")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if rows is None:
+        out = np.empty((B, Hq, S), dtype=np.float64)
+        r_ptr, n = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty(rows.size, dtype=np.float64)
+        r_ptr, n = _ptr(rows), rows.size
+    rc = _load().oracle_prefill_lse(_ptr(out), _ptr(q), _ptr(k), _DT_CODE[dt], B, Hq, Hkv, S,
+                                    D, float(scale), r_ptr, n)
+    if rc:
+        raise RuntimeError(f"oracle_prefill_lse failed ({rc})")
+    return out
+
+
+def prefill_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                     scale: float | None = None, q_rows: np.ndarray | None = None,
+                     k_rows: np.ndarray | None = None, want_dq: bool = True,
+                     want_dkv: bool = True):
+    """Gradients (dq, dk, dv) of sum <dout, prefill(q, k, v)>, fp64.
+
+    Full tensors by default ([B,Hq,S,D], [B,Hkv,S,D], [B,Hkv,S,D]); q_rows
+    (flat (b*Hq+h)*S+i) or k_rows (flat (b*Hkv+j)*S+t) select rows instead, and
+    want_dq / want_dkv skip a side (returned as None)."""
+    dt = _dtype_of(q)
+    q, k, v, dout = (_as_input(t, dt) for t in (q, k, v, dout))
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape or dout.shape != q.shape or Hq % Hkv:
+        raise ValueError("bad shapes")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    dq = dk = dv = None
+    qr = kr = None
+    nq = nk = 0
+    if want_dq:
+        if q_rows is None:
+            dq = np.empty((B, Hq, S, D), dtype=np.float64)
+        else:
+            qr = np.ascontiguousarray(q_rows, dtype=np.int64)
+            nq = qr.size
+            dq = np.empty((nq, D), dtype=np.float64)
+    if want_dkv:
+        if k_rows is None:
+            dk = np.empty((B, Hkv, S, D), dtype=np.float64)
+        else:
+            kr = np.ascontiguousarray(k_rows, dtype=np.int64)
+            nk = kr.size
+            dk = np.empty((nk, D), dtype=np.float64)
+        dv = np.empty_like(dk)
+    rc = _load().oracle_prefill_backward(_ptr(dq), _ptr(dk), _ptr(dv), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(dout), _DT_CODE[dt], B, Hq, Hkv, S, D, float(scale),
+                                         _ptr(qr), nq, _ptr(kr), nk)
+    if rc:
+        raise RuntimeError(f"oracle_prefill_backward failed ({rc})")
+    return dq, dk, dv

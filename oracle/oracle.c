@@ -354,3 +354,219 @@ int oracle_decode_paged(double *out, const void *q, const void *k_pages, const v
     return bad;
 }
 
+
+/* ------------------------------------------------------------------ */
+/* Training: log-normaliser of the forward and the backward pass       */
+/* ------------------------------------------------------------------ */
+/* The "Compressed Convolutional Attention" summary ("Resultaten") reports the
+ * backward pass of the same attention; the pages give no formulas for it, so
+ * what follows is the chain rule applied to the forward definition above.
+ * For query row i of head h (key/value head j = h / G) with scores
+ * s_t = scale * <q_i, k_t>, t <= i, and loss gradient dout_i = dL/do_i:
+ *   lse_i  = log sum_{t<=i} exp(s_t)            p_t = exp(s_t - lse_i)
+ *   o_i    = sum_t p_t v_t
+ *   dL/dv_t  gets  p_t * dout_i                  (from o_i = sum_t p_t v_t)
+ *   dp_t   = <dout_i, v_t>                        (dL/dp_t)
+ *   ds_t   = p_t * (dp_t - sum_u p_u dp_u)        (softmax Jacobian)
+ *   dL/dq_i  = scale * sum_t ds_t k_t
+ *   dL/dk_t gets scale * ds_t * q_i
+ * A key/value head's gradient collects these over every query head of its
+ * group and every query that sees it (i >= t). */
+
+/* Row statistics of causal prefill row (b, h, i) = flat row r:
+ * lse = log sum_{t<=i} exp(s_t) and delta = sum_t p_t <dout_i, v_t>.
+ * With dout NULL only lse is formed (delta = 0).  sc: scratch of i+1 doubles. */
+static void row_lse_delta(const void *q, const void *k, const void *v, const void *dout,
+                          int dt, int Hq, int Hkv, int S, int D, double scale, int64_t r,
+                          double *sc, double *lse_out, double *delta_out)
+{
+    const int i = (int)(r % S);
+    const int h = (int)((r / S) % Hq);
+    const int b = (int)(r / ((int64_t)S * Hq));
+    const int j = h / (Hq / Hkv);
+    const size_t qrow = (size_t)r * D;
+    const size_t kv0 = (((size_t)b * Hkv + j) * S) * (size_t)D;
+    double top = -INFINITY;
+    for (int t = 0; t <= i; ++t) {
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+            acc += load(q, qrow + d, dt) * load(k, kv0 + (size_t)t * D + d, dt);
+        sc[t] = acc * scale;
+        if (sc[t] > top)
+            top = sc[t];
+    }
+    double z = 0.0;
+    for (int t = 0; t <= i; ++t)
+        z += exp(sc[t] - top);
+    const double lse = top + log(z);
+    double delta = 0.0;
+    if (dout) {
+        for (int t = 0; t <= i; ++t) {
+            double dp = 0.0;
+            for (int d = 0; d < D; ++d)
+                dp += load(dout, qrow + d, dt) * load(v, kv0 + (size_t)t * D + d, dt);
+            delta += exp(sc[t] - lse) * dp;
+        }
+    }
+    *lse_out = lse;
+    *delta_out = delta;
+}
+
+/* Log-normaliser of causal prefill rows: lse[(b*Hq + h)*S + i] =
+ * log sum_{t<=i} exp(scale * <q[b,h,i], k[b,h/G,t]>).  rows: NULL for every
+ * row (lse is [B, Hq, S]); else n_rows flat row indices and lse is [n_rows]. */
+int oracle_prefill_lse(double *lse, const void *q, const void *k, int dt, int B, int Hq,
+                       int Hkv, int S, int D, double scale, const int64_t *rows,
+                       int64_t n_rows)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || Hq % Hkv != 0)
+        return 1;
+    const int64_t total = rows ? n_rows : (int64_t)B * Hq * S;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *sc = (double *)malloc(sizeof(double) * (size_t)S);
+        if (!sc) {
+#pragma omp atomic write
+            bad = 2;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t n = 0; n < total; ++n) {
+                const int64_t r = rows ? rows[n] : n;
+                double unused;
+                if (r < 0 || r >= (int64_t)B * Hq * S)
+                    continue;
+                row_lse_delta(q, k, NULL, NULL, dt, Hq, Hkv, S, D, scale, r, sc, &lse[n],
+                              &unused);
+            }
+            free(sc);
+        }
+    }
+    return bad;
+}
+
+/* Gradients of L = sum <dout, prefill(q, k, v)> for causal grouped-query
+ * prefill (shapes as oracle_prefill, dout like q).
+ *   dq: [B, Hq, S, D] or, with q_rows, [n_q, D] for the listed flat query rows
+ *       ((b*Hq + h)*S + i);
+ *   dk, dv: [B, Hkv, S, D] or, with k_rows, [n_k, D] for the listed flat
+ *       key rows ((b*Hkv + j)*S + t).
+ * dq may be NULL (no query rows) and dk/dv NULL together (no key rows).
+ * Row statistics (lse, delta) are formed first for every query row a result
+ * needs: the listed query rows, and every row of a group that has a listed key
+ * row. */
+int oracle_prefill_backward(double *dq, double *dk, double *dv, const void *q, const void *k,
+                            const void *v, const void *dout, int dt, int B, int Hq, int Hkv,
+                            int S, int D, double scale, const int64_t *q_rows, int64_t n_q,
+                            const int64_t *k_rows, int64_t n_k)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || Hq % Hkv != 0)
+        return 1;
+    if ((dk == NULL) != (dv == NULL))
+        return 1;
+    const int G = Hq / Hkv;
+    const int64_t nrows = (int64_t)B * Hq * S;
+    const int64_t nq = dq ? (q_rows ? n_q : nrows) : 0;
+    const int64_t nk = dk ? (k_rows ? n_k : (int64_t)B * Hkv * S) : 0;
+    for (int64_t n = 0; q_rows && n < nq; ++n)
+        if (q_rows[n] < 0 || q_rows[n] >= nrows)
+            return 3;
+    for (int64_t n = 0; k_rows && n < nk; ++n)
+        if (k_rows[n] < 0 || k_rows[n] >= (int64_t)B * Hkv * S)
+            return 3;
+
+    /* which query rows need their statistics */
+    double *lse = (double *)malloc(sizeof(double) * (size_t)nrows);
+    double *delta = (double *)malloc(sizeof(double) * (size_t)nrows);
+    unsigned char *need = (unsigned char *)calloc((size_t)nrows, 1);
+    unsigned char *grp = (unsigned char *)calloc((size_t)B * Hkv, 1);
+    if (!lse || !delta || !need || !grp) {
+        free(lse);
+        free(delta);
+        free(need);
+        free(grp);
+        return 2;
+    }
+    for (int64_t n = 0; n < nq; ++n)
+        need[q_rows ? q_rows[n] : n] = 1;
+    for (int64_t n = 0; n < nk; ++n)
+        grp[(k_rows ? k_rows[n] : n) / S] = 1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (grp[(r / S / Hq) * Hkv + (r / S % Hq) / G])
+            need[r] = 1;
+
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *sc = (double *)malloc(sizeof(double) * (size_t)S);
+        if (!sc) {
+#pragma omp atomic write
+            bad = 2;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < nrows; ++r)
+                if (need[r])
+                    row_lse_delta(q, k, v, dout, dt, Hq, Hkv, S, D, scale, r, sc, &lse[r],
+                                  &delta[r]);
+
+            /* dq rows: scale * sum_{t<=i} ds_t k_t */
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t n = 0; n < nq; ++n) {
+                const int64_t r = q_rows ? q_rows[n] : n;
+                const int i = (int)(r % S);
+                const int h = (int)((r / S) % Hq);
+                const int b = (int)(r / ((int64_t)S * Hq));
+                const size_t kv0 = (((size_t)b * Hkv + h / G) * S) * (size_t)D;
+                double *g = dq + (size_t)n * D;
+                for (int d = 0; d < D; ++d)
+                    g[d] = 0.0;
+                for (int t = 0; t <= i; ++t) {
+                    double s = 0.0, dp = 0.0;
+                    for (int d = 0; d < D; ++d) {
+                        s += load(q, (size_t)r * D + d, dt) * load(k, kv0 + (size_t)t * D + d, dt);
+                        dp += load(dout, (size_t)r * D + d, dt) * load(v, kv0 + (size_t)t * D + d, dt);
+                    }
+                    const double p = exp(s * scale - lse[r]);
+                    const double ds = p * (dp - delta[r]);
+                    for (int d = 0; d < D; ++d)
+                        g[d] += scale * ds * load(k, kv0 + (size_t)t * D + d, dt);
+                }
+            }
+
+            /* dk, dv rows: over the group's query heads and the queries i >= t */
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t n = 0; n < nk; ++n) {
+                const int64_t kr = k_rows ? k_rows[n] : n;
+                const int t = (int)(kr % S);
+                const int j = (int)((kr / S) % Hkv);
+                const int b = (int)(kr / ((int64_t)S * Hkv));
+                const size_t krow = (size_t)kr * D;
+                double *gk = dk + (size_t)n * D;
+                double *gv = dv + (size_t)n * D;
+                for (int d = 0; d < D; ++d)
+                    gk[d] = gv[d] = 0.0;
+                for (int h = j * G; h < (j + 1) * G; ++h)
+                    for (int i = t; i < S; ++i) {
+                        const int64_t r = ((int64_t)b * Hq + h) * S + i;
+                        double s = 0.0, dp = 0.0;
+                        for (int d = 0; d < D; ++d) {
+                            s += load(q, (size_t)r * D + d, dt) * load(k, krow + d, dt);
+                            dp += load(dout, (size_t)r * D + d, dt) * load(v, krow + d, dt);
+                        }
+                        const double p = exp(s * scale - lse[r]);
+                        const double ds = p * (dp - delta[r]);
+                        for (int d = 0; d < D; ++d) {
+                            gk[d] += scale * ds * load(q, (size_t)r * D + d, dt);
+                            gv[d] += p * load(dout, (size_t)r * D + d, dt);
+                        }
+                    }
+            }
+            free(sc);
+        }
+    }
+    free(lse);
+    free(delta);
+    free(need);
+    free(grp);
+    return bad;
+}

@@ -39,6 +39,17 @@ MUTANTS = {
     "window_off_by_one": ("? len - window : 0;\n                double *o",
                           "? len - window + 1 : 0;\n                double *o"),
     "paged_normalisation": ("o[d] = o[d] / l;", "o[d] = o[d];"),
+    "lse_without_log": ("const double lse = top + log(z);", "const double lse = top;"),
+    "backward_drops_delta": ("delta += exp(sc[t] - lse) * dp;", "delta += 0.0 * dp;"),
+    "dq_missing_scale": ("g[d] += scale * ds * load(k,", "g[d] += ds * load(k,"),
+    "dq_from_values": ("g[d] += scale * ds * load(k,", "g[d] += scale * ds * load(v,"),
+    "dq_sees_one_key_less": ("for (int t = 0; t <= i; ++t) {\n                    double s = 0.0",
+                             "for (int t = 0; t < i; ++t) {\n                    double s = 0.0"),
+    "dk_missing_scale": ("gk[d] += scale * ds *", "gk[d] += ds *"),
+    "dv_weighted_by_ds": ("gv[d] += p * load(dout,", "gv[d] += ds * load(dout,"),
+    "dkv_first_head_only": ("for (int h = j * G; h < (j + 1) * G; ++h)",
+                            "for (int h = j * G; h < j * G + 1; ++h)"),
+    "dkv_skips_own_query": ("for (int i = t; i < S; ++i)", "for (int i = t + 1; i < S; ++i)"),
 }
 
 

@@ -516,3 +516,128 @@ def test_round_bf16_does_not_round_twice():
     # the midpoint; direct rounding must still go up
     x = 1.0 + 2.0 ** -8 + 2.0 ** -30
     assert oracle.round_bf16(np.array([x]))[0] == 0x3F81
+
+
+# ---------------------------------------------------------------------------
+# Training: log-normaliser and backward pass
+# ---------------------------------------------------------------------------
+def _bwd_inputs(B, Hq, Hkv, S, D, seed):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal((B, Hq, S, D)), g.standard_normal((B, Hkv, S, D)),
+            g.standard_normal((B, Hkv, S, D)), g.standard_normal((B, Hq, S, D)))
+
+
+def test_lse_matches_torch_logsumexp_of_masked_scores():
+    q, k, _, _ = _bwd_inputs(2, 6, 3, 11, 8, 40)
+    scale = 0.7
+    kr = np.repeat(k, 2, axis=1)  # key head h // 2 for query head h
+    s = torch.from_numpy(np.einsum("bhid,bhtd->bhit", q, kr) * scale)
+    s = s.masked_fill(torch.ones(11, 11, dtype=torch.bool).triu(1), float("-inf"))
+    assert np.allclose(oracle.prefill_lse(q, k, scale=scale),
+                       torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_lse_zero_scale_is_log_of_the_number_of_keys_seen():
+    q, k, _, _ = _bwd_inputs(1, 2, 1, 9, 4, 41)
+    lse = oracle.prefill_lse(q, k, scale=0.0)
+    assert np.allclose(lse, np.log(np.arange(1, 10))[None, None, :], rtol=0, atol=1e-15)
+
+
+def test_lse_first_row_is_the_first_score_and_rows_select():
+    q, k, _, _ = _bwd_inputs(2, 4, 2, 7, 6, 42)
+    lse = oracle.prefill_lse(q, k)
+    first = np.einsum("bhd,bhd->bh", q[:, :, 0], np.repeat(k[:, :, 0], 2, axis=1)) / np.sqrt(6)
+    assert np.allclose(lse[:, :, 0], first, rtol=0, atol=1e-14)
+    rows = np.array([0, 13, 55, 9])
+    assert np.array_equal(oracle.prefill_lse(q, k, rows=rows), lse.reshape(-1)[rows])
+
+
+BWD_GEOMS = [(1, 4, 2, 9, 8), (2, 3, 1, 6, 4), (1, 2, 2, 7, 6), (2, 8, 2, 5, 16)]
+
+
+@pytest.mark.parametrize("geom", BWD_GEOMS)
+def test_backward_matches_torch_autograd(geom):
+    """torch's own gradients of float64 SDPA (is_causal, enable_gqa) on the CPU."""
+    B, Hq, Hkv, S, D = geom
+    q, k, v, do = _bwd_inputs(B, Hq, Hkv, S, D, 43)
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+    o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, enable_gqa=True, scale=0.6)
+    (o * torch.from_numpy(do)).sum().backward()
+    dq, dk, dv = oracle.prefill_backward(q, k, v, do, scale=0.6)
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v"])
+def test_backward_matches_finite_differences_of_the_forward(which):
+    """Central differences of L = <dout, prefill(q, k, v)> along a random
+    direction, with the oracle's own forward (no backward formula involved)."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 8, 6
+    q, k, v, do = _bwd_inputs(B, Hq, Hkv, S, D, 44)
+    dq, dk, dv = oracle.prefill_backward(q, k, v, do)
+    x = {"q": q, "k": k, "v": v}
+    grad = {"q": dq, "k": dk, "v": dv}[which]
+    u = np.random.default_rng(45).standard_normal(x[which].shape)
+    eps = 1e-5
+
+    def loss(sign):
+        y = dict(x)
+        y[which] = x[which] + sign * eps * u
+        return float((oracle.prefill(y["q"], y["k"], y["v"]) * do).sum())
+
+    fd = (loss(+1) - loss(-1)) / (2 * eps)
+    assert abs(fd - float((grad * u).sum())) <= 1e-7 * max(1.0, abs(fd))
+
+
+def test_backward_single_token_moves_only_the_values():
+    """One token: p = 1, so scores get no gradient and dv sums the group's dout."""
+    q, k, v, do = _bwd_inputs(2, 6, 2, 1, 8, 46)
+    dq, dk, dv = oracle.prefill_backward(q, k, v, do)
+    assert np.abs(dq).max() < 1e-15 and np.abs(dk).max() < 1e-15
+    assert np.allclose(dv, do.reshape(2, 2, 3, 1, 8).sum(axis=2), rtol=0, atol=1e-15)
+
+
+def test_backward_zero_scale_gives_suffix_means_of_dout():
+    """scale 0: p_it = 1/(i+1) and scores get no gradient."""
+    S = 7
+    q, k, v, do = _bwd_inputs(1, 4, 2, S, 4, 47)
+    dq, dk, dv = oracle.prefill_backward(q, k, v, do, scale=0.0)
+    assert np.abs(dq).max() == 0 and np.abs(dk).max() == 0
+    w = do / np.arange(1, S + 1)[None, None, :, None]
+    suffix = w[:, :, ::-1].cumsum(axis=2)[:, :, ::-1]  # sum over i >= t
+    assert np.allclose(dv, suffix.reshape(1, 2, 2, S, 4).sum(axis=2), rtol=0, atol=1e-14)
+
+
+def test_backward_gqa_equals_mha_with_group_sums():
+    """GQA gradients = MHA gradients on repeat-interleaved K/V, with each KV
+    head's gradient summed over its copies."""
+    B, Hq, Hkv, S, D = 2, 6, 2, 6, 4
+    q, k, v, do = _bwd_inputs(B, Hq, Hkv, S, D, 48)
+    G = Hq // Hkv
+    dq, dk, dv = oracle.prefill_backward(q, k, v, do)
+    mq, mk, mv = oracle.prefill_backward(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), do)
+    assert np.allclose(dq, mq, rtol=0, atol=1e-13)
+    assert np.allclose(dk, mk.reshape(B, Hkv, G, S, D).sum(axis=2), rtol=0, atol=1e-13)
+    assert np.allclose(dv, mv.reshape(B, Hkv, G, S, D).sum(axis=2), rtol=0, atol=1e-13)
+
+
+def test_backward_row_subsets_equal_the_full_result():
+    B, Hq, Hkv, S, D = 2, 4, 2, 9, 8
+    q, k, v, do = _bwd_inputs(B, Hq, Hkv, S, D, 49)
+    dq, dk, dv = oracle.prefill_backward(q, k, v, do)
+    qr, kr = np.array([70, 0, 8, 33]), np.array([35, 0, 9, 17])
+    sq, sk, sv = oracle.prefill_backward(q, k, v, do, q_rows=qr, k_rows=kr)
+    assert np.array_equal(sq, dq.reshape(-1, D)[qr])
+    assert np.array_equal(sk, dk.reshape(-1, D)[kr])
+    assert np.array_equal(sv, dv.reshape(-1, D)[kr])
+    only_q = oracle.prefill_backward(q, k, v, do, q_rows=qr, want_dkv=False)
+    assert only_q[1] is None and np.array_equal(only_q[0], sq)
+
+
+def test_backward_widens_bf16_inputs_exactly():
+    q, k, v, do = _bwd_inputs(1, 4, 2, 6, 8, 50)
+    bits = [oracle.round_bf16(x) for x in (q, k, v, do)]
+    got = oracle.prefill_backward(*bits)
+    ref = oracle.prefill_backward(*[oracle.widen(x) for x in bits])
+    for a, b in zip(got, ref):
+        assert np.array_equal(a, b)
