@@ -6,7 +6,10 @@ PyTorch supplies device memory and the current stream.  There is no CPU
 fallback: calling into the library without the built ``libattn.so`` raises.
 
     rope(x, theta, pos_offset=None, pos_shift=0, out=None)
-    prefill(q, k, v, scale=None, out=None)
+    prefill(q, k, v, scale=None, out=None, rope_theta=0.0)
+    prefill_lse(q, k, v, scale=None, out=None, lse=None, rope_theta=0.0)
+    prefill_backward(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None, workspace=None)
+    prefill_backward_workspace_size(B, Hq, S)
     decode(q, k_cache, v_cache, seqlens, max_len=None, scale=None, rope_theta=0.0, out=None,
            workspace=None)
     decode_workspace_size(B, Hq, Hkv, max_len, D)
@@ -22,7 +25,8 @@ from ._lib import (  # noqa: F401
     AttnError, lib, lib_path, DTYPE_CODES, STATUS,
 )
 
-__all__ = ["rope", "prefill", "decode", "decode_paged", "decode_workspace_size", "AttnError", "lib_path"]
+__all__ = ["rope", "prefill", "prefill_lse", "prefill_backward", "prefill_backward_workspace_size",
+           "decode", "decode_paged", "decode_workspace_size", "AttnError", "lib_path"]
 
 
 def _torch():
@@ -102,6 +106,71 @@ def prefill(q, k, v, scale: float | None = None, out=None, rope_theta: float = 0
     _call(lib().attn_prefill, out.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
           _dtype_code(q), B, Hq, Hkv, S, D, float(scale), float(rope_theta), _stream(q))
     return out
+
+
+def _check_prefill_shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,Hq,S,D] and k, v [B,Hkv,S,D]")
+    B, Hq, S, D = q.shape
+    if k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
+        raise ValueError("k/v must be [B,Hkv,S,D] with q's B, S and D")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    return B, Hq, k.shape[1], S, D
+
+
+def prefill_lse(q, k, v, scale: float | None = None, out=None, lse=None, rope_theta: float = 0.0):
+    """prefill() that also returns each row's log-normaliser (bf16 only):
+    (o [B,Hq,S,D], lse float32 [B,Hq,S]), lse = log sum_t exp(scale <q_i, k_t>)."""
+    torch = _torch()
+    B, Hq, Hkv, S, D = _check_prefill_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, S):
+        raise ValueError("lse must be float32 [B, Hq, S]")
+    _check_dev(q, k, v, out, lse)
+    _call(lib().attn_prefill_lse, out.data_ptr(), lse.data_ptr(), q.data_ptr(), k.data_ptr(),
+          v.data_ptr(), _dtype_code(q), B, Hq, Hkv, S, D, float(scale), float(rope_theta),
+          _stream(q))
+    return out, lse
+
+
+def prefill_backward_workspace_size(B: int, Hq: int, S: int) -> int:
+    return int(lib().attn_prefill_backward_workspace_size(B, Hq, S))
+
+
+def prefill_backward(q, k, v, o, dout, lse, scale: float | None = None, dq=None, dk=None, dv=None,
+                     workspace=None):
+    """Gradients (dq, dk, dv) of sum <dout, o> for o = prefill(q, k, v) (bf16).
+
+    q, k as the forward attended with them (already rotated); o and lse from
+    prefill_lse; dout like o."""
+    torch = _torch()
+    B, Hq, Hkv, S, D = _check_prefill_shapes(q, k, v)
+    if o.shape != q.shape or dout.shape != q.shape or o.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("o and dout must match q")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, S):
+        raise ValueError("lse must be float32 [B, Hq, S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("dq, dk, dv must match q, k, v")
+    if workspace is None:
+        workspace = torch.empty(max(1, prefill_backward_workspace_size(B, Hq, S)),
+                                dtype=torch.uint8, device=q.device)
+    _check_dev(q, k, v, o, dout, lse, dq, dk, dv, workspace)
+    _call(lib().attn_prefill_backward, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), q.data_ptr(),
+          k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+          _dtype_code(q), B, Hq, Hkv, S, D, float(scale), workspace.data_ptr(),
+          workspace.numel() * workspace.element_size(), _stream(q))
+    return dq, dk, dv
 
 
 def decode_workspace_size(B: int, Hq: int, Hkv: int, max_len: int, D: int) -> int:

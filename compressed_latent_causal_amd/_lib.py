@@ -25,6 +25,9 @@ P, I, D, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_float,
 SIGNATURES = {
     "attn_rope": (I, [P, P, I, I, I, I, I, P, I, D, P]),
     "attn_prefill": (I, [P, P, P, P, I, I, I, I, I, I, F, D, P]),
+    "attn_prefill_lse": (I, [P, P, P, P, P, I, I, I, I, I, I, F, D, P]),
+    "attn_prefill_backward_workspace_size": (SZ, [I, I, I]),
+    "attn_prefill_backward": (I, [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P]),
     "attn_decode_workspace_size": (SZ, [I, I, I, I, I]),
     "attn_decode": (I, [P, P, P, P, I, I, I, I, I, I, P, I, F, D, P, SZ, P]),
     "attn_decode_paged": (I, [P, P, P, P, I, I, I, I, I, I, I, P, I, P, I, I, F, D, P, SZ, P]),

@@ -47,8 +47,51 @@ ATTN_API int attn_prefill(void* o, const void* q, const void* k, const void* v, 
     if ((long long)S * D * (dtype == ATTN_BF16 ? 2 : 4) >= (1ll << 31)) return ATTN_ERR_SHAPE;
     if (!o || !q || !k || !v) return ATTN_ERR_NULL;
     if (!aligned16(o) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return ATTN_ERR_ALIGN;
-    return hip_status(attn::launch_prefill(o, q, k, v, dtype, B, Hq, Hkv, S, D, scale, rope_theta,
-                                           (hipStream_t)stream));
+    return hip_status(attn::launch_prefill(o, nullptr, q, k, v, dtype, B, Hq, Hkv, S, D, scale,
+                                           rope_theta, (hipStream_t)stream));
+}
+
+ATTN_API int attn_prefill_lse(void* o, float* lse, const void* q, const void* k, const void* v,
+                              int dtype, int B, int Hq, int Hkv, int S, int D, float scale,
+                              double rope_theta, void* stream) {
+    if (B < 0 || S < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_BF16 || !supported_dim(D) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
+    if (!(rope_theta >= 0.0) || !isfinite(rope_theta)) return ATTN_ERR_UNSUPPORTED;
+    if (B == 0 || S == 0) return ATTN_OK;
+    if ((long long)B * Hq * ((S + 31) / 32) >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    if ((long long)S * D * 2 >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    if (!o || !lse || !q || !k || !v) return ATTN_ERR_NULL;
+    if (!aligned16(o) || !aligned16(q) || !aligned16(k) || !aligned16(v) || ((uintptr_t)lse & 3u))
+        return ATTN_ERR_ALIGN;
+    return hip_status(attn::launch_prefill(o, lse, q, k, v, dtype, B, Hq, Hkv, S, D, scale,
+                                           rope_theta, (hipStream_t)stream));
+}
+
+ATTN_API size_t attn_prefill_backward_workspace_size(int B, int Hq, int S) {
+    if (B < 1 || Hq < 1 || S < 1) return 0;
+    return attn::prefill_backward_workspace_bytes(B, Hq, S);
+}
+
+ATTN_API int attn_prefill_backward(void* dq, void* dk, void* dv, const void* q, const void* k,
+                                   const void* v, const void* o, const void* dout, const float* lse,
+                                   int dtype, int B, int Hq, int Hkv, int S, int D, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || S < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_BF16 || !supported_dim(D) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
+    if (B == 0 || S == 0) return ATTN_OK;
+    // grids of (key or query blocks) x B x Hq stay 32-bit; a head's rows and
+    // its padded statistics are addressed with 32-bit byte offsets
+    if ((long long)B * Hq * ((S + 31) / 32) >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    if ((long long)S * D * 2 >= (1ll << 31) || (long long)S + 128 >= (1ll << 28)) return ATTN_ERR_SHAPE;
+    if (!dq || !dk || !dv || !q || !k || !v || !o || !dout || !lse) return ATTN_ERR_NULL;
+    if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(q) || !aligned16(k) ||
+        !aligned16(v) || !aligned16(o) || !aligned16(dout) || ((uintptr_t)lse & 3u))
+        return ATTN_ERR_ALIGN;
+    if (!workspace || workspace_bytes < attn::prefill_backward_workspace_bytes(B, Hq, S))
+        return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+    return hip_status(attn::launch_prefill_backward(dq, dk, dv, q, k, v, o, dout, lse, B, Hq, Hkv,
+                                                    S, D, scale, workspace, (hipStream_t)stream));
 }
 
 ATTN_API size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D) {
@@ -112,9 +155,9 @@ ATTN_API const char* attn_status_string(int status) {
         case ATTN_ERR_NULL: return "a required pointer is NULL";
         case ATTN_ERR_SHAPE: return "invalid sizes (negative, Hq % Hkv != 0, max_len > S_cap, or too large)";
         case ATTN_ERR_UNSUPPORTED:
-            return "unsupported argument (head dim not 64/128, dtype, theta or scale out of range, f32 decode)";
+            return "unsupported argument (head dim not 64/128, dtype, theta or scale out of range, f32 decode or backward)";
         case ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-        case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
         case ATTN_ERR_HIP: return "kernel launch failed";
         default: return "unknown status";
     }

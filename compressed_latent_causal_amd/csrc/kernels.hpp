@@ -20,10 +20,20 @@ hipError_t launch_rope(void* out, const void* in, int dtype, int B, int H, int S
                        const int32_t* pos_offset, int pos_shift, double theta, hipStream_t st);
 
 // rope_theta > 0 rotates each query at its token index on the fly (k must
-// already be rotated); rope_theta == 0 takes q as given.
-hipError_t launch_prefill(void* o, const void* q, const void* k, const void* v, int dtype, int B,
-                          int Hq, int Hkv, int S, int D, float scale, double rope_theta,
-                          hipStream_t st);
+// already be rotated); rope_theta == 0 takes q as given.  lse (bf16 only, may
+// be NULL): fp32 [B, Hq, S] log-normaliser of each row's scaled scores.
+hipError_t launch_prefill(void* o, float* lse, const void* q, const void* k, const void* v,
+                          int dtype, int B, int Hq, int Hkv, int S, int D, float scale,
+                          double rope_theta, hipStream_t st);
+
+// Backward pass of causal grouped-query prefill (bf16): gradients dq, dk, dv
+// of sum <dout, o>, from q, k, v, the forward output o, dout and the forward's
+// lse.  workspace: prefill_backward_workspace_bytes(B, Hq, S) bytes.
+size_t prefill_backward_workspace_bytes(int B, int Hq, int S);
+hipError_t launch_prefill_backward(void* dq, void* dk, void* dv, const void* q, const void* k,
+                                   const void* v, const void* o, const void* dout,
+                                   const float* lse, int B, int Hq, int Hkv, int S, int D,
+                                   float scale, void* workspace, hipStream_t st);
 
 // Split workgroups (partial results) per (sequence, KV head) and workspace
 // bytes for these sizes.

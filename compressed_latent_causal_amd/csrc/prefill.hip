@@ -76,8 +76,8 @@ constexpr float PF_SUM_LIMIT = 65536.f;
 template <int D, int HPW>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, int B, int Hq, int Hkv, int S, float c, int n_qblk, int n_hchunk,
-    int rope, RopeFreqs fr) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c,
+    int n_qblk, int n_hchunk, int rope, RopeFreqs fr) {
     constexpr int KSTEPS = D / 32;              // k-steps of S^T = K Q^T
     constexpr int DT = D / 16;                  // d tiles of O^T
     constexpr int QPB = (PF_NW / HPW) * PF_QW;  // queries per head per workgroup
@@ -352,12 +352,15 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         step(t + 1, k1, v1, k0, v0);
     }
 
-    // ---- epilogue: O = O^T / l, lane holds query qw0 + 16n + lr, dims 16dt + 4lg .. +3
+    // ---- epilogue: O = O^T / l, lane holds query qw0 + 16n + lr, dims 16dt + 4lg .. +3.
+    // The row's probabilities are exp2(c s - m_run) / l, so its log-normaliser
+    // (natural log, of the scaled scores) is ln 2 * (m_run + log2 l).
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const float lt = lacc[n];
         const int qi = qw0 + 16 * n + lr;
         if (qi >= S) continue;
+        if (lse && lg == 0) lse[(size_t)(b * Hq + h) * S + qi] = (m_run[n] + log2f(lt)) * 0.69314718055994531f;
         const float inv = 1.f / lt;
         uint16_t* const orow = o + qo_base + (size_t)qi * D + 4 * lg;
 #pragma unroll
@@ -460,29 +463,29 @@ int largest_pow2_divisor(int g, int cap) {
 }
 
 template <int D, int HPW>
-hipError_t launch_bf16(void* o, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
-                       int S, float c, double rope_theta, hipStream_t st) {
+hipError_t launch_bf16(void* o, float* lse, const void* q, const void* k, const void* v, int B,
+                       int Hq, int Hkv, int S, float c, double rope_theta, hipStream_t st) {
     constexpr int QPB = (PF_NW / HPW) * PF_QW;
     const int G = Hq / Hkv;
     const int n_qblk = ceil_div(S, QPB), n_hchunk = G / HPW;
     const long long nblk = (long long)n_qblk * B * Hkv * n_hchunk;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW>), dim3((unsigned)nblk), dim3(PF_THREADS), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, B,
-                       Hq, Hkv, S, c, n_qblk, n_hchunk, rope_theta > 0 ? 1 : 0,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                       B, Hq, Hkv, S, c, n_qblk, n_hchunk, rope_theta > 0 ? 1 : 0,
                        rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D));
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_bf16_d(void* o, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
-                         int S, float c, double th, hipStream_t st) {
+hipError_t launch_bf16_d(void* o, float* lse, const void* q, const void* k, const void* v, int B,
+                         int Hq, int Hkv, int S, float c, double th, hipStream_t st) {
     // heads per workgroup: the largest power of two dividing G, at most one per wave
     const int hpw = largest_pow2_divisor(Hq / Hkv, PF_NW);
     if constexpr (PF_NW >= 8)
-        if (hpw == 8) return launch_bf16<D, 8>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
-    if (hpw >= 4) return launch_bf16<D, 4>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
-    if (hpw == 2) return launch_bf16<D, 2>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
-    return launch_bf16<D, 1>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
+        if (hpw == 8) return launch_bf16<D, 8>(o, lse, q, k, v, B, Hq, Hkv, S, c, th, st);
+    if (hpw >= 4) return launch_bf16<D, 4>(o, lse, q, k, v, B, Hq, Hkv, S, c, th, st);
+    if (hpw == 2) return launch_bf16<D, 2>(o, lse, q, k, v, B, Hq, Hkv, S, c, th, st);
+    return launch_bf16<D, 1>(o, lse, q, k, v, B, Hq, Hkv, S, c, th, st);
 }
 
 template <int D>
@@ -501,12 +504,13 @@ hipError_t launch_f32(void* o, const void* q, const void* k, const void* v, int 
 
 }  // namespace
 
-hipError_t launch_prefill(void* o, const void* q, const void* k, const void* v, int dtype, int B,
-                          int Hq, int Hkv, int S, int D, float scale, double th, hipStream_t st) {
+hipError_t launch_prefill(void* o, float* lse, const void* q, const void* k, const void* v, int dtype,
+                          int B, int Hq, int Hkv, int S, int D, float scale, double th,
+                          hipStream_t st) {
     const float c = scale * kLog2e;
     if (dtype == kBF16)
-        return D == 64 ? launch_bf16_d<64>(o, q, k, v, B, Hq, Hkv, S, c, th, st)
-                       : launch_bf16_d<128>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
+        return D == 64 ? launch_bf16_d<64>(o, lse, q, k, v, B, Hq, Hkv, S, c, th, st)
+                       : launch_bf16_d<128>(o, lse, q, k, v, B, Hq, Hkv, S, c, th, st);
     return D == 64 ? launch_f32<64>(o, q, k, v, B, Hq, Hkv, S, c, th, st)
                    : launch_f32<128>(o, q, k, v, B, Hq, Hkv, S, c, th, st);
 }

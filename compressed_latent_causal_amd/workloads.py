@@ -82,6 +82,17 @@ def make_prefill(w: Workload, seed: int = 0):
     return q, k, v
 
 
+def make_backward(w: Workload, seed: int = 0):
+    """q, k, v as make_prefill (same draws), then the output gradient dout
+    [B,Hq,S,D] drawn next from the same generator, N(0,1)."""
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (w.B, w.Hq, w.S, w.D), w.torch_dtype)
+    k = _randn(g, (w.B, w.Hkv, w.S, w.D), w.torch_dtype)
+    v = _randn(g, (w.B, w.Hkv, w.S, w.D), w.torch_dtype)
+    dout = _randn(g, (w.B, w.Hq, w.S, w.D), w.torch_dtype)
+    return q, k, v, dout
+
+
 def make_decode(w: Workload, seed: int = 0, poison_tail: bool = False):
     """q [B,Hq,D], k/v caches [B,Hkv,S_cap,D], seqlens int32 [B] (CPU).
 

@@ -1,7 +1,7 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) causal grouped-query attention
- * library: rotary position embedding, causal prefill and single-token decode
- * over a contiguous or a paged KV cache.
+ * library: rotary position embedding, causal prefill (forward and backward)
+ * and single-token decode over a contiguous or a paged KV cache.
  *
  * What is computed (pages cited by title and section):
  *  - "Grouped Query Attention (GQA)" glossary, section "Cómo funciona GQA":
@@ -53,9 +53,9 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
     ATTN_ERR_SHAPE = 2,        /* negative size, Hq/Hkv < 1, Hq % Hkv != 0, max_len > S_cap, ... */
-    ATTN_ERR_UNSUPPORTED = 3,  /* D not 64/128, unknown dtype, theta/scale out of range, f32 decode */
+    ATTN_ERR_UNSUPPORTED = 3,  /* D not 64/128, unknown dtype, theta/scale out of range, f32 decode/training */
     ATTN_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned */
-    ATTN_ERR_WORKSPACE = 5,    /* decode workspace missing or too small */
+    ATTN_ERR_WORKSPACE = 5,    /* workspace missing or too small */
     ATTN_ERR_HIP = 6           /* a kernel launch failed */
 } attn_status;
 
@@ -102,6 +102,49 @@ int attn_rope(void *out, const void *in, int dtype, int B, int H, int S, int D,
 int attn_prefill(void *o, const void *q, const void *k, const void *v, int dtype,
                  int B, int Hq, int Hkv, int S, int D, float scale, double rope_theta,
                  void *stream);
+
+/*
+ * attn_prefill that also writes each row's log-normaliser, for training:
+ *   lse[b,h,i] = log sum_{t<=i} exp(scale * <q[b,h,i,:], k[b,h/G,t,:]>)
+ * (natural log; device fp32 [B, Hq, S], 4-byte aligned).  o and every other
+ * argument as attn_prefill, bf16 only.  The forward's probabilities are the
+ * exponentials of its scores minus lse, so lse is what attn_prefill_backward
+ * needs to recompute them.
+ */
+int attn_prefill_lse(void *o, float *lse, const void *q, const void *k, const void *v,
+                     int dtype, int B, int Hq, int Hkv, int S, int D, float scale,
+                     double rope_theta, void *stream);
+
+/*
+ * Bytes of device workspace attn_prefill_backward needs (0 on invalid sizes):
+ * two fp32 row statistics per query row, each head padded to whole 64-row
+ * tiles plus one.
+ */
+size_t attn_prefill_backward_workspace_size(int B, int Hq, int S);
+
+/*
+ * Backward pass of causal grouped-query prefill ("Compressed Convolutional
+ * Attention" summary, "Resultaten", which reports this pass for the same
+ * attention): the gradients of sum <dout, o> for o = attn_prefill(q, k, v),
+ *   p_it = exp(scale <q_i, k_t> - lse_i),  ds_it = p_it (<dout_i, v_t> - <dout_i, o_i>)
+ *   dq_i = scale sum_{t<=i} ds_it k_t
+ *   dk_t = scale sum_{h in group} sum_{i>=t} ds_it q_i
+ *   dv_t = sum_{h in group} sum_{i>=t} p_it dout_i
+ * q, o, dout, dq: [B, Hq, S, D];  k, v, dk, dv: [B, Hkv, S, D];  lse: fp32
+ * [B, Hq, S] from attn_prefill_lse on the same q, k, v, with o its output.
+ * q and k are the tensors attention saw (already rotated); the gradients are
+ * with respect to them.  bf16 only: bf16 matrix-core products with fp32
+ * accumulation, p and ds rounded to bf16 before their products, each
+ * gradient rounded once to bf16.  Outputs must not overlap inputs.
+ * workspace: at least attn_prefill_backward_workspace_size(B, Hq, S) bytes,
+ * 16-byte aligned, contents on entry irrelevant, not shared by calls that may
+ * overlap.  Three kernels are enqueued (row statistics, dk/dv, dq); dk and dv
+ * sum the group's query heads in registers, so every gradient is written once.
+ */
+int attn_prefill_backward(void *dq, void *dk, void *dv, const void *q, const void *k,
+                          const void *v, const void *o, const void *dout, const float *lse,
+                          int dtype, int B, int Hq, int Hkv, int S, int D, float scale,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Bytes of device workspace attn_decode needs for these sizes (0 on invalid

@@ -108,6 +108,56 @@ def test_prefill_validation(L):
     assert p(*args(o=None, q=None, k=None, v=None, S=0)) == OK
 
 
+def test_prefill_lse_validation(L):
+    p = lambda *a: L.attn_prefill_lse(*a)
+    args = lambda **kw: [kw.get("o", FAKE), kw.get("lse", FAKE), kw.get("q", FAKE),
+                         kw.get("k", FAKE), kw.get("v", FAKE), kw.get("dt", BF16), kw.get("B", 1),
+                         kw.get("Hq", 8), kw.get("Hkv", 2), kw.get("S", 16), kw.get("D", 64),
+                         kw.get("scale", 0.125), kw.get("theta", 0.0), None]
+    assert p(*args(Hkv=3)) == ESHAPE
+    assert p(*args(dt=F32)) == EUNSUP  # bf16 only
+    assert p(*args(D=96)) == EUNSUP
+    assert p(*args(scale=0.0)) == EUNSUP
+    assert p(*args(theta=-2.0)) == EUNSUP
+    for name in ("o", "lse", "q", "k", "v"):
+        assert p(*args(**{name: None})) == ENULL
+    for name in "oqkv":
+        assert p(*args(**{name: FAKE + 4})) == EALIGN
+    assert p(*args(lse=FAKE + 2)) == EALIGN  # lse needs 4-byte alignment only
+    assert p(*args(B=1, Hq=1, Hkv=1, S=1 << 23, D=128)) == ESHAPE
+    assert p(*args(o=None, lse=None, q=None, k=None, v=None, B=0)) == OK
+
+
+def test_prefill_backward_workspace_and_validation(L):
+    ws = L.attn_prefill_backward_workspace_size
+    # two fp32 per row, each head padded to whole 64-row tiles plus one
+    assert ws(2, 8, 100) == 2 * 8 * (128 + 64) * 8
+    assert ws(1, 1, 64) == (64 + 64) * 8
+    assert ws(0, 8, 100) == 0 and ws(1, 0, 5) == 0 and ws(1, 1, 0) == 0
+    need = ws(1, 8, 16)
+    p = lambda *a: L.attn_prefill_backward(*a)
+    names = ["dq", "dk", "dv", "q", "k", "v", "o", "dout"]
+    args = lambda **kw: [kw.get(n, FAKE) for n in names] + [
+        kw.get("lse", FAKE), kw.get("dt", BF16), kw.get("B", 1), kw.get("Hq", 8), kw.get("Hkv", 2),
+        kw.get("S", 16), kw.get("D", 64), kw.get("scale", 0.125), kw.get("ws", FAKE),
+        kw.get("wsb", need), None]
+    assert p(*args(Hkv=3)) == ESHAPE
+    assert p(*args(Hq=0)) == ESHAPE
+    assert p(*args(S=-1)) == ESHAPE
+    assert p(*args(dt=F32)) == EUNSUP
+    assert p(*args(D=32)) == EUNSUP
+    assert p(*args(scale=float("nan"))) == EUNSUP
+    for name in names + ["lse"]:
+        assert p(*args(**{name: None})) == ENULL
+    for name in names:
+        assert p(*args(**{name: FAKE + 8})) == EALIGN
+    assert p(*args(ws=None)) == EWS
+    assert p(*args(wsb=need - 1)) == EWS
+    assert p(*args(ws=FAKE + 4)) == EALIGN
+    assert p(*args(B=1, Hq=1, Hkv=1, S=1 << 23, D=128)) == ESHAPE
+    assert p(*args(**{n: None for n in names}, lse=None, ws=None, B=0)) == OK
+
+
 # ---------------------------------------------------------------- decode
 def test_decode_workspace_size(L):
     ws = L.attn_decode_workspace_size
