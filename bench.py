@@ -1,6 +1,7 @@
 """Benchmark of the causal GQA attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+                    [--no-backward]
 
 Headline workload: the Llama-3.1-8B-shaped prefill layer (batch 4, 32 query
 heads, 8 KV heads, head dim 128, 4096 tokens, bf16, RoPE theta 5e5).  One step
@@ -10,7 +11,8 @@ step (4*B*Hq*D*S(S+1)/2 flops: QK^T and PV over unmasked pairs only), inputs
 resident in HBM.  The `roofline` object prices the prefill kernel alone, timed
 with HIP events on the stream it runs on.  The `decode` object reports KV-cache
 GB/s of the two decode workloads (one decode step over several layers' caches
-back to back, caches evicted before each timed step), and `cpu_baseline` times
+back to back, caches evicted before each timed step), the `backward` object the
+training backward pass of both prefill workloads, and `cpu_baseline` times
 the fp64 CPU oracle on a bounded sample of the same prefill workload.  Prints
 one JSON line on stdout.
 """
@@ -214,6 +216,50 @@ def bench_decode(w, iters, warmup, layers, page_size=0):
             "step": "one fused decode launch per layer (query RoPE at len-1, split-K, merge)"}
 
 
+def bench_backward(w, iters, warmup):
+    """The backward pass of one prefill layer (attn_prefill_backward: row
+    statistics, dK/dV and dQ kernels) on the forward's o and lse, inputs
+    resident, each call timed with HIP events on its stream.  TFLOP/s counts
+    the five products of the backward over unmasked pairs (2.5x the forward's
+    count); the kernels execute seven (S and dP are formed in both the dK/dV
+    and the dQ kernel)."""
+    import torch
+    import compressed_latent_causal_amd as attn
+    from compressed_latent_causal_amd import workloads as wl
+
+    q, k, v, dout = (t.cuda() for t in wl.make_backward(w, seed=0))
+    o, lse = attn.prefill_lse(q, k, v, scale=w.scale)
+    ws = torch.empty(attn.prefill_backward_workspace_size(w.B, w.Hq, w.S), dtype=torch.uint8,
+                     device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        attn.prefill_backward(q, k, v, o, dout, lse, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                              workspace=ws)
+
+    settle(step, 0.5)
+    for _ in range(warmup):
+        step()
+    ms = []
+    for _ in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    ms.sort()
+    med = ms[len(ms) // 2]
+    flops = 2.5 * prefill_flops(w.B, w.Hq, w.S, w.D)
+    tf = flops / (med * 1e-3) / 1e12
+    return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+            "head_dim": w.D, "seq_len": w.S, "ms_median": round(med, 5), "ms_min": round(ms[0], 5),
+            "TFLOP_per_s": round(tf, 1), "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flop_counted": flops, "iters": iters,
+            "step": "attn_prefill_backward: dq, dk, dv from q, k, v, o, dout, lse (bf16)"}
+
+
 DECODE_LAYERS = {"gqa_decode": 4, "long_decode": 8}  # 4 GiB of caches either way
 # (reported name, workload, page size): the paged line reads the gqa workload's
 # cache through 256-token pages
@@ -267,9 +313,11 @@ def main():
     ap.add_argument("--decode-iters", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "gqa_decode", "long_decode", "gqa_decode_paged256",
-                                       "ccgqa_prefill", "copy"],
+                                       "ccgqa_prefill", "backward_llama8b_prefill",
+                                       "backward_ccgqa_prefill", "copy"],
                     help="time one workload alone and print its line (profiling runs; `copy` is "
                          "the plain copy that calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -288,6 +336,10 @@ def main():
 
     if args.only == "copy":
         print(json.dumps(bench_copy()), flush=True)
+        return
+    if args.only and args.only.startswith("backward_"):
+        b = bench_backward(wl.WORKLOADS[args.only[len("backward_"):]], args.steps, args.warmup)
+        print(json.dumps(b), flush=True)
         return
     lines = {name: (wname, page) for name, wname, page in DECODE_LINES}
     if args.only in lines:
@@ -335,6 +387,13 @@ def main():
             log(f"decode {name}: {d['ms_per_layer_median']:.4f} ms per layer, {d['GB_per_s']:.0f} GB/s")
             dec[name] = d
         result["decode"] = dec
+    if not args.no_backward:
+        bwd = {}
+        for name in ("llama8b_prefill", "ccgqa_prefill"):
+            b = bench_backward(wl.WORKLOADS[name], args.steps, 3)
+            log(f"backward {name}: {b['ms_median']:.4f} ms, {b['TFLOP_per_s']:.0f} TFLOP/s")
+            bwd[name] = b
+        result["backward"] = bwd
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
         log(f"cpu baseline: {result['cpu_baseline']}")

@@ -38,6 +38,10 @@ namespace {
 
 constexpr int BW_BQ = 64;  // queries per Q/dO tile (dK/dV kernel)
 constexpr int BW_BN = 64;  // keys per K/V tile (dQ kernel)
+// LDS operand fragments read ahead of the products that use them
+#ifndef BW_PD
+#define BW_PD 4
+#endif
 
 // Rows of row statistics per head: whole Q tiles plus one (the stats of a tile
 // are fetched 128 rows at a time).
@@ -196,21 +200,27 @@ __global__ __launch_bounds__(NW * 64, (NK == 1 && NW == 4) ? 2 : 1) void bwd_dkd
                     sacc[i][nk] = f32x4_t{0, 0, 0, 0};
                     pacc[i][nk] = dl[i];
                 }
+            // operand f = (k-step f / 4, sub-tile (f / 2) % 2, Q or dO by f % 2),
+            // read BW_PD operands ahead of the products that use it
+            constexpr int NAF = 4 * KSTEPS;
+            auto afrag = [&](int f) __attribute__((always_inline)) {
+                const char* base = (f % 2) ? gs : qs;
+                return *(const bf16x8_t*)(base + aoff[f / 4] + (32 * hh + 16 * ((f / 2) % 2)) * ROW);
+            };
+            bf16x8_t af[NAF];
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                bf16x8_t qa[2], ga[2];
+            for (int f = 0; f < BW_PD; ++f) af[f] = afrag(f);
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    qa[i] = *(const bf16x8_t*)(qs + aoff[s] + (32 * hh + 16 * i) * ROW);
-                    ga[i] = *(const bf16x8_t*)(gs + aoff[s] + (32 * hh + 16 * i) * ROW);
+            for (int f = 0; f < NAF; ++f) {
+                if (f + BW_PD < NAF) af[f + BW_PD] = afrag(f + BW_PD);
+                __builtin_amdgcn_sched_barrier(0);
+                const int s = f / 4, i = (f / 2) % 2;
+#pragma unroll
+                for (int nk = 0; nk < NK; ++nk) {
+                    if (f % 2) pacc[i][nk] = mfma16(af[f], vf[nk][s], pacc[i][nk]);
+                    else sacc[i][nk] = mfma16(af[f], kf[nk][s], sacc[i][nk]);
                 }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int nk = 0; nk < NK; ++nk) {
-                        sacc[i][nk] = mfma16(qa[i], kf[nk][s], sacc[i][nk]);
-                        pacc[i][nk] = mfma16(ga[i], vf[nk][s], pacc[i][nk]);
-                    }
+                __builtin_amdgcn_sched_barrier(0);
             }
             // P = exp2(c s - lse2), dS = P (dP - delta); zero where the query
             // precedes the key or lies past the sequence
@@ -245,15 +255,25 @@ __global__ __launch_bounds__(NW * 64, (NK == 1 && NW == 4) ? 2 : 1) void bwd_dkd
             }
             // dV^T += dO^T P and dK^T += Q^T dS: the A operands are the half's 32
             // rows read transposed, in the row order the P and dS packing uses
+            // operand f = (d tile f / 2, dO^T or Q^T by f % 2), read BW_PD ahead
+            constexpr int NTF = 2 * DT;
+            auto tfrag = [&](int f) __attribute__((always_inline)) {
+                return v_frag_at<D>(((f % 2) ? qs : gs) + toff[f / 2] + 32 * hh * ROW);
+            };
+            bf16x8_t tf[NTF];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const bf16x8_t gt = v_frag_at<D>(gs + toff[dt] + 32 * hh * ROW);
-                const bf16x8_t qt = v_frag_at<D>(qs + toff[dt] + 32 * hh * ROW);
+            for (int f = 0; f < BW_PD; ++f) tf[f] = tfrag(f);
+#pragma unroll
+            for (int f = 0; f < NTF; ++f) {
+                if (f + BW_PD < NTF) tf[f + BW_PD] = tfrag(f + BW_PD);
+                __builtin_amdgcn_sched_barrier(0);
+                const int dt = f / 2;
 #pragma unroll
                 for (int nk = 0; nk < NK; ++nk) {
-                    dva[dt][nk] = mfma16(gt, pb[nk], dva[dt][nk]);
-                    dka[dt][nk] = mfma16(qt, sb[nk], dka[dt][nk]);
+                    if (f % 2) dka[dt][nk] = mfma16(tf[f], sb[nk], dka[dt][nk]);
+                    else dva[dt][nk] = mfma16(tf[f], pb[nk], dva[dt][nk]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
@@ -401,19 +421,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                     sacc[hf][n] = f32x4_t{0, 0, 0, 0};
                     pacc[hf][n] = f32x4_t{nd[n], nd[n], nd[n], nd[n]};
                 }
+            // operand f = (k-step f / 4, key tile 2kk + (f / 2) % 2, K or V by f % 2),
+            // read BW_PD operands ahead of its two products
+            constexpr int NAF = 4 * KSTEPS;
+            auto afrag = [&](int f) __attribute__((always_inline)) {
+                const int mt = 2 * kk + (f / 2) % 2;
+                return (f % 2) ? *(const bf16x8_t*)(vs + voff[f / 4] + 16 * mt * ROW)
+                               : *(const bf16x8_t*)(ks + koff[f / 4] + 16 * mt * ROW);
+            };
+            bf16x8_t af[NAF];
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s)
+            for (int f = 0; f < BW_PD; ++f) af[f] = afrag(f);
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int mt = 2 * kk + hf;
-                    const bf16x8_t ka = *(const bf16x8_t*)(ks + koff[s] + 16 * mt * ROW);
-                    const bf16x8_t va = *(const bf16x8_t*)(vs + voff[s] + 16 * mt * ROW);
+            for (int f = 0; f < NAF; ++f) {
+                if (f + BW_PD < NAF) af[f + BW_PD] = afrag(f + BW_PD);
+                __builtin_amdgcn_sched_barrier(0);
+                const int s = f / 4, hf = (f / 2) % 2;
 #pragma unroll
-                    for (int n = 0; n < 2; ++n) {
-                        sacc[hf][n] = mfma16(ka, qf[n][s], sacc[hf][n]);
-                        pacc[hf][n] = mfma16(va, gf[n][s], pacc[hf][n]);
-                    }
+                for (int n = 0; n < 2; ++n) {
+                    if (f % 2) pacc[hf][n] = mfma16(af[f], gf[n][s], pacc[hf][n]);
+                    else sacc[hf][n] = mfma16(af[f], qf[n][s], sacc[hf][n]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+            }
             // dS^T = P^T (dP^T - delta), zero above the diagonal, packed as the
             // B operand (keys 4lg + r of both 16-key tiles)
             bf16x8_t sb[2];
@@ -435,12 +465,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 }
                 sb[n] = __builtin_bit_cast(bf16x8_t, dw);
             }
-            // dQ^T += K^T dS^T
+            // dQ^T += K^T dS^T, the K^T operand of d tile dt read BW_PD / 2 ahead
+            constexpr int TPD = BW_PD / 2 > 0 ? BW_PD / 2 : 1;
+            auto tfrag = [&](int dt) __attribute__((always_inline)) {
+                return v_frag_at<D>(ks + toff[dt] + 32 * kk * ROW);
+            };
+            bf16x8_t tf[DT];
+#pragma unroll
+            for (int dt = 0; dt < TPD; ++dt) tf[dt] = tfrag(dt);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const bf16x8_t kt = v_frag_at<D>(ks + toff[dt] + 32 * kk * ROW);
-                qa[dt][0] = mfma16(kt, sb[0], qa[dt][0]);
-                qa[dt][1] = mfma16(kt, sb[1], qa[dt][1]);
+                if (dt + TPD < DT) tf[dt + TPD] = tfrag(dt + TPD);
+                __builtin_amdgcn_sched_barrier(0);
+                qa[dt][0] = mfma16(tf[dt], sb[0], qa[dt][0]);
+                qa[dt][1] = mfma16(tf[dt], sb[1], qa[dt][1]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
