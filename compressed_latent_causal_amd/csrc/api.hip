@@ -109,6 +109,8 @@ ATTN_API int attn_decode(void* o, const void* q, const void* k_cache, const void
     if (dtype != ATTN_BF16 || !supported_dim(D) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
     if (!(rope_theta >= 0.0) || !isfinite(rope_theta)) return ATTN_ERR_UNSUPPORTED;
     if (B > kMaxGridYZ || (long long)Hkv * ((Hq / Hkv + 15) / 16) > kMaxGridYZ) return ATTN_ERR_SHAPE;
+    // a group's partial results are addressed with 32-bit byte offsets
+    if ((long long)max_len * D * 2 >= (1ll << 31)) return ATTN_ERR_SHAPE;
     if (B == 0) return ATTN_OK;
     if (!o || !q || !k_cache || !v_cache || !seqlens) return ATTN_ERR_NULL;
     if (!aligned16(o) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
@@ -135,6 +137,7 @@ ATTN_API int attn_decode_paged(void* o, const void* q, const void* k_pages, cons
     if (dtype != ATTN_BF16 || !supported_dim(D) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
     if (!(rope_theta >= 0.0) || !isfinite(rope_theta)) return ATTN_ERR_UNSUPPORTED;
     if ((long long)B * max_pages > INT32_MAX) return ATTN_ERR_SHAPE;
+    if ((long long)max_len * D * 2 >= (1ll << 31)) return ATTN_ERR_SHAPE;
     if (B == 0) return ATTN_OK;
     if (!o || !q || !k_pages || !v_pages || !block_table || !seqlens) return ATTN_ERR_NULL;
     if (!aligned16(o) || !aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) ||

@@ -99,6 +99,24 @@ __device__ inline int wave_sum(int x) {
     const auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
     return (int)(b[0] + b[1]);
 }
+// Max and sum over each 16-lane row (every lane of the row gets the result);
+// all lanes of the wave must be active.
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x124>(x));
+    return fmaxf(x, dpp_f<0x128>(x));
+}
+__device__ inline float row16_sum(float x) {
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x124>(x);
+    return x + dpp_f<0x128>(x);
+}
 __device__ inline int wave_inclusive_scan(int x) {
     x = dpp_add<0x111>(x);  // row shift right by 1, 2, 4, 8: prefix sums within rows
     x = dpp_add<0x112>(x);
@@ -116,13 +134,14 @@ __device__ inline void store_agent(float* p, float x) {
 __device__ inline float load_agent(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline f32x4_t load4_agent(const float* p) {
-    // two 8-byte device-coherent loads (p is 16-byte aligned)
-    unsigned long long* const q = (unsigned long long*)const_cast<float*>(p);
-    const unsigned long long v0 = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long v1 = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return f32x4_t{__uint_as_float((unsigned)v0), __uint_as_float((unsigned)(v0 >> 32)),
-                   __uint_as_float((unsigned)v1), __uint_as_float((unsigned)(v1 >> 32))};
+// 16-byte device-coherent load and store (sc1: the per-XCD L2's non-coherent
+// lines are bypassed) through a buffer resource, one instruction where 8- or
+// 4-byte atomic accesses would take two or four
+__device__ inline f32x4_t load4_coherent(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 16));
+}
+__device__ inline void store4_coherent(f32x4_t x, __amdgpu_buffer_rsrc_t rs, int byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rs, byte_off, 0, 16);
 }
 
 template <int D>
@@ -489,24 +508,30 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
         }
         return;
     }
-    for (int e = tid; e < GH * D; e += DC_NW * 64) {
-        const int hd = e / D, d = e % D;
-        float M = -INFINITY;
+    {
+        // this workgroup's partial o vectors, 16 bytes (4 dims of a head) per store
+        const __amdgpu_buffer_rsrc_t ors =
+            buffer_rsrc(ws_o + (size_t)(b * Hq + h0) * NC * D, GH * NC * D * 4);
+        for (int e = tid; e < GH * (D / 4); e += DC_NW * 64) {
+            const int hd = e / (D / 4), d = 4 * (e % (D / 4));
+            float M = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < DC_NW; ++ww) M = fmaxf(M, cm[ww * DC_HEADS + hd]);
-        float L = 0.f, O = 0.f;
+            for (int ww = 0; ww < DC_NW; ++ww) M = fmaxf(M, cm[ww * DC_HEADS + hd]);
+            float L = 0.f;
+            f32x4_t O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ww = 0; ww < DC_NW; ++ww) {
-            const float mw = cm[ww * DC_HEADS + hd];
-            const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * c);
-            L += f * cl[ww * DC_HEADS + hd];
-            O += f * co[(ww * DC_HEADS + hd) * OS + d];
-        }
-        const size_t slot = (size_t)(b * Hq + h0 + hd) * NC + chunk;
-        store_agent(ws_o + slot * D + d, O);
-        if (d == 0) {
-            store_agent(ws_ml + slot * 2, M);
-            store_agent(ws_ml + slot * 2 + 1, L);
+            for (int ww = 0; ww < DC_NW; ++ww) {
+                const float mw = cm[ww * DC_HEADS + hd];
+                const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * c);
+                L += f * cl[ww * DC_HEADS + hd];
+                O += f * *(const f32x4_t*)(co + (ww * DC_HEADS + hd) * OS + d);
+            }
+            store4_coherent(O, ors, ((hd * NC + chunk) * D + d) * 4);
+            if (d == 0) {
+                const size_t slot = (size_t)(b * Hq + h0 + hd) * NC + chunk;
+                store_agent(ws_ml + slot * 2, M);
+                store_agent(ws_ml + slot * 2 + 1, L);
+            }
         }
     }
 
@@ -538,15 +563,21 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
         mine &= __hip_atomic_load(tags + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
     if (!__syncthreads_and(mine)) return;
 
-    // ---- merge (log-sum-exp over the nwg partials).  Partials are taken in
-    // blocks of MB: the block's (max, sum) pairs are staged in LDS with one
-    // parallel load, each head's running max / factor / sum are updated there,
-    // and every thread folds the o vectors of its items (a head and 4
-    // consecutive dims each) with 16-byte loads, MU of them in flight.
-    constexpr int MB = DecodeSmem<D>::kMB, MU = 8, EPI = 4;
+    // ---- merge (log-sum-exp over the nwg partials).  Each thread folds one or
+    // two items (a head and 4 consecutive dims each).  Partials are taken in
+    // blocks: every thread first issues the loads of its items' o vectors for
+    // the whole block (NSLOT 16-byte loads: 24 partials of one item, or 12 of
+    // two), then the block's (max, sum) pairs, so a block costs one memory
+    // round trip.  The pairs go to LDS, where one 16-lane row per head forms
+    // its running max, factors and sum with row reductions, and the threads
+    // fold their o vectors with those factors.
+    constexpr int NSLOT = 24, EPI = 4, MBX = NSLOT;
     constexpr int NITEM = DC_HEADS * D / EPI / (DC_NW * 64);  // items per thread, at most
-    float* const bm = (float*)vs0;         // [DC_HEADS][MB] max, then factor
-    float* const bl = bm + DC_HEADS * MB;  // [DC_HEADS][MB] sum
+    static_assert(NITEM >= 1 && NITEM <= 2 && NSLOT % NITEM == 0, "merge slots");
+    const int ipt = GH * (D / EPI) > DC_NW * 64 ? 2 : 1;  // items this workgroup's threads fold
+    const int MB = NSLOT / ipt;                           // partials per block
+    float* const bm = (float*)vs0;          // [DC_HEADS][MBX] max, then factor
+    float* const bl = bm + DC_HEADS * MBX;  // [DC_HEADS][MBX] sum
     float* const run = sstat;  // [DC_HEADS] running max, [DC_HEADS] alpha, [DC_HEADS] L
     if (tid < DC_HEADS) {
         run[tid] = -INFINITY;
@@ -557,62 +588,87 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     for (int it = 0; it < NITEM; ++it)
 #pragma unroll
         for (int e = 0; e < EPI; ++e) acc[it][e] = 0.f;
+    constexpr int NML = ceil_div(DC_HEADS * MBX, DC_NW * 64);  // (max, sum) pairs per thread
+    // the group's partial o vectors [GH][NC][D]
+    const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(ws_o + (size_t)(b * Hq + h0) * NC * D, GH * NC * D * 4);
     for (int c0 = 0; c0 < nwg; c0 += MB) {
         const int nb = min(MB, nwg - c0);
-        __syncthreads();
-        for (int e = tid; e < GH * nb; e += DC_NW * 64) {
-            const int hd = e / nb, ch = e % nb;
-            const size_t sl = (size_t)(b * Hq + h0 + hd) * NC + c0 + ch;
-            bm[hd * MB + ch] = load_agent(ws_ml + sl * 2);
-            bl[hd * MB + ch] = load_agent(ws_ml + sl * 2 + 1);
+        // slot k: item k / MB, partial c0 + k % MB
+        f32x4_t oc[NSLOT];
+#pragma unroll
+        for (int k = 0; k < NSLOT; ++k) {
+            const int it = (NITEM > 1 && k >= MB) ? 1 : 0, u = k - it * MB;
+            const int item = tid + it * DC_NW * 64;
+            const bool ok = it < ipt && item < GH * (D / EPI) && u < nb;
+            const int hd = ok ? item / (D / EPI) : 0, d = EPI * (item % (D / EPI));
+            oc[k] = ok ? load4_coherent(ors, ((hd * NC + c0 + u) * D + d) * 4)
+                       : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        float pm[NML], pl[NML];
+#pragma unroll
+        for (int r = 0; r < NML; ++r) {
+            const int e = tid + r * DC_NW * 64;
+            pm[r] = pl[r] = 0.f;
+            if (e < GH * nb) {
+                const size_t sl = (size_t)(b * Hq + h0 + e / nb) * NC + c0 + e % nb;
+                pm[r] = load_agent(ws_ml + sl * 2);
+                pl[r] = load_agent(ws_ml + sl * 2 + 1);
+            }
+        }
+        __syncthreads();  // the previous block's factors have been used
+#pragma unroll
+        for (int r = 0; r < NML; ++r) {
+            const int e = tid + r * DC_NW * 64;
+            if (e < GH * nb) {
+                bm[(e / nb) * MBX + e % nb] = pm[r];
+                bl[(e / nb) * MBX + e % nb] = pl[r];
+            }
         }
         __syncthreads();
-        for (int hd = w; hd < GH; hd += DC_NW) {  // per head: running max, rescale, factors, sum
-            const float mprev = run[hd];
-            float mx = mprev;
-            for (int ch = lane; ch < nb; ch += 64) mx = fmaxf(mx, bm[hd * MB + ch]);
-#pragma unroll
-            for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, xor_shfl(mx, sh));
+        {  // one 16-lane row per head: running max, rescale, factors, sum
+            static_assert(DC_HEADS == 4 * DC_NW && MBX <= 32, "a row per head, two partials per lane");
+            const int j = lane & 15, hd = 4 * w + (lane >> 4);
+            const bool hv = hd < GH;
+            const int r = hv ? hd : 0;
+            const bool v0 = hv && j < nb, v1 = hv && j + 16 < nb && j + 16 < MBX;
+            const float m0 = v0 ? bm[r * MBX + j] : -INFINITY;
+            const float m1 = v1 ? bm[r * MBX + j + 16] : -INFINITY;
+            const float l0 = v0 ? bl[r * MBX + j] : 0.f;
+            const float l1 = v1 ? bl[r * MBX + j + 16] : 0.f;
+            const float mprev = run[r];
+            const float mx = row16_max(fmaxf(fmaxf(m0, m1), mprev));
             const float mref = (mx == -INFINITY) ? 0.f : mx;
             const float alpha = (mprev == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mprev - mref) * c);
-            float ls = 0.f;
-            for (int ch = lane; ch < nb; ch += 64) {
-                const float m = bm[hd * MB + ch];
-                const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mref) * c);
-                bm[hd * MB + ch] = f;
-                ls = fmaf(f, bl[hd * MB + ch], ls);
-            }
-#pragma unroll
-            for (int sh = 32; sh >= 1; sh >>= 1) ls += xor_shfl(ls, sh);
-            if (lane == 0) {
-                run[hd] = mx;
-                run[DC_HEADS + hd] = alpha;
-                run[2 * DC_HEADS + hd] = fmaf(run[2 * DC_HEADS + hd], alpha, ls);
+            const float f0 = (m0 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m0 - mref) * c);
+            const float f1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m1 - mref) * c);
+            const float ls = row16_sum(fmaf(f0, l0, f1 * l1));
+            if (v0) bm[r * MBX + j] = f0;
+            if (v1) bm[r * MBX + j + 16] = f1;
+            if (hv && j == 0) {
+                run[r] = mx;
+                run[DC_HEADS + r] = alpha;
+                run[2 * DC_HEADS + r] = fmaf(run[2 * DC_HEADS + r], alpha, ls);
             }
         }
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < NITEM; ++it) {
             const int item = tid + it * DC_NW * 64;
-            if (item >= GH * (D / EPI)) break;
-            const int hd = item / (D / EPI), d = EPI * (item % (D / EPI));
+            if (it >= ipt || item >= GH * (D / EPI)) break;
+            const int hd = item / (D / EPI);
             const float alpha = run[DC_HEADS + hd];
 #pragma unroll
             for (int e = 0; e < EPI; ++e) acc[it][e] *= alpha;
-            const size_t sb = (size_t)(b * Hq + h0 + hd) * NC + c0;
-            for (int ch0 = 0; ch0 < nb; ch0 += MU) {
-                f32x4_t oc[MU];
+        }
 #pragma unroll
-                for (int u = 0; u < MU; ++u)
-                    oc[u] = (ch0 + u < nb) ? load4_agent(ws_o + (sb + ch0 + u) * D + d)
-                                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < NSLOT; ++k) {  // branch-free, so the factor reads batch up
+            const int it = (NITEM > 1 && k >= MB) ? 1 : 0, u = k - it * MB;
+            const int item = tid + it * DC_NW * 64;
+            const bool ok = it < ipt && item < GH * (D / EPI) && u < nb;
+            const float fr = bm[min(item / (D / EPI), DC_HEADS - 1) * MBX + u];
+            const float f = ok ? fr : 0.f;
 #pragma unroll
-                for (int u = 0; u < MU; ++u) {
-                    const float f = (ch0 + u < nb) ? bm[hd * MB + ch0 + u] : 0.f;
-#pragma unroll
-                    for (int e = 0; e < EPI; ++e) acc[it][e] = fmaf(f, oc[u][e], acc[it][e]);
-                }
-            }
+            for (int e = 0; e < EPI; ++e) acc[it][e] = fmaf(f, oc[k][e], acc[it][e]);
         }
     }
 #pragma unroll

@@ -167,7 +167,9 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D);
  * Cache slots at or beyond seqlens[b] are never read into the result (they may
  * hold anything, NaN included).  A sequence with seqlens[b] == 0 gets a zero
  * row.  Out-of-contract lengths are clamped to [0, max_len] on the device.
- * max_len <= S_cap is a host-side upper bound of the lengths.
+ * max_len <= S_cap is a host-side upper bound of the lengths, and one head's
+ * max_len keys must span less than 2 GiB (max_len * D * 2 < 2^31), else
+ * ATTN_ERR_SHAPE.
  * rope_theta > 0: q is taken unrotated and each sequence's query is rotated
  * on the fly at position seqlens[b] - 1 (bit for bit what attn_rope with
  * pos_offset = seqlens, pos_shift = -1 produces); rope_theta == 0: q is used
@@ -202,7 +204,8 @@ int attn_decode(void *o, const void *q, const void *k_cache, const void *v_cache
  *   k_t, v_t the rows of head h / G.
  *
  * page_size: a positive multiple of 32.  0 <= seqlens[b] <= max_len <=
- * max_pages * page_size (lengths are clamped to [0, max_len] on the device).
+ * max_pages * page_size (lengths are clamped to [0, max_len] on the device),
+ * and max_len * D * 2 < 2^31 as for attn_decode.
  * Table entries of the pages a query sees must lie in [0, num_pages); the
  * kernel clamps any other entry it reads into that range, so no read leaves
  * the page pool (the result is then unspecified).  Pages and rows that no

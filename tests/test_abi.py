@@ -205,6 +205,8 @@ def test_decode_validation(L):
     assert d(*args(ws_bytes=need - 1)) == EWS
     assert d(*args(ws=FAKE + 4)) == EALIGN
     assert d(*args(B=70000)) == ESHAPE
+    # one head's max_len keys must span less than 2 GiB
+    assert d(*args(S_cap=1 << 23, max_len=1 << 23)) == ESHAPE
     assert d(*args(o=None, q=None, kc=None, vc=None, lens=None, ws=None, B=0)) == OK
 
 
@@ -227,6 +229,7 @@ def test_decode_paged_validation(L):
     assert d(*args(max_pages=0)) == ESHAPE
     assert d(*args(max_len=257)) == ESHAPE               # beyond max_pages * page_size
     assert d(*args(max_len=-1)) == ESHAPE
+    assert d(*args(page=1 << 16, max_pages=1 << 8, max_len=1 << 23)) == ESHAPE  # keys span 2 GiB
     assert d(*args(dt=F32)) == EUNSUP
     assert d(*args(D=96)) == EUNSUP
     assert d(*args(scale=float("inf"))) == EUNSUP
