@@ -34,7 +34,10 @@
 // unnormalised partial (max, sum, o[D]) per head to the fp32 workspace and
 // tags it; a workgroup that finds every partial of its (sequence, KV head,
 // head slice) tagged by this call combines them (log-sum-exp rescaling) and
-// writes the output, so one launch does the whole step.  Cache slots at or past a
+// writes the output, so one launch does the whole step.  That merge ends the
+// launch, so it is built for latency: a block of partials costs one memory
+// round trip, and each head's statistics come from DPP row reductions rather
+// than chained lane shuffles.  Cache slots at or past a
 // sequence's length never reach the result: loads of rows past it re-read the
 // last valid row (row 0 of an empty sequence) and their scores are masked.
 //
@@ -148,8 +151,6 @@ template <int D>
 struct DecodeSmem {
     // one V sub-tile slot per wave, in each of two arrays
     static constexpr int kSlots = DC_NW * DC_SUB * D * 2;
-    // partials per block of the final merge: its (factor, sum) table fills one array
-    static constexpr int kMB = kSlots / (2 * DC_HEADS * 4);
 };
 
 // Where the cached keys/values live.  Contiguous: k, v [B, Hkv, S_cap, D].
@@ -574,6 +575,7 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     constexpr int NSLOT = 24, EPI = 4, MBX = NSLOT;
     constexpr int NITEM = DC_HEADS * D / EPI / (DC_NW * 64);  // items per thread, at most
     static_assert(NITEM >= 1 && NITEM <= 2 && NSLOT % NITEM == 0, "merge slots");
+    static_assert(2 * DC_HEADS * MBX * 4 <= DecodeSmem<D>::kSlots, "merge tables fit one V slot array");
     const int ipt = GH * (D / EPI) > DC_NW * 64 ? 2 : 1;  // items this workgroup's threads fold
     const int MB = NSLOT / ipt;                           // partials per block
     float* const bm = (float*)vs0;          // [DC_HEADS][MBX] max, then factor
