@@ -66,6 +66,8 @@ def _load():
             i = ctypes.c_int
             lib.oracle_rope.argtypes = [P, P, i, i, i, i, i, P, ctypes.c_double]
             lib.oracle_rope.restype = None
+            lib.oracle_rope_transpose.argtypes = [P, P, i, i, i, i, i, P, ctypes.c_double]
+            lib.oracle_rope_transpose.restype = None
             lib.oracle_prefill.argtypes = [P, P, P, P, i, i, i, i, i, i,
                                            ctypes.c_double, P, ctypes.c_int64]
             lib.oracle_prefill.restype = i
@@ -169,6 +171,25 @@ def rope(x: np.ndarray, theta: float, pos_offset=None) -> np.ndarray:
     out = np.empty(x.shape, dtype=np.float64)
     _load().oracle_rope(_ptr(out), _ptr(x), _DT_CODE[dt], B, H, S, D, _ptr(off),
                         float(theta))
+    return out
+
+
+def rope_transpose(dy: np.ndarray, theta: float, pos_offset=None) -> np.ndarray:
+    """Transpose of the rotary embedding (the gradient map of rope): each pair
+    of dy [B, H, S, D] turned back by its angle.  Returns fp64 [B, H, S, D]."""
+    dt = _dtype_of(dy)
+    dy = _as_input(dy, dt)
+    B, H, S, D = dy.shape
+    if D % 2:
+        raise ValueError("RoPE needs an even head dim")
+    off = None
+    if pos_offset is not None:
+        off = np.ascontiguousarray(pos_offset, dtype=np.int32)
+        if off.shape != (B,):
+            raise ValueError("pos_offset must have shape [B]")
+    out = np.empty(dy.shape, dtype=np.float64)
+    _load().oracle_rope_transpose(_ptr(out), _ptr(dy), _DT_CODE[dt], B, H, S, D, _ptr(off),
+                                  float(theta))
     return out
 
 

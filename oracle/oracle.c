@@ -146,6 +146,32 @@ void oracle_rope(double *out, const void *x, int dt, int B, int H, int S, int D,
     }
 }
 
+/* Transpose of the rotary embedding, for gradients: the rotation of pair i at
+ * position p is the 2x2 matrix [[cos a, -sin a], [sin a, cos a]] with
+ * a = p * theta^(-2i/D); its transpose maps a gradient dy of the rotated pair
+ * back to the gradient of the unrotated pair:
+ *     out[2i] = dy[2i] cos a + dy[2i+1] sin a,
+ *     out[2i+1] = -dy[2i] sin a + dy[2i+1] cos a.
+ * Shapes and positions as oracle_rope. */
+void oracle_rope_transpose(double *out, const void *dy, int dt, int B, int H, int S, int D,
+                           const int32_t *pos_offset, double theta)
+{
+#pragma omp parallel for schedule(static)
+    for (long long r = 0; r < (long long)B * H * S; ++r) {
+        const int t = (int)(r % S);
+        const int b = (int)(r / ((long long)S * H));
+        const long long base = pos_offset ? pos_offset[b] : 0;
+        const size_t at = (size_t)r * (size_t)D;
+        for (int j = 0; j < D / 2; ++j) {
+            const double a = (double)(base + t) * pow(theta, -(2.0 * j) / D);
+            const double ca = cos(a), sa = sin(a);
+            const double g0 = load(dy, at + 2 * j, dt), g1 = load(dy, at + 2 * j + 1, dt);
+            out[at + 2 * j] = g0 * ca + g1 * sa;
+            out[at + 2 * j + 1] = g1 * ca - g0 * sa;
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Attention                                                           */
 /* ------------------------------------------------------------------ */

@@ -50,6 +50,9 @@ MUTANTS = {
     "dkv_first_head_only": ("for (int h = j * G; h < (j + 1) * G; ++h)",
                             "for (int h = j * G; h < j * G + 1; ++h)"),
     "dkv_skips_own_query": ("for (int i = t; i < S; ++i)", "for (int i = t + 1; i < S; ++i)"),
+    "rope_transpose_is_the_rotation": ("out[at + 2 * j] = g0 * ca + g1 * sa;",
+                                       "out[at + 2 * j] = g0 * ca - g1 * sa;"),
+    "rope_transpose_ignores_offset": ("(double)(base + t) * pow", "(double)(t) * pow"),
 }
 
 

@@ -641,3 +641,39 @@ def test_backward_widens_bf16_inputs_exactly():
     ref = oracle.prefill_backward(*[oracle.widen(x) for x in bits])
     for a, b in zip(got, ref):
         assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Transpose of RoPE (the gradient map through the rotation)
+# ---------------------------------------------------------------------------
+def test_rope_transpose_is_the_adjoint_of_rope():
+    """<y, R x> = <R^T y, x> for random x, y: the defining property of the
+    transpose, checked against the separately pinned forward rotation."""
+    g = np.random.default_rng(60)
+    x = g.standard_normal((2, 3, 11, 16))
+    y = g.standard_normal((2, 3, 11, 16))
+    off = np.array([5, 1000], dtype=np.int32)
+    lhs = float((y * oracle.rope(x, 1e4, off)).sum())
+    rhs = float((oracle.rope_transpose(y, 1e4, off) * x).sum())
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_rope_transpose_undoes_rope_and_is_identity_at_position_zero():
+    g = np.random.default_rng(61)
+    x = g.standard_normal((1, 2, 9, 64))
+    back = oracle.rope_transpose(oracle.rope(x, 5e5, np.array([123], dtype=np.int32)), 5e5,
+                                 np.array([123], dtype=np.int32))
+    assert np.allclose(back, x, rtol=0, atol=1e-12)
+    first = oracle.rope_transpose(x[:, :, :1], 5e5)
+    assert np.array_equal(first, x[:, :, :1])
+
+
+def test_rope_transpose_turns_pair_zero_back_by_the_position():
+    """Pair 0 has frequency 1: (1, 0) at position p goes to (cos p, -sin p)."""
+    S = 7
+    y = np.zeros((1, 1, S, 4))
+    y[..., 0] = 1.0
+    out = oracle.rope_transpose(y, 1e4)
+    p = np.arange(S)
+    assert np.allclose(out[0, 0, :, 0], np.cos(p), rtol=0, atol=1e-15)
+    assert np.allclose(out[0, 0, :, 1], -np.sin(p), rtol=0, atol=1e-15)
