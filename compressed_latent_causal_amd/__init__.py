@@ -6,6 +6,7 @@ PyTorch supplies device memory and the current stream.  There is no CPU
 fallback: calling into the library without the built ``libattn.so`` raises.
 
     rope(x, theta, pos_offset=None, pos_shift=0, out=None)
+    rope_backward(dy, theta, pos_offset=None, pos_shift=0, out=None)
     prefill(q, k, v, scale=None, out=None, rope_theta=0.0)
     prefill_lse(q, k, v, scale=None, out=None, lse=None, rope_theta=0.0)
     prefill_backward(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None, workspace=None)
@@ -25,7 +26,7 @@ from ._lib import (  # noqa: F401
     AttnError, lib, lib_path, DTYPE_CODES, STATUS,
 )
 
-__all__ = ["rope", "prefill", "prefill_lse", "prefill_backward", "prefill_backward_workspace_size",
+__all__ = ["rope", "rope_backward", "prefill", "prefill_lse", "prefill_backward", "prefill_backward_workspace_size",
            "decode", "decode_paged", "decode_workspace_size", "AttnError", "lib_path"]
 
 
@@ -81,6 +82,29 @@ def rope(x, theta: float, pos_offset=None, pos_shift: int = 0, out=None):
         po = pos_offset.data_ptr()
     _call(lib().attn_rope, out.data_ptr(), x.data_ptr(), _dtype_code(x), B, H, S, D, po,
           int(pos_shift), float(theta), _stream(x))
+    return out
+
+
+def rope_backward(dy, theta: float, pos_offset=None, pos_shift: int = 0, out=None):
+    """Transpose of rope(): carries a gradient of the rotated tensor back to the
+    unrotated one (same positions and theta).  out may be dy itself."""
+    torch = _torch()
+    if dy.dim() != 4:
+        raise ValueError("dy must be [B, H, S, D]")
+    B, H, S, D = dy.shape
+    if out is None:
+        out = torch.empty_like(dy)
+    if out.shape != dy.shape or out.dtype != dy.dtype:
+        raise ValueError("out must match dy")
+    _check_dev(dy, out)
+    po = 0
+    if pos_offset is not None:
+        if pos_offset.dtype != torch.int32 or pos_offset.shape != (B,):
+            raise ValueError("pos_offset must be int32 [B]")
+        _check_dev(pos_offset)
+        po = pos_offset.data_ptr()
+    _call(lib().attn_rope_backward, out.data_ptr(), dy.data_ptr(), _dtype_code(dy), B, H, S, D, po,
+          int(pos_shift), float(theta), _stream(dy))
     return out
 
 

@@ -24,6 +24,7 @@ STATUS = {
 P, I, D, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "attn_rope": (I, [P, P, I, I, I, I, I, P, I, D, P]),
+    "attn_rope_backward": (I, [P, P, I, I, I, I, I, P, I, D, P]),
     "attn_prefill": (I, [P, P, P, P, I, I, I, I, I, I, F, D, P]),
     "attn_prefill_lse": (I, [P, P, P, P, P, I, I, I, I, I, I, F, D, P]),
     "attn_prefill_backward_workspace_size": (SZ, [I, I, I]),

@@ -21,8 +21,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; 
 
 }  // namespace
 
-ATTN_API int attn_rope(void* out, const void* in, int dtype, int B, int H, int S, int D,
-                       const int32_t* pos_offset, int pos_shift, double theta, void* stream) {
+namespace {
+int rope_call(void* out, const void* in, int dtype, int B, int H, int S, int D,
+              const int32_t* pos_offset, int pos_shift, double theta, int transpose, void* stream) {
     if (B < 0 || S < 0 || H < 1) return ATTN_ERR_SHAPE;
     if (!known_dtype(dtype) || !supported_dim(D) || !(theta > 0.0) || !isfinite(theta))
         return ATTN_ERR_UNSUPPORTED;
@@ -31,7 +32,19 @@ ATTN_API int attn_rope(void* out, const void* in, int dtype, int B, int H, int S
     if (!out || !in) return ATTN_ERR_NULL;
     if (!aligned16(out) || !aligned16(in) || ((uintptr_t)pos_offset & 3u)) return ATTN_ERR_ALIGN;
     return hip_status(attn::launch_rope(out, in, dtype, B, H, S, D, pos_offset, pos_shift, theta,
-                                        (hipStream_t)stream));
+                                        transpose, (hipStream_t)stream));
+}
+}  // namespace
+
+ATTN_API int attn_rope(void* out, const void* in, int dtype, int B, int H, int S, int D,
+                       const int32_t* pos_offset, int pos_shift, double theta, void* stream) {
+    return rope_call(out, in, dtype, B, H, S, D, pos_offset, pos_shift, theta, 0, stream);
+}
+
+ATTN_API int attn_rope_backward(void* out, const void* in, int dtype, int B, int H, int S, int D,
+                                const int32_t* pos_offset, int pos_shift, double theta,
+                                void* stream) {
+    return rope_call(out, in, dtype, B, H, S, D, pos_offset, pos_shift, theta, 1, stream);
 }
 
 ATTN_API int attn_prefill(void* o, const void* q, const void* k, const void* v, int dtype, int B,

@@ -16,8 +16,11 @@ struct RopeFreqs;
 // theta^(-2i/D) for i < D/2, in double (host side)
 RopeFreqs rope_freqs(double theta, int D);
 
+// transpose != 0 applies the transpose of the rotation (rotation by the
+// negated angle), the map of gradients back through RoPE.
 hipError_t launch_rope(void* out, const void* in, int dtype, int B, int H, int S, int D,
-                       const int32_t* pos_offset, int pos_shift, double theta, hipStream_t st);
+                       const int32_t* pos_offset, int pos_shift, double theta, int transpose,
+                       hipStream_t st);
 
 // rope_theta > 0 rotates each query at its token index on the fly (k must
 // already be rotated); rope_theta == 0 takes q as given.  lse (bf16 only, may

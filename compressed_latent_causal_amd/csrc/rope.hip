@@ -18,6 +18,10 @@
 //   * sine and cosine of the reduced angle are evaluated in fp32.
 // The rotation itself is two fp32 multiply/FMA pairs per channel pair and the
 // result is rounded to the storage type once (round to nearest even).
+//
+// The same kernel applies the transpose of the rotation (the map that carries
+// a gradient of the rotated tensor back to the unrotated one): the rotation by
+// the negated angle, i.e. the same cosines with the sines negated.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,7 +32,7 @@ namespace {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_kernel(T* out, const T* in, int H, int S, int HB,
                                                    const int32_t* __restrict__ pos_offset,
-                                                   int pos_shift, RopeFreqs fr) {
+                                                   int pos_shift, RopeFreqs fr, int transpose) {
     constexpr int EPT = 16 / sizeof(T);  // elements per 16-byte chunk
     constexpr int PPT = EPT / 2;         // channel pairs per thread
     constexpr int CH = D / EPT;          // chunks per row
@@ -42,7 +46,10 @@ __global__ __launch_bounds__(256) void rope_kernel(T* out, const T* in, int H, i
     const long long p = (long long)(pos_offset ? pos_offset[b] : 0) + pos_shift + s;
     float cs[PPT], sn[PPT];
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) rope_cos_sin(p, fr.f[c * PPT + j], cs[j], sn[j]);
+    for (int j = 0; j < PPT; ++j) {
+        rope_cos_sin(p, fr.f[c * PPT + j], cs[j], sn[j]);
+        if (transpose) sn[j] = -sn[j];
+    }
 
     const size_t head_stride = (size_t)S * D;
     const size_t off = ((size_t)b * H * S + s) * D + (size_t)c * EPT;
@@ -83,7 +90,7 @@ __global__ __launch_bounds__(256) void rope_kernel(T* out, const T* in, int H, i
 
 template <typename T, int D>
 hipError_t launch_rope_t(void* out, const void* in, int B, int H, int S, const int32_t* pos_offset,
-                         int pos_shift, double theta, hipStream_t st) {
+                         int pos_shift, double theta, int transpose, hipStream_t st) {
     constexpr int TS = 256 / (D / (16 / sizeof(T)));
     const RopeFreqs fr = rope_freqs(theta, D);
     // Heads per workgroup: all of them when the token blocks alone fill the
@@ -95,7 +102,7 @@ hipError_t launch_rope_t(void* out, const void* in, int B, int H, int S, const i
     HB = min(HB, H);
     dim3 grid(ceil_div(S, TS), B, ceil_div(H, HB));
     hipLaunchKernelGGL((rope_kernel<T, D>), grid, dim3(256), 0, st, (T*)out, (const T*)in, H, S, HB,
-                       pos_offset, pos_shift, fr);
+                       pos_offset, pos_shift, fr, transpose);
     return hipGetLastError();
 }
 
@@ -108,12 +115,14 @@ RopeFreqs rope_freqs(double theta, int D) {
 }
 
 hipError_t launch_rope(void* out, const void* in, int dtype, int B, int H, int S, int D,
-                       const int32_t* pos_offset, int pos_shift, double theta, hipStream_t st) {
+                       const int32_t* pos_offset, int pos_shift, double theta, int transpose,
+                       hipStream_t st) {
+    const int tr = transpose ? 1 : 0;
     if (dtype == kBF16)
-        return D == 64 ? launch_rope_t<uint16_t, 64>(out, in, B, H, S, pos_offset, pos_shift, theta, st)
-                       : launch_rope_t<uint16_t, 128>(out, in, B, H, S, pos_offset, pos_shift, theta, st);
-    return D == 64 ? launch_rope_t<float, 64>(out, in, B, H, S, pos_offset, pos_shift, theta, st)
-                   : launch_rope_t<float, 128>(out, in, B, H, S, pos_offset, pos_shift, theta, st);
+        return D == 64 ? launch_rope_t<uint16_t, 64>(out, in, B, H, S, pos_offset, pos_shift, theta, tr, st)
+                       : launch_rope_t<uint16_t, 128>(out, in, B, H, S, pos_offset, pos_shift, theta, tr, st);
+    return D == 64 ? launch_rope_t<float, 64>(out, in, B, H, S, pos_offset, pos_shift, theta, tr, st)
+                   : launch_rope_t<float, 128>(out, in, B, H, S, pos_offset, pos_shift, theta, tr, st);
 }
 
 }  // namespace attn

@@ -82,6 +82,19 @@ int attn_rope(void *out, const void *in, int dtype, int B, int H, int S, int D,
               const int32_t *pos_offset, int pos_shift, double theta, void *stream);
 
 /*
+ * Transpose of attn_rope, for gradients: out = R^T in, where R is the rotation
+ * attn_rope applies with the same positions and theta.  Pair (2i, 2i+1) turns
+ * by the negated angle:
+ *     out[2i]   =  in[2i] cos(a) + in[2i+1] sin(a)
+ *     out[2i+1] = -in[2i] sin(a) + in[2i+1] cos(a),   a = p * theta^(-2i/D).
+ * Given the gradients attn_prefill_backward returns for the rotated q and k,
+ * this yields the gradients of the unrotated ones.  Arguments, layout,
+ * rounding and errors as attn_rope (out == in allowed).
+ */
+int attn_rope_backward(void *out, const void *in, int dtype, int B, int H, int S, int D,
+                       const int32_t *pos_offset, int pos_shift, double theta, void *stream);
+
+/*
  * Causal grouped-query attention over one sequence block ("prefill").
  *
  *   q, o: [B, Hq, S, D];  k, v: [B, Hkv, S, D];  Hq % Hkv == 0, G = Hq / Hkv.
@@ -133,7 +146,8 @@ size_t attn_prefill_backward_workspace_size(int B, int Hq, int S);
  * q, o, dout, dq: [B, Hq, S, D];  k, v, dk, dv: [B, Hkv, S, D];  lse: fp32
  * [B, Hq, S] from attn_prefill_lse on the same q, k, v, with o its output.
  * q and k are the tensors attention saw (already rotated); the gradients are
- * with respect to them.  bf16 only: bf16 matrix-core products with fp32
+ * with respect to them (attn_rope_backward carries dq and dk back through the
+ * rotation).  bf16 only: bf16 matrix-core products with fp32
  * accumulation, p and ds rounded to bf16 before their products, each
  * gradient rounded once to bf16.  Outputs must not overlap inputs.
  * workspace: at least attn_prefill_backward_workspace_size(B, Hq, S) bytes,

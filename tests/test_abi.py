@@ -59,8 +59,9 @@ def test_enum_values_match_header():
 
 
 # ---------------------------------------------------------------- rope
-def test_rope_validation(L):
-    r = lambda *a: L.attn_rope(*a)
+@pytest.mark.parametrize("name", ["attn_rope", "attn_rope_backward"])
+def test_rope_validation(L, name):
+    r = lambda *a: getattr(L, name)(*a)
     assert r(FAKE, FAKE, BF16, -1, 8, 16, 128, None, 0, 1e4, None) == ESHAPE
     assert r(FAKE, FAKE, BF16, 1, 0, 16, 128, None, 0, 1e4, None) == ESHAPE
     assert r(FAKE, FAKE, BF16, 1, 8, -2, 128, None, 0, 1e4, None) == ESHAPE

@@ -212,3 +212,34 @@ def test_prefill_backward_full_size_sampled_rows():
     _assert_grad(dq.reshape(-1, w.D)[qr].double().numpy(), rq, "dq rows", allow)
     _assert_grad(dk.reshape(-1, w.D)[kr].double().numpy(), rk, "dk rows")
     _assert_grad(dv.reshape(-1, w.D)[kr].double().numpy(), rv, "dv rows")
+
+
+def test_training_step_with_rope_end_to_end():
+    """Forward with the query RoPE fused and K rotated by attn_rope, backward
+    on the rotated q and k, then attn_rope_backward for dq and dk: the
+    gradients of the unrotated q and k match the oracle's chain (its backward
+    on its own rotations, then its transposed rotation)."""
+    B, Hq, Hkv, S, D, theta = 1, 8, 2, 160, 128, 5e5
+    w = wl.custom("prefill", "bf16", B, Hq, Hkv, D, S)
+    q, k, v, dout = wl.make_backward(w, seed=15)
+    say("training step with RoPE")
+    qd, kd, vd, gd = (t.cuda() for t in (q, k, v, dout))
+    kr = attn.rope(kd, theta)
+    o, lse = attn.prefill_lse(qd, kr, vd, rope_theta=theta)
+    qr = attn.rope(qd, theta)  # the rotated q the forward attended with
+    dqr, dkr, dv = attn.prefill_backward(qr, kr, vd, o, gd, lse)
+    dq = attn.rope_backward(dqr, theta)
+    dk = attn.rope_backward(dkr, theta)
+    torch.cuda.synchronize()
+    # oracle chain: rotations rounded to bf16 at the same boundaries as the GPU's
+    rq = oracle.round_bf16(oracle.rope(_bits(q), theta))
+    rk = oracle.round_bf16(oracle.rope(_bits(k), theta))
+    gq, gk, gv = oracle.prefill_backward(rq, rk, _bits(v), _bits(dout))
+    ref_dq = oracle.rope_transpose(gq, theta)
+    ref_dk = oracle.rope_transpose(gk, theta)
+    allow = _dq_delta_allowance(rq, rk, _bits(v), _bits(dout), w.scale)
+    # a rotation preserves each pair's length, so the dq allowance carries over pairwise
+    pair = np.sqrt(allow[..., 0::2] ** 2 + allow[..., 1::2] ** 2)
+    _assert_grad(dq.cpu().double().numpy(), ref_dq, "dq (unrotated)", np.repeat(pair, 2, axis=-1))
+    _assert_grad(dk.cpu().double().numpy(), ref_dk, "dk (unrotated)")
+    _assert_grad(dv.cpu().double().numpy(), gv, "dv")

@@ -165,6 +165,37 @@ def test_rope_decode_positions_from_lengths():
     assert_rope_rounding(y, oracle.rope(bits(q), 5e5, lens.numpy() - 1), bits(q))
 
 
+@pytest.mark.parametrize("D,theta,B,H,S,offsets", [
+    (128, 5e5, 2, 3, 37, [0, 131000]),
+    (64, 1e4, 1, 8, 300, [5]),
+    (128, 5e5, 3, 40, 1, [1, 8191, 131071]),
+])
+def test_rope_backward_bf16_matches_rounded_oracle_transpose(D, theta, B, H, S, offsets):
+    """The transpose carries the same rounding guarantee as the rotation: the
+    same angles with negated sines, one product and one FMA per output."""
+    g = rand_bf16((B, H, S, D), 200 + S)
+    off = None if offsets is None else torch.tensor(offsets, dtype=torch.int32)
+    say(f"rope_backward bf16 B={B} H={H} S={S} D={D} theta={theta} offsets={offsets}")
+    y = attn.rope_backward(dev(g), theta, None if off is None else dev(off))
+    torch.cuda.synchronize()
+    ref = oracle.rope_transpose(bits(g), theta, None if off is None else off.numpy())
+    assert_rope_rounding(bits(y), ref, bits(g))
+
+
+def test_rope_backward_fp32_undoes_rope_and_works_in_place():
+    x = torch.randn(2, 4, 50, 128, generator=torch.Generator().manual_seed(13))
+    offs = torch.tensor([3, 70000], dtype=torch.int32)
+    say("rope_backward fp32")
+    xd, od = dev(x), dev(offs)
+    y = attn.rope_backward(xd, 5e5, od)
+    assert_close(host_f64(y), oracle.rope_transpose(x.numpy(), 5e5, offs.numpy()), 2e-6,
+                 what="rope_backward fp32")
+    back = attn.rope_backward(attn.rope(xd, 5e5, od), 5e5, od)
+    assert_close(host_f64(back), x.double().numpy(), 2e-6, what="rope_backward(rope(x))")
+    attn.rope_backward(xd, 5e5, od, out=xd)
+    assert torch.equal(xd, y)
+
+
 # ============================================================== prefill
 def _oracle_prefill_e2e(q, k, v, theta, scale, dtype, rows=None):
     """Oracle pipeline: RoPE in fp64, rounded to the storage type (the dtype
