@@ -243,3 +243,47 @@ def test_training_step_with_rope_end_to_end():
     _assert_grad(dq.cpu().double().numpy(), ref_dq, "dq (unrotated)", np.repeat(pair, 2, axis=-1))
     _assert_grad(dk.cpu().double().numpy(), ref_dk, "dk (unrotated)")
     _assert_grad(dv.cpu().double().numpy(), gv, "dv")
+
+
+def test_prefill_backward_ignores_workspace_contents():
+    """The row statistics are rewritten on every call, padding rows included:
+    a NaN-filled workspace and a reused one give the same gradients."""
+    w = wl.custom("prefill", "bf16", 2, 8, 2, 64, 130)
+    q, k, v, dout = (t.cuda() for t in wl.make_backward(w, seed=16))
+    say("backward with a NaN-filled workspace")
+    o, lse = attn.prefill_lse(q, k, v)
+    n = attn.prefill_backward_workspace_size(w.B, w.Hq, w.S)
+    ws = torch.full((n // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    a = attn.prefill_backward(q, k, v, o, dout, lse, workspace=ws)
+    b = attn.prefill_backward(q, k, v, o, dout, lse, workspace=ws)
+    c = attn.prefill_backward(q, k, v, o, dout, lse)
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, b, c):
+        assert torch.isfinite(x.float()).all()
+        assert torch.equal(x, y) and torch.equal(x, z)
+
+
+def test_prefill_lse_full_size_sampled_rows():
+    """llama8b_prefill's log-normaliser on sampled rows (first, last and
+    block-edge queries included) within the per-row rounding bound."""
+    w = wl.WORKLOADS["llama8b_prefill"]
+    say("lse llama8b_prefill sampled rows")
+    q, k, v = wl.make_prefill(w, seed=0)
+    _, lse = attn.prefill_lse(q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    g = np.random.default_rng(5)
+    S = w.S
+    rows = np.concatenate([g.integers(0, w.B * w.Hq * S, 40),
+                           np.array([0, 31, 32, 63, 64, S - 1, w.B * w.Hq * S - 1])])
+    ref = oracle.prefill_lse(_bits(q), _bits(k), rows=rows)
+    got = lse.reshape(-1).cpu()[torch.from_numpy(rows)].double().numpy()
+    qf = oracle.widen(_bits(q)).reshape(-1, w.D)[rows]
+    G = w.Hq // w.Hkv
+    bound = []
+    for n, r in enumerate(rows):
+        i, h, b = r % S, (r // S) % w.Hq, r // (S * w.Hq)
+        kf = np.abs(oracle.widen(_bits(k[b, h // G, :i + 1])))
+        bound.append(2.0 ** -8 * ((kf @ np.abs(qf[n])).max() * w.scale + 1.0) + 1e-5)
+    err = np.abs(got - ref)
+    say(f"lse rows: max err {err.max():.3e}, worst err/bound {(err / np.array(bound)).max():.3f}")
+    assert (err <= np.array(bound)).all()
