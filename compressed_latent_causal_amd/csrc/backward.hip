@@ -209,7 +209,7 @@ __global__ __launch_bounds__(NW * 64, (NK == 1 && NW == 4) ? 2 : 1) void bwd_dkd
             };
             bf16x8_t af[NAF];
 #pragma unroll
-            for (int f = 0; f < BW_PD; ++f) af[f] = afrag(f);
+            for (int f = 0; f < BW_PD && f < NAF; ++f) af[f] = afrag(f);
 #pragma unroll
             for (int f = 0; f < NAF; ++f) {
                 if (f + BW_PD < NAF) af[f + BW_PD] = afrag(f + BW_PD);
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(NW * 64, (NK == 1 && NW == 4) ? 2 : 1) void bwd_dkd
             };
             bf16x8_t tf[NTF];
 #pragma unroll
-            for (int f = 0; f < BW_PD; ++f) tf[f] = tfrag(f);
+            for (int f = 0; f < BW_PD && f < NTF; ++f) tf[f] = tfrag(f);
 #pragma unroll
             for (int f = 0; f < NTF; ++f) {
                 if (f + BW_PD < NTF) tf[f + BW_PD] = tfrag(f + BW_PD);
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             };
             bf16x8_t af[NAF];
 #pragma unroll
-            for (int f = 0; f < BW_PD; ++f) af[f] = afrag(f);
+            for (int f = 0; f < BW_PD && f < NAF; ++f) af[f] = afrag(f);
 #pragma unroll
             for (int f = 0; f < NAF; ++f) {
                 if (f + BW_PD < NAF) af[f + BW_PD] = afrag(f + BW_PD);
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             };
             bf16x8_t tf[DT];
 #pragma unroll
-            for (int dt = 0; dt < TPD; ++dt) tf[dt] = tfrag(dt);
+            for (int dt = 0; dt < TPD && dt < DT; ++dt) tf[dt] = tfrag(dt);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 if (dt + TPD < DT) tf[dt + TPD] = tfrag(dt + TPD);
