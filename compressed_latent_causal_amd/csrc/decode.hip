@@ -27,7 +27,10 @@
 //     with the group's query heads (padded to 16) as the N dimension;
 //   * V rows are copied (16-byte loads, whole rows per lane group) into the
 //     wave's own LDS slot and read back with the LDS transpose read as the A
-//     operand of O^T = V^T P^T, P taken from registers as bf16;
+//     operand of O^T = V^T P^T, P taken from registers as bf16.  These copies
+//     carry the non-temporal cache policy: V bytes are read once per step, and
+//     the hint lifts the stream rate by 6 to 9% on this card (K loads with the
+//     same hint are slower, so they keep the default policy);
 //   * the softmax is online in fp32 (exp2 domain), one query head per lane.
 // The four waves then merge in LDS.  A sequence with a single split workgroup
 // writes its bf16 output right there.  Otherwise each workgroup writes one
@@ -64,6 +67,7 @@ namespace {
 constexpr int DC_NW = 4;      // waves per split workgroup
 constexpr int DC_SUB = 32;    // tokens per wave sub-tile
 constexpr int DC_HEADS = 16;  // query heads per split workgroup (MFMA N)
+constexpr int DC_V_POLICY = 2;  // cache policy of the V copies: nt (non-temporal)
 
 // Smallest number of sub-tiles one split workgroup is given: it bounds the
 // split workgroups (partial results) of a group, ceil(n_sub / DC_UMIN), and so
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
             const int tok = min(t0 + vrow[u], we - 1);
             __builtin_amdgcn_global_load_lds((const void*)(vb + (size_t)(tok - r0) * D + vcol[u] * 8),
                                              (__attribute__((address_space(3))) void*)(slot + u * 1024),
-                                             16, 0, 0);
+                                             16, 0, DC_V_POLICY);
         }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
