@@ -29,7 +29,7 @@
 //     wave's own LDS slot and read back with the LDS transpose read as the A
 //     operand of O^T = V^T P^T, P taken from registers as bf16.  These copies
 //     carry the non-temporal cache policy: V bytes are read once per step, and
-//     the hint lifts the stream rate by 6 to 9% on this card (K loads with the
+//     the hint lifts the stream rate by 7 to 9% on MI355X (K loads with the
 //     same hint are slower, so they keep the default policy);
 //   * the softmax is online in fp32 (exp2 domain), one query head per lane.
 // The four waves then merge in LDS.  A sequence with a single split workgroup
