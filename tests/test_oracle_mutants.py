@@ -31,6 +31,12 @@ MUTANTS = {
                              "int j = h % Hkv;\n                int n"),
     "decode_length_short": ("int n = seqlens[b];", "int n = seqlens[b] > 0 ? seqlens[b] - 1 : 0;"),
     "bf16_truncates": ("double r = rint(ldexp(x, -k));", "double r = trunc(ldexp(x, -k));"),
+    "f32_truncates": ("out[i] = (float)in[i]; /* C conversion",
+                      "{ float f = (float)in[i]; if (fabs((double)f) > fabs(in[i])) "
+                      "f = nextafterf(f, 0.0f); out[i] = f; } /* C conversion"),
+    "f32_flushes_subnormals": ("out[i] = (float)in[i]; /* C conversion",
+                               "out[i] = fabs(in[i]) < 0x1p-126 ? (float)copysign(0.0, in[i]) "
+                               ": (float)in[i]; /* C conversion"),
     "missing_normalisation": ("o[d] /= l;", "o[d] /= 1.0;"),
     "paged_ignores_table": ("size_t pg = (size_t)block_table[(size_t)b * max_pages + t / page_size];",
                             "size_t pg = (size_t)b * max_pages + t / page_size;"),

@@ -44,29 +44,31 @@ def _worked_example():
 
 
 def test_worked_example_inputs_are_the_pages_draws(golden_dir):
+    # The GQA glossary page ("Cómo funciona GQA") seeds torch's generator and
+    # draws q, k, v in that order with the shapes the golden file records; the
+    # tiny workload must hand out exactly those tensors.
     g = json.load(open(os.path.join(golden_dir, "gqa_worked_example.json")))
-    torch.manual_seed(g["seed"])
-    q = torch.randn(*g["q_shape"])
-    k = torch.randn(*g["kv_shape"])
-    v = torch.randn(*g["kv_shape"])
-    _, q2, k2, v2 = _worked_example()
-    assert np.array_equal(q.numpy(), q2)
-    assert np.array_equal(k.numpy(), k2)
-    assert np.array_equal(v.numpy(), v2)
+    w, q, k, v = _worked_example()
+    shapes = {"q": g["q_shape"], "k": g["kv_shape"], "v": g["kv_shape"]}
+    gen = torch.Generator().manual_seed(g["seed"])
+    drawn = {name: torch.randn(*shapes[name], generator=gen).numpy() for name in g["draw_order"]}
+    assert [w.B, w.Hq, w.S, w.D] == g["q_shape"] and [w.B, w.Hkv, w.S, w.D] == g["kv_shape"]
+    assert np.array_equal(drawn["q"], q)
+    assert np.array_equal(drawn["k"], k)
+    assert np.array_equal(drawn["v"], v)
 
 
 def test_worked_example_shape_and_mha_equivalence(golden_dir):
+    # GQA equals multi-head attention whose key/value heads are each copied to
+    # the G consecutive query heads of their group (same page and section).
     g = json.load(open(os.path.join(golden_dir, "gqa_worked_example.json")))
-    _, q, k, v = _worked_example()
+    w, q, k, v = _worked_example()
     out = oracle.prefill(q, k, v)
     assert list(out.shape) == g["output_shape"]
-    r = g["repeat_interleave_factor"]
-    k_full = np.repeat(k, r, axis=1)   # numpy repeat along an axis == repeat_interleave
-    v_full = np.repeat(v, r, axis=1)
-    ref = oracle.prefill(q, k_full, v_full)
-    close = bool(np.allclose(out, ref, atol=g["equivalence_atol"], rtol=0))
-    assert close == g["equals_repeat_interleaved_mha"]
-    # Same arithmetic in the same order: the equivalence holds bit for bit.
+    assert w.G == g["repeat_interleave_factor"]
+    ref = oracle.prefill(q, np.repeat(k, w.G, axis=1), np.repeat(v, w.G, axis=1))
+    assert g["equals_repeat_interleaved_mha"]
+    # same arithmetic in the same order: the equivalence holds bit for bit
     assert np.array_equal(out, ref)
 
 
@@ -78,14 +80,14 @@ def test_worked_example_matches_torch_sdpa():
 
 
 def test_cached_values_per_token(golden_dir):
+    # per token and layer the cache holds one key and one value vector per KV
+    # head: 2 * Hkv * D scalars (256 for the example), against 2 * Hq * D
+    # (1024) for multi-head attention ("Por qué GQA reduce la caché KV")
     g = json.load(open(os.path.join(golden_dir, "gqa_worked_example.json")))
-    _, q, k, _ = _worked_example()
-    hkv, d = k.shape[1], k.shape[3]
-    hq = q.shape[1]
-    assert oracle.kv_values_per_token(hkv, d) == g["cached_values_per_token_per_layer_gqa"]
-    assert oracle.kv_values_per_token(hq, d) == g["cached_values_per_token_per_layer_mha"]
-    # the page counts k[0, :, 0].numel() * 2
-    assert k[0, :, 0].size * 2 == g["cached_values_per_token_per_layer_gqa"]
+    w = wl.WORKLOADS["tiny_gqa"]
+    assert oracle.kv_values_per_token(w.Hkv, w.D) == 2 * w.Hkv * w.D
+    assert oracle.kv_values_per_token(w.Hkv, w.D) == g["cached_values_per_token_per_layer_gqa"]
+    assert oracle.kv_values_per_token(w.Hq, w.D) == g["cached_values_per_token_per_layer_mha"]
 
 
 def test_llama_kv_cache_bytes(golden_dir):
@@ -516,6 +518,60 @@ def test_round_bf16_does_not_round_twice():
     # the midpoint; direct rounding must still go up
     x = 1.0 + 2.0 ** -8 + 2.0 ** -30
     assert oracle.round_bf16(np.array([x]))[0] == 0x3F81
+
+
+def _f32_bits(a):
+    return [int(x) for x in np.asarray(a, dtype=np.float32).view(np.uint32)]
+
+
+def test_round_f32_ties_overflow_subnormals_and_zero():
+    # binary32 keeps 24 significant bits: the spacing above 1 is 2^-23, the
+    # largest finite value is (2 - 2^-23) 2^127 (0x7F7FFFFF), the smallest
+    # subnormal 2^-149.  Expected bit patterns follow from those facts alone.
+    cases = {
+        1.0 + 2.0 ** -24: 0x3F800000,               # halfway between 1 and 1+2^-23 -> 1 (even)
+        1.0 + 3 * 2.0 ** -24: 0x3F800002,           # halfway between 1+2^-23 and 1+2^-22 -> even
+        1.0 + 2.0 ** -24 + 2.0 ** -50: 0x3F800001,  # just above halfway -> up
+        1.0 + 2.0 ** -24 - 2.0 ** -50: 0x3F800000,  # just below halfway -> down
+        -(1.0 + 3 * 2.0 ** -24): 0xBF800002,
+        (2.0 - 2.0 ** -23) * 2.0 ** 127: 0x7F7FFFFF,                 # largest finite, exact
+        (2.0 - 2.0 ** -23) * 2.0 ** 127 + 2.0 ** 103: 0x7F800000,    # halfway to 2^128 -> inf
+        (2.0 - 2.0 ** -23) * 2.0 ** 127 + 2.0 ** 102: 0x7F7FFFFF,    # below halfway -> largest
+        -(2.0 ** 129): 0xFF800000,
+        2.0 ** -149: 0x00000001,                    # smallest subnormal
+        2.0 ** -150: 0x00000000,                    # halfway to zero -> zero (even)
+        3 * 2.0 ** -150: 0x00000002,                # halfway between 1 and 2 ulps -> even
+        2.0 ** -150 + 2.0 ** -170: 0x00000001,      # just above halfway -> up
+        -0.0: 0x80000000,
+        float("inf"): 0x7F800000,
+    }
+    got = oracle.round_f32(np.array(list(cases.keys())))
+    assert _f32_bits(got) == list(cases.values())
+    nan = oracle.round_f32(np.array([np.nan]))
+    assert _f32_bits(nan)[0] & 0x7FFFFFFF > 0x7F800000
+
+
+def test_round_f32_matches_numpy_cast_and_is_nearest():
+    rng = np.random.default_rng(49)
+    x = np.concatenate([
+        rng.standard_normal(20000),
+        rng.standard_normal(2000) * 1e-40,                       # subnormal range
+        rng.standard_normal(2000) * 3e38,                        # overflow edge
+        rng.integers(0, 2**64 - 1, 20000, dtype=np.uint64).view(np.float64),
+    ])
+    x = x[np.isfinite(x)]
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float32)
+    got = oracle.round_f32(x)
+    assert _f32_bits(got) == _f32_bits(ref)
+    # and, independently of any library cast, the result is a nearest binary32
+    # value: no neighbour (one ulp up or down) is strictly closer
+    fin = np.isfinite(got) & (np.abs(x) < 3e38)
+    g, xv = got[fin], x[fin]
+    up = np.nextafter(g, np.float32(np.inf)).astype(np.float64)
+    dn = np.nextafter(g, np.float32(-np.inf)).astype(np.float64)
+    err = np.abs(g.astype(np.float64) - xv)
+    assert np.all(err <= np.abs(up - xv)) and np.all(err <= np.abs(dn - xv))
 
 
 # ---------------------------------------------------------------------------
