@@ -13,8 +13,10 @@ with HIP events on the stream it runs on.  The `decode` object reports KV-cache
 GB/s of the two decode workloads (one decode step over several layers' caches
 back to back, caches evicted before each timed step), the `backward` object the
 training backward pass of both prefill workloads, and `cpu_baseline` times
-the fp64 CPU oracle on a bounded sample of the same prefill workload.  Prints
-one JSON line on stdout.
+the fp64 CPU oracle on a bounded sample of the same prefill workload (and on
+the gqa_decode batch).  `prefill_ccgqa` times the compressed-latent prefill
+(batch 2, 8 query heads, 2 KV heads, head dim 64, 16384 tokens) the same way
+as the headline step.  Prints one JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -273,6 +275,51 @@ DECODE_LINES = [("gqa_decode", "gqa_decode", 0), ("long_decode", "long_decode", 
                 ("gqa_decode_paged256", "gqa_decode", 256)]
 
 
+def prefill_line(w, steps, warmup):
+    """The prefill step of workload w (RoPE of K, then the prefill kernel with
+    the query RoPE fused), timed as the headline step is; reported beside it."""
+    flops = prefill_flops(w.B, w.Hq, w.S, w.D)
+    ms_step, ms_kern, kern_sorted = bench_prefill(w, steps, warmup)
+    tk = flops / (ms_kern * 1e-3) / 1e12
+    return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+            "head_dim": w.D, "seq_len": w.S, "rope_theta": w.theta,
+            "kernel": f"prefill_bf16_kernel<{w.D},4>", "flop_per_launch": flops,
+            "kernel_ms_mean": round(ms_kern, 5), "kernel_ms_min": round(kern_sorted[0], 5),
+            "TFLOP_per_s": round(tk, 1), "frac_of_mfma_peak": round(tk / PEAK_BF16_TFLOPS, 4),
+            "ms_per_step": round(ms_step, 5),
+            "step_TFLOP_per_s": round(flops / (ms_step * 1e-3) / 1e12, 1), "steps": steps,
+            "step": "rope(K) + causal GQA prefill with the query RoPE fused"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_decode(w):
+    """The oracle's decode (fp64 C, OpenMP over (sequence, head) rows) on the
+    whole batch of a decode workload, in GB/s of the same KV-cache bytes the
+    GPU line counts."""
+    import oracle
+    from compressed_latent_causal_amd import workloads as wl
+
+    q, kc, vc, lens = wl.make_decode(w, seed=0)
+    qb, kb, vb = (wl.to_numpy_bits(t) for t in (q, kc, vc))
+    t0 = time.perf_counter()
+    oracle.decode(qb, kb, vb, lens.numpy(), scale=w.scale)
+    el = time.perf_counter() - t0
+    nbytes = decode_bytes(lens.tolist(), w.Hkv, w.D)
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the whole {w.name} batch ({w.B} sequences, {int(lens.sum())} cached tokens), "
+                      f"{el:.2f} s wall"}
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The oracle (fp64 C, OpenMP) on a random sample of output rows of the
     same prefill workload: RoPE of all keys and of the sampled queries, then
@@ -306,7 +353,7 @@ def cpu_baseline(w, budget_s=15.0):
         elapsed = time.perf_counter() - t_start
         batch = min(batch * 2, 4096)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{n_rows} randomly drawn distinct output rows of {w.name} (of {n_total}), "
                       f"RoPE of all keys included, {elapsed:.1f} s wall"}
 
@@ -386,6 +433,11 @@ def main():
     if args.only:
         print(json.dumps(result), flush=True)
         return
+    # the compressed-latent prefill at 16k tokens, timed the same way
+    cc = prefill_line(wl.WORKLOADS["ccgqa_prefill"], args.steps, args.warmup)
+    log(f"prefill ccgqa_prefill: kernel mean {cc['kernel_ms_mean']:.4f} ms "
+        f"({cc['TFLOP_per_s']:.1f} TFLOP/s), step {cc['ms_per_step']:.4f} ms")
+    result["prefill_ccgqa"] = cc
     if not args.no_decode:
         dec = {}
         for name, wname, page in DECODE_LINES:
@@ -402,6 +454,8 @@ def main():
         result["backward"] = bwd
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        if not args.no_decode:
+            result["cpu_baseline"]["decode"] = cpu_baseline_decode(wl.WORKLOADS["gqa_decode"])
         log(f"cpu baseline: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
 

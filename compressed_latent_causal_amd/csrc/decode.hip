@@ -188,7 +188,7 @@ template <int D, bool PAGED>
 __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, DecodeCache cache, const int32_t* __restrict__ seqlens,
     float* __restrict__ ws_o, float* __restrict__ ws_ml, unsigned long long* __restrict__ ws_tag,
-    uint16_t* __restrict__ o, int Hq, int Hkv, int max_len, int NC, float c, int n_hchunk,
+    unsigned long long* __restrict__ ws_epoch, uint16_t* __restrict__ o, int Hq, int Hkv, int max_len, int NC, float c, int n_hchunk,
     int rope, RopeFreqs fr, unsigned long long tag, int B, int budget) {
     constexpr int KSTEPS = D / 32, DT = D / 16;
     constexpr int ROW = D * 2;                 // bytes per cache row
@@ -343,16 +343,25 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
             vb += off;
             r0 = min(t0, we - 1) / cache.page * cache.page;
         }
+        // rows before the window's first token (only in the sub-tile holding
+        // it, which lies in one page) re-read that token's row, as rows past
+        // the length re-read the last one: every row read is one the query
+        // sees, so a non-finite value outside the window never meets a zero
+        // probability in the product
+        auto row_tok = [&](int t) __attribute__((always_inline)) {
+            if constexpr (PAGED) t = max(t, w0);
+            return min(t, we - 1);
+        };
 #pragma unroll
         for (int u = 0; u < VINST; ++u) {
-            const int tok = min(t0 + vrow[u], we - 1);
+            const int tok = row_tok(t0 + vrow[u]);
             __builtin_amdgcn_global_load_lds((const void*)(vb + (size_t)(tok - r0) * D + vcol[u] * 8),
                                              (__attribute__((address_space(3))) void*)(slot + u * 1024),
                                              16, 0, DC_V_POLICY);
         }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const int tok = min(t0 + 16 * mt + lr, we - 1);
+            const int tok = row_tok(t0 + 16 * mt + lr);
 #pragma unroll
             for (int s = 0; s < KSTEPS; ++s)
                 kd[mt][s] = *(const bf16x8_t*)(kb + (size_t)(tok - r0) * D + 32 * s + 8 * lg);
@@ -513,6 +522,18 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
         }
         return;
     }
+    // This call's tag for the group: the host's call tag mixed with the
+    // group's epoch word, which the group's merging workgroup advances (below).
+    // Every workgroup of the group reads the epoch before it publishes
+    // anything, and the epoch only moves once all of them have published, so
+    // they all use the same tag.  Successive calls see successive epochs, so
+    // the tag changes even when a captured graph replays a launch with the
+    // same host tag.  The load is issued here, ahead of the partial stores,
+    // so its latency overlaps theirs.
+    const size_t grp = ((size_t)b * Hkv + kvh) * (size_t)n_hchunk + (size_t)hc;
+    const unsigned long long epoch =
+        __hip_atomic_load(ws_epoch + grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long ctag = tag ^ (epoch * 0x9E3779B97F4A7C15ull);
     {
         // this workgroup's partial o vectors, 16 bytes (4 dims of a head) per store
         const __amdgpu_buffer_rsrc_t ors =
@@ -549,24 +570,43 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
     // sees the other's tag.  Two may both merge (identical results, written
     // twice).  Slots written by other calls, or holding anything at all, carry
     // another tag, so the workspace needs no clearing between calls.
-    // Partials and tags are written and read with device-coherent
-    // (agent-scope) accesses, which bypass the per-XCD L2's non-coherent
-    // lines: once such a store has completed it is visible to every CU, and no
-    // device-wide fence (an L2 write-back and invalidate, costly for the
-    // workgroups still streaming the cache) is needed.
-    unsigned long long* const tags =
-        ws_tag + (((size_t)b * Hkv + kvh) * (size_t)n_hchunk + (size_t)hc) * (size_t)NC;
-    __builtin_amdgcn_s_waitcnt(0x0070);  // this thread's partial stores completed
+    //
+    // Why completed device-scope accesses suffice, with no fence.  In the
+    // AMDGPU memory model of LLVM's AMDGPU backend documentation (the GFX942
+    // section, which GFX950 follows), agent-scope atomic loads and stores are
+    // plain loads and stores with the SC1 bit, the device scope of the CDNA3
+    // instruction set's memory-scope bits: such a store writes through the
+    // issuing XCD's L2, and such a load misses in any L1 or L2 line that is not
+    // coherent at device scope, so it returns what completed device-scope
+    // stores from any XCD left in memory.  The same document's agent-scope
+    // release is an L2 write-back followed by a wait for vmcnt(0), and its
+    // acquire an L1/L2 invalidate; the write-back exists for earlier stores
+    // made without SC1 and the invalidate for later loads made without it.
+    // Here every store that is published (partials, their (max, sum) pairs and
+    // the tag) and every load that consumes them carries SC1 (the relaxed
+    // agent-scope atomics, and the 16-byte buffer accesses with cache policy
+    // bit 4, SC1), so the release reduces to the vmcnt(0) waits below, before
+    // the tag store, and the acquire to nothing: the partial loads are issued
+    // only after the barrier whose outcome depends on the tag loads.  A device-
+    // wide fence (L2 write-back and invalidate) measured 50% slower, because it
+    // stalls the workgroups still streaming the cache.
+    unsigned long long* const tags = ws_tag + grp * (size_t)NC;
+    __builtin_amdgcn_s_waitcnt(0x0070);  // this thread's partial stores (and epoch load) completed
     __syncthreads();
     if (tid == 0) {
-        __hip_atomic_store(tags + chunk, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(tags + chunk, ctag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_waitcnt(0x0070);  // the tag store completed
     }
     __syncthreads();
     int mine = 1;
     for (int ch = tid; ch < nwg; ch += DC_NW * 64)
-        mine &= __hip_atomic_load(tags + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+        mine &= __hip_atomic_load(tags + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ctag;
     if (!__syncthreads_and(mine)) return;
+    // every workgroup of the group has read the epoch (each did before its tag
+    // store): advance it for the group's next call (a store, so two merging
+    // workgroups leave the same value)
+    if (tid == 0)
+        __hip_atomic_store(ws_epoch + grp, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // ---- merge (log-sum-exp over the nwg partials).  Each thread folds one or
     // two items (a head and 4 consecutive dims each).  Partials are taken in
@@ -740,8 +780,10 @@ hipError_t launch_decode_d(void* o, const void* q, const DecodeCache& cache, int
     float* const ws_o = (float*)workspace;
     float* const ws_ml = ws_o + (size_t)B * Hq * NC * D;
     unsigned long long* const ws_tag = (unsigned long long*)(ws_ml + (size_t)B * Hq * NC * 2);
+    unsigned long long* const ws_epoch = ws_tag + (size_t)groups * NC;
     hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)nblocks), dim3(DC_NW * 64), 0,
-                       st, (const uint16_t*)q, cache, seqlens, ws_o, ws_ml, ws_tag, (uint16_t*)o, Hq,
+                       st, (const uint16_t*)q, cache, seqlens, ws_o, ws_ml, ws_tag, ws_epoch,
+                       (uint16_t*)o, Hq,
                        Hkv, max_len, NC, c, n_hchunk, rope_theta > 0 ? 1 : 0,
                        rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D), tag, B, budget);
     return hipGetLastError();
@@ -781,11 +823,12 @@ int decode_num_chunks(int B, int Hkv, int max_len) {
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int D) {
     // fp32 partials (o[D], max, sum) per (sequence, query head, split workgroup),
-    // then one 64-bit call tag per (sequence, KV head, head slice, split workgroup)
+    // then one 64-bit call tag per (sequence, KV head, head slice, split
+    // workgroup), then one 64-bit epoch per (sequence, KV head, head slice)
     const size_t NC = (size_t)decode_num_chunks(B, Hkv, max_len);
     const size_t n_hchunk = (size_t)ceil_div(Hq / Hkv, DC_HEADS);
     return (size_t)B * Hq * NC * (size_t)(D + 2) * sizeof(float) +
-           (size_t)B * Hkv * n_hchunk * NC * sizeof(unsigned long long);
+           (size_t)B * Hkv * n_hchunk * (NC + 1) * sizeof(unsigned long long);
 }
 
 hipError_t launch_decode(void* o, const void* q, const void* k_cache, const void* v_cache, int B,

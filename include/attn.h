@@ -163,10 +163,11 @@ int attn_prefill_backward(void *dq, void *dk, void *dv, const void *q, const voi
 /*
  * Bytes of device workspace attn_decode needs for these sizes (0 on invalid
  * sizes).  The workspace holds fp32 partial results (D + 2 floats) per
- * (sequence, query head, split workgroup) and one 64-bit call tag per
- * (sequence, KV head, slice of up to 16 query heads, split workgroup).  A
- * split workgroup covers at least 16 x 32 cache tokens, so a sequence has at
- * most ceil(max_len / 512) of them.
+ * (sequence, query head, split workgroup), one 64-bit call tag per
+ * (sequence, KV head, slice of up to 16 query heads, split workgroup) and one
+ * 64-bit epoch per (sequence, KV head, slice).  A split workgroup covers at
+ * least 16 x 32 cache tokens, so a sequence has at most ceil(max_len / 512)
+ * of them.
  */
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D);
 
@@ -190,8 +191,11 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D);
  * as given (already rotated).  The cache holds keys already rotated.
  * workspace: device buffer of at least attn_decode_workspace_size(...) bytes,
  * 16-byte aligned; its contents on entry do not matter (each call tags the
- * partial results it writes), and it must not be shared by calls that may
- * overlap.  dtype: BF16 only.  scale > 0 and finite.  One kernel is enqueued:
+ * partial results it writes with a host sequence number mixed with a per-group
+ * epoch kept in the workspace and advanced on the device, so the tags also
+ * differ between replays of one call captured in a HIP graph), and it must
+ * not be shared by calls that may overlap.  The call enqueues no memset or
+ * copy, so it may be captured in a graph.  dtype: BF16 only.  scale > 0 and finite.  One kernel is enqueued:
  * its workgroups read the lengths and split the batch's keys into nearly
  * equal parts (a sequence's keys go to one or more workgroups), and one that
  * finds all partial results of its (sequence, KV head) written merges them.

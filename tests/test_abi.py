@@ -168,8 +168,9 @@ def test_decode_workspace_size(L):
     n = ws(32, 32, 8, 8192, 128)
     # 8192 tokens = 256 sub-tiles of 32; a split workgroup takes at least 16
     # of them -> at most 16 partials per group; (D + 2) floats per (sequence,
-    # head, partial) and an 8-byte tag per (sequence, KV head, partial)
-    assert n == 32 * 32 * 16 * 130 * 4 + 32 * 8 * 16 * 8
+    # head, partial), an 8-byte tag per (sequence, KV head, partial) and an
+    # 8-byte epoch per (sequence, KV head)
+    assert n == 32 * 32 * 16 * 130 * 4 + 32 * 8 * 16 * 8 + 32 * 8 * 8
     # partials per (sequence, head, chunk): grows with max_len, never shrinks
     sizes = [ws(1, 64, 8, L_, 128) for L_ in (1, 512, 4096, 131072)]
     assert sizes == sorted(sizes) and sizes[0] > 0

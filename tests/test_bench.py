@@ -65,3 +65,12 @@ def test_cpu_baseline_record_on_a_small_workload():
     assert r["value"] > 0 and r["cores"] >= 1
     n = int(r["sample"].split()[0])
     assert 0 < n <= w.B * w.Hq * w.S
+    assert r["cpu_model"] == bench.cpu_model() and r["cpu_model"]
+
+
+def test_cpu_baseline_decode_record_on_a_small_workload():
+    w = wl.custom("decode", "bf16", 3, 8, 2, 64, 200, theta=5e5, len_lo=1, len_hi=200)
+    r = bench.cpu_baseline_decode(w)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s"
+    assert r["value"] > 0 and r["cores"] >= 1
+    assert "3 sequences" in r["sample"]

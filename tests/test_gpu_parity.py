@@ -522,6 +522,108 @@ def test_decode_paged_matches_oracle(case):
             assert (got[b] == 0).all()
 
 
+def test_decode_paged_window_never_reads_rows_before_the_window():
+    """Rows before a sequence's window share a page (and a 32-token sub-tile)
+    with the first row it sees; they hold NaN here, and must not reach the
+    output (a zero probability times NaN would)."""
+    B, Hq, Hkv, S_cap, D, P = 4, 8, 2, 2000, 128, 64
+    lens, window = [2000, 1000, 77, 40], 50
+    g = torch.Generator().manual_seed(77)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kc = torch.randn(B, Hkv, S_cap, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Hkv, S_cap, D, generator=g).to(torch.bfloat16)
+    lt = torch.tensor(lens, dtype=torch.int32)
+    for b, n in enumerate(lens):
+        lo = max(0, n - window)
+        kc[b, :, :lo] = float("nan")
+        vc[b, :, :lo] = float("nan")
+    kp, vp, table = wl.to_pages(kc, vc, lt, P, seed=3)
+    say(f"decode paged window {window}, NaN before the window, lens={lens}")
+    o = attn.decode_paged(dev(q), dev(kp), dev(vp), dev(table), dev(lt), max_len=max(lens),
+                          window=window)
+    ref = oracle.decode_paged(bits(q), bits(kp), bits(vp), np.maximum(table.numpy(), 0),
+                              lt.numpy(), window=window)
+    assert_close(host_f64(o), ref, BF16_MAX, BF16_MEAN, what="decode paged window NaN before")
+
+
+GRAPH_CASES = [  # B, Hq, Hkv, S_cap, D, paged page size (0: contiguous), window
+    (4, 32, 8, 6000, 128, 0, 0),      # few groups: several split workgroups each
+    (32, 32, 8, 8192, 128, 0, 0),     # the gqa_decode geometry
+    (3, 16, 2, 9000, 64, 256, 0),
+    (3, 16, 2, 9000, 128, 128, 3000),
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_CASES)
+def test_decode_in_a_captured_graph_matches_oracle_on_every_replay(case):
+    """One decode call captured in a HIP graph and replayed with new queries
+    and lengths written into its input buffers between replays (and eager
+    decode calls on the same workspace in between): every replay must match
+    the oracle, and a replay on unchanged inputs must repeat its result."""
+    B, Hq, Hkv, S_cap, D, P, window = case
+    theta = 5e5
+    g = torch.Generator().manual_seed(1000 + B + P)
+    kc = torch.randn(B, Hkv, S_cap, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Hkv, S_cap, D, generator=g).to(torch.bfloat16)
+    full = torch.full((B,), S_cap, dtype=torch.int32)
+    if P:
+        kp, vp, table = wl.to_pages(kc, vc, full, P, seed=4)
+        kd, vd, tb = dev(kp), dev(vp), dev(table)
+    else:
+        kd, vd = dev(kc), dev(vc)
+    qd = torch.zeros(B, Hq, D, dtype=torch.bfloat16, device=DEV)
+    ld = torch.zeros(B, dtype=torch.int32, device=DEV)
+    od = torch.zeros(B, Hq, D, dtype=torch.bfloat16, device=DEV)
+    ws = torch.full((attn.decode_workspace_size(B, Hq, Hkv, S_cap, D),), 0xA5, dtype=torch.uint8,
+                    device=DEV)
+
+    def call(q_, l_, out_):
+        if P:
+            return attn.decode_paged(q_, kd, vd, tb, l_, max_len=S_cap, window=window,
+                                     rope_theta=theta, out=out_, workspace=ws)
+        return attn.decode(q_, kd, vd, l_, max_len=S_cap, rope_theta=theta, out=out_,
+                           workspace=ws)
+
+    def expect(q, lens):
+        rq = oracle.round_bf16(oracle.rope(bits(q)[:, :, None, :], theta, lens.numpy() - 1))[:, :, 0]
+        if P:
+            return oracle.decode_paged(rq, bits(kp), bits(vp), table.numpy(), lens.numpy(),
+                                       window=window)
+        return oracle.decode(rq, bits(kc), bits(vc), lens.numpy())
+
+    say(f"decode graph capture {case}")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(qd, ld, od)
+    torch.cuda.synchronize()
+    prev = None
+    for r in range(4):
+        gg = torch.Generator().manual_seed(2000 + r)
+        q = torch.randn(B, Hq, D, generator=gg).to(torch.bfloat16)
+        lens = torch.randint(max(1, S_cap // 3), S_cap + 1, (B,), generator=gg, dtype=torch.int32)
+        if r == 3:   # unchanged inputs: the replay must repeat the previous result
+            q, lens = prev_q, prev_lens
+        qd.copy_(dev(q))
+        ld.copy_(dev(lens))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = od.clone()
+        if r == 3:
+            assert torch.equal(got, prev)
+        else:
+            assert_close(host_f64(got), expect(q, lens), BF16_MAX, BF16_MEAN,
+                         what=f"graph replay {r} {case}")
+        prev, prev_q, prev_lens = got, q, lens
+        # eager work on the same workspace between replays, with other lengths
+        eager_lens = torch.full((B,), S_cap - 7 * (r + 1), dtype=torch.int32)
+        eager = call(dev(q), dev(eager_lens), torch.empty_like(od))
+        torch.cuda.synchronize()
+        if r == 0:
+            assert_close(host_f64(eager), expect(q, eager_lens), BF16_MAX, BF16_MEAN,
+                         what=f"eager between replays {case}")
+
+
 def test_decode_paged_in_order_equals_contiguous_decode_bitwise():
     """The gqa_decode workload laid out as 256-token pages in order: the
     paged path reads the same rows in the same split, so it agrees bitwise."""
