@@ -13,6 +13,7 @@ fallback: calling into the library without the built ``libattn.so`` raises.
     prefill_backward_workspace_size(B, Hq, S)
     decode(q, k_cache, v_cache, seqlens, max_len=None, scale=None, rope_theta=0.0, out=None,
            workspace=None)
+    decode_noalloc(q, k_cache, v_cache, seqlens, out, max_len=None, scale=None, rope_theta=0.0)
     decode_workspace_size(B, Hq, Hkv, max_len, D)
 
 Shapes follow the C ABI: x [B,H,S,D]; q/o [B,Hq,S,D], k/v [B,Hkv,S,D];
@@ -23,11 +24,12 @@ from __future__ import annotations
 import math
 
 from ._lib import (  # noqa: F401
-    AttnError, lib, lib_path, DTYPE_CODES, STATUS,
+    AttnError, lib, lib_path, DTYPE_CODES, STATUS, DECODE_SCRATCH_BYTES,
 )
 
 __all__ = ["rope", "rope_backward", "prefill", "prefill_lse", "prefill_backward", "prefill_backward_workspace_size",
-           "decode", "decode_paged", "decode_workspace_size", "AttnError", "lib_path"]
+           "decode", "decode_noalloc", "decode_paged", "decode_workspace_size", "AttnError",
+           "lib_path", "DECODE_SCRATCH_BYTES"]
 
 
 def _torch():
@@ -233,6 +235,34 @@ def decode(q, k_cache, v_cache, seqlens, max_len: int | None = None, scale: floa
           v_cache.data_ptr(), _dtype_code(q), B, Hq, Hkv, S_cap, D, seqlens.data_ptr(),
           int(max_len), float(scale), float(rope_theta), workspace.data_ptr(),
           workspace.numel() * workspace.element_size(), _stream(q))
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, seqlens, out, max_len: int | None = None,
+                   scale: float | None = None, rope_theta: float = 0.0):
+    """decode() through the allocation-free entry point: no workspace, the
+    library's static per-device scratch instead (problems whose
+    decode_workspace_size exceeds DECODE_SCRATCH_BYTES are rejected).  The
+    caller passes the output buffer out [B,Hq,D]; nothing is allocated."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,Hq,D] and caches [B,Hkv,S_cap,D]")
+    B, Hq, D = q.shape
+    _, Hkv, S_cap, _ = k_cache.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("caches must be [B,Hkv,S_cap,D] with q's B and D")
+    if seqlens.dtype != torch.int32 or seqlens.shape != (B,):
+        raise ValueError("seqlens must be int32 [B]")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if max_len is None:
+        max_len = S_cap
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check_dev(q, k_cache, v_cache, seqlens, out)
+    _call(lib().attn_decode_noalloc, out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+          v_cache.data_ptr(), _dtype_code(q), B, Hq, Hkv, S_cap, D, seqlens.data_ptr(),
+          int(max_len), float(scale), float(rope_theta), _stream(q))
     return out
 
 

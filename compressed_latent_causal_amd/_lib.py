@@ -18,7 +18,11 @@ STATUS = {
     4: "ATTN_ERR_ALIGN",
     5: "ATTN_ERR_WORKSPACE",
     6: "ATTN_ERR_HIP",
+    7: "ATTN_ERR_SCRATCH",
 }
+
+# ATTN_DECODE_SCRATCH_BYTES: static per-device scratch of attn_decode_noalloc
+DECODE_SCRATCH_BYTES = 16 << 20
 
 # exported functions and their ctypes signatures (mirrors include/attn.h)
 P, I, D, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_float, ctypes.c_size_t
@@ -31,6 +35,7 @@ SIGNATURES = {
     "attn_prefill_backward": (I, [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P]),
     "attn_decode_workspace_size": (SZ, [I, I, I, I, I]),
     "attn_decode": (I, [P, P, P, P, I, I, I, I, I, I, P, I, F, D, P, SZ, P]),
+    "attn_decode_noalloc": (I, [P, P, P, P, I, I, I, I, I, I, P, I, F, D, P]),
     "attn_decode_paged": (I, [P, P, P, P, I, I, I, I, I, I, I, P, I, P, I, I, F, D, P, SZ, P]),
     "attn_status_string": (ctypes.c_char_p, [I]),
 }

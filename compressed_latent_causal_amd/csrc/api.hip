@@ -113,10 +113,13 @@ ATTN_API size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, 
     return attn::decode_workspace_bytes(B, Hq, Hkv, max_len, D);
 }
 
-ATTN_API int attn_decode(void* o, const void* q, const void* k_cache, const void* v_cache, int dtype,
-                         int B, int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens,
-                         int max_len, float scale, double rope_theta, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+namespace {
+// Checks shared by the contiguous decode entry points (everything but the
+// workspace).  *empty is set when there is nothing to do.
+int decode_checks(void* o, const void* q, const void* k_cache, const void* v_cache, int dtype,
+                  int B, int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens, int max_len,
+                  float scale, double rope_theta, bool* empty) {
+    *empty = false;
     if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_cap < 1 || max_len < 0 || max_len > S_cap)
         return ATTN_ERR_SHAPE;
     if (dtype != ATTN_BF16 || !supported_dim(D) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
@@ -124,17 +127,47 @@ ATTN_API int attn_decode(void* o, const void* q, const void* k_cache, const void
     if (B > kMaxGridYZ || (long long)Hkv * ((Hq / Hkv + 15) / 16) > kMaxGridYZ) return ATTN_ERR_SHAPE;
     // a group's partial results are addressed with 32-bit byte offsets
     if ((long long)max_len * D * 2 >= (1ll << 31)) return ATTN_ERR_SHAPE;
-    if (B == 0) return ATTN_OK;
+    if (B == 0) {
+        *empty = true;
+        return ATTN_OK;
+    }
     if (!o || !q || !k_cache || !v_cache || !seqlens) return ATTN_ERR_NULL;
     if (!aligned16(o) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
         ((uintptr_t)seqlens & 3u))
         return ATTN_ERR_ALIGN;
+    return ATTN_OK;
+}
+}  // namespace
+
+ATTN_API int attn_decode(void* o, const void* q, const void* k_cache, const void* v_cache, int dtype,
+                         int B, int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens,
+                         int max_len, float scale, double rope_theta, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    bool empty = false;
+    const int rc = decode_checks(o, q, k_cache, v_cache, dtype, B, Hq, Hkv, S_cap, D, seqlens,
+                                 max_len, scale, rope_theta, &empty);
+    if (rc != ATTN_OK || empty) return rc;
     const size_t need = attn::decode_workspace_bytes(B, Hq, Hkv, max_len, D);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
     return hip_status(attn::launch_decode(o, q, k_cache, v_cache, B, Hq, Hkv, S_cap, D, seqlens,
                                           max_len, scale, rope_theta, workspace,
                                           (hipStream_t)stream));
+}
+
+ATTN_API int attn_decode_noalloc(void* o, const void* q, const void* k_cache, const void* v_cache,
+                                 int dtype, int B, int Hq, int Hkv, int S_cap, int D,
+                                 const int32_t* seqlens, int max_len, float scale,
+                                 double rope_theta, void* stream) {
+    bool empty = false;
+    const int rc = decode_checks(o, q, k_cache, v_cache, dtype, B, Hq, Hkv, S_cap, D, seqlens,
+                                 max_len, scale, rope_theta, &empty);
+    if (rc != ATTN_OK || empty) return rc;
+    if (attn::decode_workspace_bytes(B, Hq, Hkv, max_len, D) > (size_t)ATTN_DECODE_SCRATCH_BYTES)
+        return ATTN_ERR_SCRATCH;
+    return hip_status(attn::launch_decode_noalloc(o, q, k_cache, v_cache, B, Hq, Hkv, S_cap, D,
+                                                  seqlens, max_len, scale, rope_theta,
+                                                  (hipStream_t)stream));
 }
 
 ATTN_API int attn_decode_paged(void* o, const void* q, const void* k_pages, const void* v_pages,
@@ -175,6 +208,9 @@ ATTN_API const char* attn_status_string(int status) {
         case ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
         case ATTN_ERR_HIP: return "kernel launch failed";
+        case ATTN_ERR_SCRATCH:
+            return "the problem needs more scratch than the allocation-free entry point holds "
+                   "(ATTN_DECODE_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

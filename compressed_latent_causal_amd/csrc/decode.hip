@@ -57,8 +57,17 @@
 #include <atomic>
 #include <chrono>
 
+#include "../../include/attn.h"
 #include "common.hpp"
 #include "kernels.hpp"
+
+// Scratch of the allocation-free decode entry point (attn_decode_noalloc): the
+// split pass's partial results, call tags and epochs, in a static array that
+// each device holds from the library's load to the end of the process.  Host
+// code never uses its name as an address (on the host it names a stand-in,
+// not device memory): the device address is looked up per device with
+// hipGetSymbolAddress and passed to the kernel as its workspace.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_SCRATCH_BYTES];
 
 namespace attn {
 
@@ -837,6 +846,46 @@ hipError_t launch_decode(void* o, const void* q, const void* k_cache, const void
     const DecodeCache cache{(const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr, S_cap, 0, 0, 0, 0};
     return launch_decode_any<false>(o, q, cache, B, Hq, Hkv, D, seqlens, max_len, scale, rope_theta,
                                     workspace, st);
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on device dev, looked up once per device with
+// that device current (each device holds its own copy of the array).
+hipError_t scratch_address(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_decode_noalloc(void* o, const void* q, const void* k_cache, const void* v_cache,
+                                 int B, int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens,
+                                 int max_len, float scale, double rope_theta, hipStream_t st) {
+    int dev = 0;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    void* ws = nullptr;
+    if ((e = scratch_address(dev, &ws)) != hipSuccess) return e;
+    return launch_decode(o, q, k_cache, v_cache, B, Hq, Hkv, S_cap, D, seqlens, max_len, scale,
+                         rope_theta, ws, st);
 }
 
 hipError_t launch_decode_paged(void* o, const void* q, const void* k_pages, const void* v_pages,

@@ -49,6 +49,12 @@ hipError_t launch_decode(void* o, const void* q, const void* k_cache, const void
                          int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens, int max_len,
                          float scale, double rope_theta, void* workspace, hipStream_t st);
 
+// launch_decode with the library's static per-device scratch as its workspace
+// (the caller has checked that decode_workspace_bytes fits it).
+hipError_t launch_decode_noalloc(void* o, const void* q, const void* k_cache, const void* v_cache,
+                                 int B, int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens,
+                                 int max_len, float scale, double rope_theta, hipStream_t st);
+
 // Decode over a paged cache (pages [num_pages, Hkv, page_size, D], page_size a
 // multiple of 32, block_table [B, max_pages]); window > 0 limits each query to
 // its sequence's last `window` tokens.

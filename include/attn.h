@@ -56,8 +56,12 @@ typedef enum {
     ATTN_ERR_UNSUPPORTED = 3,  /* D not 64/128, unknown dtype, theta/scale out of range, f32 decode/training */
     ATTN_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_WORKSPACE = 5,    /* workspace missing or too small */
-    ATTN_ERR_HIP = 6           /* a kernel launch failed */
+    ATTN_ERR_HIP = 6,          /* a kernel launch failed */
+    ATTN_ERR_SCRATCH = 7       /* attn_decode_noalloc: the problem exceeds ATTN_DECODE_SCRATCH_BYTES */
 } attn_status;
+
+/* Bytes of the static per-device scratch behind attn_decode_noalloc. */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
 
 /*
  * Rotary position embedding of x [B, H, S, D] into out [B, H, S, D].
@@ -204,6 +208,29 @@ int attn_decode(void *o, const void *q, const void *k_cache, const void *v_cache
                 int B, int Hq, int Hkv, int S_cap, int D, const int32_t *seqlens,
                 int max_len, float scale, double rope_theta, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, results and errors are those of
+ * attn_decode; the split pass's partial results live instead in a static
+ * array of ATTN_DECODE_SCRATCH_BYTES (16 MiB) that every device the library
+ * runs on holds until the process ends.  The call allocates and frees nothing.
+ * The problem must fit that array: attn_decode_workspace_size(B, Hq, Hkv,
+ * max_len, D) <= ATTN_DECODE_SCRATCH_BYTES (both decode workloads of 32 x 8192
+ * and 1 x 131072 tokens at D = 128 need about 8.5 MB), else ATTN_ERR_SCRATCH
+ * with nothing enqueued.  All calls on one device share its array and find
+ * the previous call's contents there, which, as for attn_decode, do not matter
+ * (nothing needs to start at zero); calls that may overlap on one device (on
+ * concurrent streams) race on it and must not be issued.  The first call on a
+ * device looks up the array's device address (hipGetSymbolAddress, with that
+ * device current), so make it outside graph capture.  The stream's device
+ * (the current device for the null stream) selects the array.
+ */
+int attn_decode_noalloc(void *o, const void *q, const void *k_cache, const void *v_cache,
+                        int dtype, int B, int Hq, int Hkv, int S_cap, int D,
+                        const int32_t *seqlens, int max_len, float scale, double rope_theta,
+                        void *stream);
 
 /*
  * Decode over a paged KV cache, optionally limited to a sliding window.

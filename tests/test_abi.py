@@ -14,7 +14,7 @@ from compressed_latent_causal_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
-OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP = range(7)
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP, ESCRATCH = range(8)
 F32, BF16 = 0, 1
 FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(7):
+    for s in range(8):
         assert L.attn_status_string(s).decode()
     assert L.attn_status_string(99) == b"unknown status"
 
@@ -52,7 +52,7 @@ def test_enum_values_match_header():
     text = open(HEADER).read()
     for name, val in [("ATTN_F32", 0), ("ATTN_BF16", 1), ("ATTN_OK", 0), ("ATTN_ERR_NULL", 1),
                       ("ATTN_ERR_SHAPE", 2), ("ATTN_ERR_UNSUPPORTED", 3), ("ATTN_ERR_ALIGN", 4),
-                      ("ATTN_ERR_WORKSPACE", 5), ("ATTN_ERR_HIP", 6)]:
+                      ("ATTN_ERR_WORKSPACE", 5), ("ATTN_ERR_HIP", 6), ("ATTN_ERR_SCRATCH", 7)]:
         assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
         if name.startswith("ATTN_ERR") or name == "ATTN_OK":
             assert _lib.STATUS[val] == name
@@ -275,3 +275,31 @@ def test_package_does_not_import_the_oracle():
             assert not re.search(r"^\s*(import|from)\s+compressed_latent_causal_amd\b", text,
                                  re.M), f
             assert "libattn" not in text, f
+
+
+def test_decode_noalloc_validation(L):
+    """Same checks as attn_decode, minus the workspace; problems whose
+    workspace would exceed the static scratch are refused before any HIP call."""
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.DECODE_SCRATCH_BYTES
+    d = lambda *a: L.attn_decode_noalloc(*a)
+    args = lambda **kw: [kw.get("o", FAKE), kw.get("q", FAKE), kw.get("k", FAKE), kw.get("v", FAKE),
+                         kw.get("dt", BF16), kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 2),
+                         kw.get("S_cap", 64), kw.get("D", 128), kw.get("lens", FAKE),
+                         kw.get("max_len", 64), kw.get("scale", 0.1), kw.get("theta", 0.0), None]
+    assert d(*args(Hkv=3)) == ESHAPE
+    assert d(*args(max_len=65)) == ESHAPE
+    assert d(*args(dt=F32)) == EUNSUP
+    assert d(*args(D=96)) == EUNSUP
+    assert d(*args(scale=0.0)) == EUNSUP
+    for name in ("o", "q", "k", "v", "lens"):
+        assert d(*args(**{name: None})) == ENULL
+    assert d(*args(lens=FAKE + 2)) == EALIGN
+    assert d(*args(o=None, q=None, k=None, v=None, lens=None, B=0)) == OK
+    # the two decode workloads fit the scratch; twice the first does not
+    ws = L.attn_decode_workspace_size
+    assert ws(32, 32, 8, 8192, 128) <= _lib.DECODE_SCRATCH_BYTES
+    assert ws(1, 64, 8, 131072, 128) <= _lib.DECODE_SCRATCH_BYTES
+    assert ws(64, 32, 8, 8192, 128) > _lib.DECODE_SCRATCH_BYTES
+    assert d(*args(B=64, Hq=32, Hkv=8, S_cap=8192, max_len=8192)) == ESCRATCH
