@@ -84,6 +84,9 @@ def _load():
                                                     ctypes.c_double, P, ctypes.c_int64, P,
                                                     ctypes.c_int64]
             lib.oracle_prefill_backward.restype = i
+            lib.oracle_cca_mix.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, P, P, i, P, P, P,
+                                           ctypes.c_double]
+            lib.oracle_cca_mix.restype = i
             lib.oracle_round_bf16.argtypes = [P, P, ctypes.c_size_t]
             lib.oracle_round_bf16.restype = None
             lib.oracle_round_f32.argtypes = [P, P, ctypes.c_size_t]
@@ -360,3 +363,43 @@ def prefill_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarr
     if rc:
         raise RuntimeError(f"oracle_prefill_backward failed ({rc})")
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# CCA pre-attention operations ("Compressed Convolutional Attention",
+# "Methodologie" items 2-4)
+# ---------------------------------------------------------------------------
+def cca_mix(q: np.ndarray, k: np.ndarray, v: np.ndarray, conv_q: np.ndarray, conv_k: np.ndarray,
+            mix_q: np.ndarray, mix_k: np.ndarray, pos_offset=None, theta: float = 0.0):
+    """The compressed q~ [B,Hq,S,D], k~, v~ [B,Hkv,S,D] through the CCA
+    pre-attention operations (oracle.c, oracle_cca_mix): a causal depthwise
+    sequence convolution of width W (conv_q [Hq,D,W], conv_k [Hkv,D,W]; tap i
+    weighs the token i steps back), a dense channel mix per head (mix_q
+    [Hq,D,D], mix_k [Hkv,D,D]; row c is output channel c), plus the group's
+    pre-convolution query/key mean; RoPE of the result when theta > 0; and
+    the value shift (second half of each head's channels from the previous
+    token).  All inputs share one dtype.  Returns fp64 (q, k, v)."""
+    dt = _dtype_of(q)
+    q, k, v, conv_q, conv_k, mix_q, mix_k = (_as_input(t, dt) for t in
+                                             (q, k, v, conv_q, conv_k, mix_q, mix_k))
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    W = conv_q.shape[-1]
+    if (k.shape != (B, Hkv, S, D) or v.shape != k.shape or Hq % Hkv or D % 2
+            or conv_q.shape != (Hq, D, W) or conv_k.shape != (Hkv, D, W)
+            or mix_q.shape != (Hq, D, D) or mix_k.shape != (Hkv, D, D)):
+        raise ValueError("bad shapes")
+    off = None
+    if pos_offset is not None:
+        off = np.ascontiguousarray(pos_offset, dtype=np.int32)
+        if off.shape != (B,):
+            raise ValueError("pos_offset must have shape [B]")
+    qo = np.empty((B, Hq, S, D), dtype=np.float64)
+    ko = np.empty((B, Hkv, S, D), dtype=np.float64)
+    vo = np.empty((B, Hkv, S, D), dtype=np.float64)
+    rc = _load().oracle_cca_mix(_ptr(qo), _ptr(ko), _ptr(vo), _ptr(q), _ptr(k), _ptr(v),
+                                _DT_CODE[dt], B, Hq, Hkv, S, D, _ptr(conv_q), _ptr(conv_k), W,
+                                _ptr(mix_q), _ptr(mix_k), _ptr(off), float(theta))
+    if rc:
+        raise RuntimeError(f"oracle_cca_mix failed ({rc})")
+    return qo, ko, vo

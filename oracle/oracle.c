@@ -596,3 +596,122 @@ int oracle_prefill_backward(double *dq, double *dk, double *dv, const void *q, c
     free(grp);
     return bad;
 }
+
+
+/* ------------------------------------------------------------------ */
+/* CCA pre-attention operations on the compressed q, k, v              */
+/* ------------------------------------------------------------------ */
+/* "Compressed Convolutional Attention" summary, "Methodologie", items 2-4.
+ * The summary names the operations without their sizes or exact form; this
+ * oracle follows the plainest reading of it (stated item by item below).
+ * Inputs are the compressed per-head vectors q~ [B, Hq, S, D], k~, v~
+ * [B, Hkv, S, D]; query head h belongs to KV group h / G, G = Hq / Hkv.
+ *
+ *  (2a) sequence mixing: a causal depthwise convolution over the sequence, of
+ *       width W, per channel c of every head:
+ *           s[t, c] = sum_{i < W, t - i >= 0} conv[h, c, i] * x[t - i, c]
+ *       (tap i weighs the token i steps back; tokens before the first are 0);
+ *  (2b) channel mixing within a head: a dense D x D map per head,
+ *           z[t, c] = sum_{c'} mix[h, c, c'] * s[t, c'];
+ *  (2c) QK-mean: the mean of the pre-convolution query and key vectors of a
+ *       token, shared by the group (the query heads of a group first averaged),
+ *           m[t, j] = ( (1/G) sum_{h in group j} q~[t, h] + k~[t, j] ) / 2,
+ *       is added to the convolved vectors: q[t, h] = z_q[t, h] + m[t, h / G],
+ *       k[t, j] = z_k[t, j] + m[t, j] (a skip path of the pre-convolution
+ *       values, and a component q and k of one token share);
+ *  (4)  RoPE, when theta > 0, on those q and k at absolute position
+ *       pos_offset[b] + t (oracle_rope, the same rotation as everywhere);
+ *  (3)  value shift: each head's values come half from the current token and
+ *       half from the previous one: v[t, c] = v~[t, c] for c < D/2 and
+ *       v~[t - 1, c] for c >= D/2 (0 at t = 0).
+ * conv_q [Hq, D, W], conv_k [Hkv, D, W], mix_q [Hq, D, D], mix_k [Hkv, D, D]
+ * (row c of mix is output channel c) share the inputs' element type dt.
+ * Outputs are fp64 [B, Hq, S, D], [B, Hkv, S, D], [B, Hkv, S, D]. */
+int oracle_cca_mix(double *q_out, double *k_out, double *v_out, const void *q, const void *k,
+                   const void *v, int dt, int B, int Hq, int Hkv, int S, int D,
+                   const void *conv_q, const void *conv_k, int W, const void *mix_q,
+                   const void *mix_k, const int32_t *pos_offset, double theta)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || W <= 0 || Hq % Hkv != 0 || D % 2)
+        return 1;
+    const int G = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *mean = (double *)malloc(sizeof(double) * (size_t)Hkv * D);
+        double *conv = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!mean || !conv) {
+#pragma omp atomic write
+            bad = 2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t bt = 0; bt < (int64_t)B * S; ++bt) {
+                const int b = (int)(bt / S), t = (int)(bt % S);
+                /* (2c) the token's pre-convolution mean, per KV group */
+                for (int j = 0; j < Hkv; ++j)
+                    for (int c = 0; c < D; ++c) {
+                        double qsum = 0.0;
+                        for (int r = 0; r < G; ++r)
+                            qsum += load(q, (((size_t)b * Hq + (size_t)j * G + r) * S + t) * D + c, dt);
+                        const double kv = load(k, (((size_t)b * Hkv + j) * S + t) * D + c, dt);
+                        mean[(size_t)j * D + c] = 0.5 * (qsum / G + kv);
+                    }
+                /* (2a), (2b) and the mean, for the query heads and then the key heads */
+                for (int n = 0; n < Hq + Hkv; ++n) {
+                    const int isq = n < Hq;
+                    const int h = isq ? n : n - Hq;
+                    const int H = isq ? Hq : Hkv;
+                    const void *x = isq ? q : k;
+                    const void *cw = isq ? conv_q : conv_k;
+                    const void *mw = isq ? mix_q : mix_k;
+                    const double *mrow = mean + (size_t)(isq ? h / G : h) * D;
+                    double *out = (isq ? q_out : k_out) + (((size_t)b * H + h) * S + t) * D;
+                    for (int c = 0; c < D; ++c) {
+                        double acc = 0.0;
+                        for (int i = 0; i < W; ++i) {
+                            int src = t - i;
+                            if (src < 0)
+                                continue;
+                            acc += load(cw, ((size_t)h * D + c) * W + i, dt) *
+                                   load(x, (((size_t)b * H + h) * S + src) * D + c, dt);
+                        }
+                        conv[c] = acc;
+                    }
+                    for (int c = 0; c < D; ++c) {
+                        double acc = 0.0;
+                        for (int c2 = 0; c2 < D; ++c2)
+                            acc += load(mw, ((size_t)h * D + c) * D + c2, dt) * conv[c2];
+                        out[c] = acc + mrow[c];
+                    }
+                }
+                /* (3) value shift */
+                for (int j = 0; j < Hkv; ++j)
+                    for (int c = 0; c < D; ++c) {
+                        const size_t at = (((size_t)b * Hkv + j) * S + t) * D + c;
+                        double val;
+                        if (c < D / 2)
+                            val = load(v, at, dt);
+                        else
+                            val = t > 0 ? load(v, at - (size_t)D, dt) : 0.0;
+                        v_out[at] = val;
+                    }
+            }
+        }
+        free(mean);
+        free(conv);
+    }
+    if (bad)
+        return bad;
+    /* (4) RoPE of the mixed q and k at their absolute positions */
+    if (theta > 0.0) {
+        double *tmp = (double *)malloc(sizeof(double) * (size_t)B * Hq * S * D);
+        if (!tmp)
+            return 2;
+        memcpy(tmp, q_out, sizeof(double) * (size_t)B * Hq * S * D);
+        oracle_rope(q_out, tmp, OR_F64, B, Hq, S, D, pos_offset, theta);
+        memcpy(tmp, k_out, sizeof(double) * (size_t)B * Hkv * S * D);
+        oracle_rope(k_out, tmp, OR_F64, B, Hkv, S, D, pos_offset, theta);
+        free(tmp);
+    }
+    return 0;
+}

@@ -59,6 +59,25 @@ MUTANTS = {
     "rope_transpose_is_the_rotation": ("out[at + 2 * j] = g0 * ca + g1 * sa;",
                                        "out[at + 2 * j] = g0 * ca - g1 * sa;"),
     "rope_transpose_ignores_offset": ("(double)(base + t) * pow", "(double)(t) * pow"),
+    "cca_conv_taps_reversed": ("acc += load(cw, ((size_t)h * D + c) * W + i, dt) *",
+                               "acc += load(cw, ((size_t)h * D + c) * W + (W - 1 - i), dt) *"),
+    "cca_conv_wraps_around": ("if (src < 0)\n                                continue;",
+                              "if (src < 0)\n                                src += S;"),
+    "cca_conv_looks_ahead": ("int src = t - i;", "int src = t + i < S ? t + i : -1;"),
+    "cca_mix_transposed": ("load(mw, ((size_t)h * D + c) * D + c2, dt)",
+                           "load(mw, ((size_t)h * D + c2) * D + c, dt)"),
+    "cca_mean_without_half": ("mean[(size_t)j * D + c] = 0.5 * (qsum / G + kv);",
+                              "mean[(size_t)j * D + c] = (qsum / G + kv);"),
+    "cca_mean_of_sum_not_average": ("0.5 * (qsum / G + kv)", "0.5 * (qsum + kv)"),
+    "cca_mean_modulo_groups": ("mean + (size_t)(isq ? h / G : h) * D",
+                               "mean + (size_t)(isq ? h % Hkv : h) * D"),
+    "cca_mean_dropped_from_keys": ("out[c] = acc + mrow[c];", "out[c] = acc + (isq ? mrow[c] : 0.0);"),
+    "cca_shift_wrong_half": ("if (c < D / 2)\n                            val = load(v, at, dt);",
+                             "if (c >= D / 2)\n                            val = load(v, at, dt);"),
+    "cca_shift_from_next_token": ("val = t > 0 ? load(v, at - (size_t)D, dt) : 0.0;",
+                                  "val = t + 1 < S ? load(v, at + (size_t)D, dt) : 0.0;"),
+    "cca_rope_misses_keys": ("oracle_rope(k_out, tmp, OR_F64, B, Hkv, S, D, pos_offset, theta);",
+                             "memcpy(k_out, tmp, sizeof(double) * (size_t)B * Hkv * S * D);"),
 }
 
 

@@ -733,3 +733,182 @@ def test_rope_transpose_turns_pair_zero_back_by_the_position():
     p = np.arange(S)
     assert np.allclose(out[0, 0, :, 0], np.cos(p), rtol=0, atol=1e-15)
     assert np.allclose(out[0, 0, :, 1], -np.sin(p), rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# CCA pre-attention operations ("Compressed Convolutional Attention",
+# "Methodologie" items 2-4; the readings are stated in oracle.c)
+# ---------------------------------------------------------------------------
+def _cca_inputs(B, Hq, Hkv, S, D, W, seed):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal((B, Hq, S, D)), g.standard_normal((B, Hkv, S, D)),
+            g.standard_normal((B, Hkv, S, D)), g.standard_normal((Hq, D, W)),
+            g.standard_normal((Hkv, D, W)), g.standard_normal((Hq, D, D)),
+            g.standard_normal((Hkv, D, D)))
+
+
+def _cca_brute(q, k, v, cq, ck, mq, mk, theta=0.0):
+    """The three operations written out in pure Python loops (no numpy in the
+    arithmetic), RoPE with math.cos / math.sin on adjacent pairs."""
+    B, Hq, S, D = q.shape
+    Hkv, W = k.shape[1], cq.shape[-1]
+    G = Hq // Hkv
+    ql, kl, vl = q.tolist(), k.tolist(), v.tolist()
+    cql, ckl, mql, mkl = cq.tolist(), ck.tolist(), mq.tolist(), mk.tolist()
+
+    def head(x, cw, mw, mean, b, h, t):
+        s = [sum(cw[h][c][i] * x[b][h][t - i][c] for i in range(W) if t - i >= 0) for c in range(D)]
+        z = [sum(mw[h][c][c2] * s[c2] for c2 in range(D)) + mean[c] for c in range(D)]
+        if theta > 0:
+            for i in range(D // 2):
+                a = t * theta ** (-2.0 * i / D)
+                x0, x1 = z[2 * i], z[2 * i + 1]
+                z[2 * i], z[2 * i + 1] = x0 * math.cos(a) - x1 * math.sin(a), x0 * math.sin(a) + x1 * math.cos(a)
+        return z
+
+    qo = [[[None] * S for _ in range(Hq)] for _ in range(B)]
+    ko = [[[None] * S for _ in range(Hkv)] for _ in range(B)]
+    vo = [[[None] * S for _ in range(Hkv)] for _ in range(B)]
+    for b in range(B):
+        for t in range(S):
+            means = []
+            for j in range(Hkv):
+                qbar = [sum(ql[b][h][t][c] for h in range(j * G, (j + 1) * G)) / G for c in range(D)]
+                means.append([0.5 * (qbar[c] + kl[b][j][t][c]) for c in range(D)])
+            for h in range(Hq):
+                qo[b][h][t] = head(ql, cql, mql, means[h // G], b, h, t)
+            for j in range(Hkv):
+                ko[b][j][t] = head(kl, ckl, mkl, means[j], b, j, t)
+                vo[b][j][t] = [vl[b][j][t][c] if c < D // 2 else (vl[b][j][t - 1][c] if t > 0 else 0.0)
+                               for c in range(D)]
+    return np.array(qo), np.array(ko), np.array(vo)
+
+
+@pytest.mark.parametrize("geom,theta", [((1, 4, 2, 6, 4, 3), 0.0), ((2, 3, 1, 5, 6, 2), 0.0),
+                                        ((1, 2, 2, 7, 4, 4), 1e4), ((1, 4, 1, 4, 8, 1), 10.0)])
+def test_cca_mix_matches_brute_force(geom, theta):
+    B, Hq, Hkv, S, D, W = geom
+    args = _cca_inputs(B, Hq, Hkv, S, D, W, 60 + S)
+    got = oracle.cca_mix(*args, theta=theta)
+    ref = _cca_brute(*args, theta=theta)
+    for g_, r_ in zip(got, ref):
+        assert np.max(np.abs(g_ - r_)) < 1e-12
+
+
+def test_cca_sequence_convolution_is_a_causal_depthwise_conv1d():
+    # with the identity as channel mix, q - mean is torch's depthwise conv1d of
+    # q~ (weights flipped: conv1d's last tap weighs the current token) over the
+    # sequence padded on the left, cut to the first S outputs
+    B, Hq, Hkv, S, D, W = 2, 4, 4, 11, 8, 4
+    q, k, v, cq, ck, _, _ = _cca_inputs(B, Hq, Hkv, S, D, W, 61)
+    eye_q, eye_k = np.broadcast_to(np.eye(D), (Hq, D, D)).copy(), np.broadcast_to(np.eye(D), (Hkv, D, D)).copy()
+    qo, ko, _ = oracle.cca_mix(q, k, v, cq, ck, eye_q, eye_k)
+    mean = 0.5 * (q + k)  # G = 1: each query head's own key head
+
+    def conv(x, w):  # x [B,H,S,D], w [H,D,W] -> [B,H,S,D]
+        H = x.shape[1]
+        xt = torch.from_numpy(x).permute(0, 1, 3, 2).reshape(B, H * D, S)
+        wt = torch.from_numpy(w).reshape(H * D, 1, W).flip(-1)
+        y = F.conv1d(xt, wt, groups=H * D, padding=W - 1)[..., :S]
+        return y.reshape(B, H, D, S).permute(0, 1, 3, 2).numpy()
+
+    assert np.max(np.abs((qo - mean) - conv(q, cq))) < 1e-12
+    assert np.max(np.abs((ko - mean) - conv(k, ck))) < 1e-12
+
+
+def test_cca_channel_mix_is_a_matrix_per_head_applied_to_each_token():
+    # a single tap of weight 1 makes the sequence convolution the identity;
+    # then q - mean = mix_q[h] @ q~[t] for every token (row c = output channel)
+    B, Hq, Hkv, S, D = 1, 6, 2, 5, 8
+    q, k, v, _, _, mq, mk = _cca_inputs(B, Hq, Hkv, S, D, 1, 62)
+    ones_q, ones_k = np.ones((Hq, D, 1)), np.ones((Hkv, D, 1))
+    qo, ko, _ = oracle.cca_mix(q, k, v, ones_q, ones_k, mq, mk)
+    G = Hq // Hkv
+    mean_k = 0.5 * (q.reshape(B, Hkv, G, S, D).mean(axis=2) + k)
+    mean_q = np.repeat(mean_k, G, axis=1)
+    ref_q = torch.matmul(torch.from_numpy(q), torch.from_numpy(mq).transpose(-1, -2).unsqueeze(0)).numpy()
+    ref_k = torch.matmul(torch.from_numpy(k), torch.from_numpy(mk).transpose(-1, -2).unsqueeze(0)).numpy()
+    assert np.max(np.abs(qo - mean_q - ref_q)) < 1e-12
+    assert np.max(np.abs(ko - mean_k - ref_k)) < 1e-12
+
+
+def test_cca_qk_mean_alone_when_the_mix_is_zero():
+    # zero channel mix leaves the mean only: with G = 1 q and k become the same
+    # vector (q~ + k~) / 2; with G > 1 every head of a group gets its group's
+    # mean of the averaged query heads and the key head
+    for (Hq, Hkv) in ((4, 4), (6, 2)):
+        B, S, D, W = 2, 5, 6, 3
+        q, k, v, cq, ck, _, _ = _cca_inputs(B, Hq, Hkv, S, D, W, 63)
+        qo, ko, _ = oracle.cca_mix(q, k, v, cq, ck, np.zeros((Hq, D, D)), np.zeros((Hkv, D, D)))
+        G = Hq // Hkv
+        if G == 1:
+            assert np.array_equal(qo, ko)
+            assert np.max(np.abs(qo - (q + k) / 2)) < 1e-15
+        for h in range(Hq):
+            assert np.array_equal(qo[:, h], ko[:, h // G])
+        grp = q.reshape(B, Hkv, G, S, D).mean(axis=2)
+        assert np.max(np.abs(ko - (grp + k) / 2)) < 1e-15
+
+
+def test_cca_group_of_identical_heads_reduces_to_one_head():
+    # query heads that are copies of one another (inputs and weights) give the
+    # result of one query head per group
+    B, Hkv, S, D, W, G = 1, 2, 6, 4, 3, 3
+    q1, k, v, cq1, ck, mq1, mk = _cca_inputs(B, Hkv, Hkv, S, D, W, 64)
+    rep = lambda a, ax: np.repeat(a, G, axis=ax)
+    qo, ko, vo = oracle.cca_mix(rep(q1, 1), k, v, rep(cq1, 0), ck, rep(mq1, 0), mk)
+    qo1, ko1, vo1 = oracle.cca_mix(q1, k, v, cq1, ck, mq1, mk)
+    assert np.max(np.abs(qo - rep(qo1, 1))) < 1e-12
+    assert np.max(np.abs(ko - ko1)) < 1e-12 and np.array_equal(vo, vo1)
+
+
+def test_cca_is_causal_and_local_in_time():
+    # a change at token t0 reaches q and k only at t0 .. t0 + W - 1 and v only
+    # at t0 (first half) and t0 + 1 (second half)
+    B, Hq, Hkv, S, D, W = 1, 4, 2, 12, 4, 3
+    args = list(_cca_inputs(B, Hq, Hkv, S, D, W, 65))
+    base = oracle.cca_mix(*args)
+    t0 = 5
+    for which in range(3):
+        pert = [a.copy() for a in args]
+        pert[which][:, :, t0] += 1.0
+        out = oracle.cca_mix(*pert)
+        for o_new, o_old, name in zip(out, base, "qkv"):
+            changed = np.any(o_new != o_old, axis=(0, 1, 3))
+            hit = np.nonzero(changed)[0]
+            if name == "v":
+                assert set(hit) <= ({t0, t0 + 1} if which == 2 else set())
+            else:
+                assert set(hit) <= set(range(t0, t0 + W))
+                if which < 2:
+                    assert t0 in hit
+
+
+def test_cca_value_shift_takes_the_second_half_from_the_previous_token():
+    B, Hq, Hkv, S, D, W = 2, 4, 2, 7, 8, 2
+    q, k, v, cq, ck, mq, mk = _cca_inputs(B, Hq, Hkv, S, D, W, 66)
+    _, _, vo = oracle.cca_mix(q, k, v, cq, ck, mq, mk)
+    assert np.array_equal(vo[..., :D // 2], v[..., :D // 2])
+    assert np.array_equal(vo[:, :, 1:, D // 2:], v[:, :, :-1, D // 2:])
+    assert not vo[:, :, 0, D // 2:].any()
+
+
+def test_cca_rope_is_the_rotation_of_the_mixed_vectors():
+    B, Hq, Hkv, S, D, W = 2, 4, 2, 9, 8, 3
+    args = _cca_inputs(B, Hq, Hkv, S, D, W, 67)
+    off = np.array([3, 1000], dtype=np.int32)
+    qo, ko, vo = oracle.cca_mix(*args, pos_offset=off, theta=1e4)
+    q0, k0, v0 = oracle.cca_mix(*args)
+    assert np.max(np.abs(qo - oracle.rope(q0, 1e4, off))) < 1e-12
+    assert np.max(np.abs(ko - oracle.rope(k0, 1e4, off))) < 1e-12
+    assert np.array_equal(vo, v0)
+
+
+def test_cca_mix_widens_bf16_inputs_exactly():
+    B, Hq, Hkv, S, D, W = 1, 4, 2, 6, 8, 2
+    args = _cca_inputs(B, Hq, Hkv, S, D, W, 68)
+    bits = [oracle.round_bf16(a) for a in args]
+    got = oracle.cca_mix(*bits, theta=500.0)
+    ref = oracle.cca_mix(*(oracle.widen(b) for b in bits), theta=500.0)
+    for g_, r_ in zip(got, ref):
+        assert np.array_equal(g_, r_)
