@@ -15,6 +15,8 @@ fallback: calling into the library without the built ``libattn.so`` raises.
            workspace=None)
     decode_noalloc(q, k_cache, v_cache, seqlens, out, max_len=None, scale=None, rope_theta=0.0)
     decode_workspace_size(B, Hq, Hkv, max_len, D)
+    cca_mix(q, k, v, conv_q, conv_k, mix_q, mix_k, rope_theta=0.0, pos_offset=None,
+            q_out=None, k_out=None, v_out=None)
 
 Shapes follow the C ABI: x [B,H,S,D]; q/o [B,Hq,S,D], k/v [B,Hkv,S,D];
 decode q/o [B,Hq,D], caches [B,Hkv,S_cap,D], seqlens int32 [B] on the device.
@@ -29,7 +31,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = ["rope", "rope_backward", "prefill", "prefill_lse", "prefill_backward", "prefill_backward_workspace_size",
            "decode", "decode_noalloc", "decode_paged", "decode_workspace_size", "AttnError",
-           "lib_path", "DECODE_SCRATCH_BYTES"]
+           "lib_path", "DECODE_SCRATCH_BYTES", "cca_mix"]
 
 
 def _torch():
@@ -307,3 +309,39 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, max_len: int | None 
           float(scale), float(rope_theta), workspace.data_ptr(),
           workspace.numel() * workspace.element_size(), _stream(q))
     return out
+
+
+def cca_mix(q, k, v, conv_q, conv_k, mix_q, mix_k, rope_theta: float = 0.0, pos_offset=None,
+            q_out=None, k_out=None, v_out=None):
+    """CCA pre-attention operations on the compressed q [B,Hq,S,D], k, v
+    [B,Hkv,S,D] (bf16): causal depthwise sequence convolution (conv_q [Hq,D,W],
+    conv_k [Hkv,D,W]; tap i weighs the token i steps back), channel mix per
+    head (mix_q [Hq,D,D], mix_k [Hkv,D,D]; row c = output channel c), plus the
+    group's pre-convolution query/key mean; RoPE at position pos_offset[b] + t
+    when rope_theta > 0; value shift (last D/2 channels from the previous
+    token).  Returns (q_out, k_out, v_out), ready for prefill(..., rope_theta=0)."""
+    torch = _torch()
+    B, Hq, Hkv, S, D = _check_prefill_shapes(q, k, v)
+    W = conv_q.shape[-1] if conv_q.dim() == 3 else -1
+    if (conv_q.shape != (Hq, D, W) or conv_k.shape != (Hkv, D, W) or mix_q.shape != (Hq, D, D)
+            or mix_k.shape != (Hkv, D, D)):
+        raise ValueError("conv_q [Hq,D,W], conv_k [Hkv,D,W], mix_q [Hq,D,D], mix_k [Hkv,D,D]")
+    if any(t.dtype != q.dtype for t in (conv_q, conv_k, mix_q, mix_k)):
+        raise ValueError("weights must share the activations' dtype")
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    v_out = torch.empty_like(v) if v_out is None else v_out
+    if q_out.shape != q.shape or k_out.shape != k.shape or v_out.shape != v.shape:
+        raise ValueError("outputs must match q, k, v")
+    po = 0
+    if pos_offset is not None:
+        if pos_offset.dtype != torch.int32 or pos_offset.shape != (B,):
+            raise ValueError("pos_offset must be int32 [B]")
+        _check_dev(pos_offset)
+        po = pos_offset.data_ptr()
+    _check_dev(q, k, v, conv_q, conv_k, mix_q, mix_k, q_out, k_out, v_out)
+    _call(lib().attn_cca_mix, q_out.data_ptr(), k_out.data_ptr(), v_out.data_ptr(), q.data_ptr(),
+          k.data_ptr(), v.data_ptr(), _dtype_code(q), B, Hq, Hkv, S, D, conv_q.data_ptr(),
+          conv_k.data_ptr(), W, mix_q.data_ptr(), mix_k.data_ptr(), po, float(rope_theta),
+          _stream(q))
+    return q_out, k_out, v_out

@@ -64,4 +64,14 @@ hipError_t launch_decode_paged(void* o, const void* q, const void* k_pages, cons
                                int max_len, int window, float scale, double rope_theta,
                                void* workspace, hipStream_t st);
 
+// CCA pre-attention operations (bf16): causal depthwise sequence convolution
+// of width W (conv_q [Hq, D, W], conv_k [Hkv, D, W]), channel mix per head
+// (mix_q [Hq, D, D], mix_k [Hkv, D, D]), the group's pre-convolution
+// query/key mean, RoPE when rope_theta > 0, and the value shift.
+int cca_max_width();
+hipError_t launch_cca_mix(void* q_out, void* k_out, void* v_out, const void* q, const void* k,
+                          const void* v, int B, int Hq, int Hkv, int S, int D, const void* conv_q,
+                          const void* conv_k, int W, const void* mix_q, const void* mix_k,
+                          const int32_t* pos_offset, double rope_theta, hipStream_t st);
+
 }  // namespace attn

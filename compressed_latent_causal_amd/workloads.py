@@ -115,6 +115,34 @@ def make_decode(w: Workload, seed: int = 0, poison_tail: bool = False):
     return q, k, v, lens
 
 
+# Width of the causal sequence convolution of the CCA pre-attention operations
+# (the summary gives none; 4 is a common short-convolution width).
+CCA_CONV_WIDTH = 4
+
+
+def make_cca(w: Workload, seed: int = 0, width: int = CCA_CONV_WIDTH):
+    """Inputs of the CCA pre-attention operations (CPU, dtype of the workload):
+    the compressed q~ [B,Hq,S,D], k~, v~ [B,Hkv,S,D] drawn as make_prefill
+    draws q, k, v, then from the same generator the sequence-convolution taps
+    conv_q [Hq,D,width], conv_k [Hkv,D,width] ~ N(0, 1/width) and the
+    channel-mixing matrices mix_q [Hq,D,D], mix_k [Hkv,D,D] ~ N(0, 1/D), so
+    the mixed vectors keep about unit scale."""
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (w.B, w.Hq, w.S, w.D), w.torch_dtype)
+    k = _randn(g, (w.B, w.Hkv, w.S, w.D), w.torch_dtype)
+    v = _randn(g, (w.B, w.Hkv, w.S, w.D), w.torch_dtype)
+
+    def scaled(shape, s):
+        x = torch.randn(*shape, generator=g, dtype=torch.float32) * s
+        return x if w.torch_dtype == torch.float32 else x.to(w.torch_dtype)
+
+    conv_q = scaled((w.Hq, w.D, width), width ** -0.5)
+    conv_k = scaled((w.Hkv, w.D, width), width ** -0.5)
+    mix_q = scaled((w.Hq, w.D, w.D), w.D ** -0.5)
+    mix_k = scaled((w.Hkv, w.D, w.D), w.D ** -0.5)
+    return q, k, v, conv_q, conv_k, mix_q, mix_k
+
+
 def poison_cache_tail(cache: torch.Tensor, lens: torch.Tensor) -> None:
     """Write NaN into cache[b, :, t, :] for every t >= lens[b] (in place)."""
     for b in range(cache.shape[0]):

@@ -265,6 +265,39 @@ int attn_decode_paged(void *o, const void *q, const void *k_pages, const void *v
                       int max_len, int window, float scale, double rope_theta,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * CCA pre-attention operations on the compressed q~, k~, v~ ("Compressed
+ * Convolutional Attention" summary, "Methodologie", items 2 to 4; the summary
+ * names the operations but not their sizes or exact form, so each is taken in
+ * its plainest form):
+ *   sequence mixing, a causal depthwise convolution of width W per channel:
+ *     s[t,c] = sum_{i<W, t-i>=0} conv[h,c,i] x~[t-i,c]   (tap i: i tokens back)
+ *   channel mixing within a head, a dense D x D map (row c = output channel c):
+ *     z[t,c] = sum_c' mix[h,c,c'] s[t,c']
+ *   QK-mean, the mean of the token's pre-convolution query (the group's query
+ *   heads averaged) and key, added to every convolved q head of the KV group
+ *   and to its k head:
+ *     m[t,j] = ((1/G) sum_{h in group j} q~[t,h] + k~[t,j]) / 2
+ *     q[t,h] = z_q[t,h] + m[t,h/G],   k[t,j] = z_k[t,j] + m[t,j]
+ *   RoPE (item 4) of q and k at absolute position pos_offset[b] + t when
+ *   rope_theta > 0 (the rotation of attn_rope; rope_theta == 0: none);
+ *   value shift (item 3): v[t,c] = v~[t,c] for c < D/2, v~[t-1,c] for
+ *   c >= D/2 (zero at t = 0).
+ * q~, q_out: [B, Hq, S, D];  k~, v~, k_out, v_out: [B, Hkv, S, D];  conv_q
+ * [Hq, D, W], conv_k [Hkv, D, W], mix_q [Hq, D, D], mix_k [Hkv, D, D]; all
+ * bf16 (dtype BF16 only), W = conv_width in 1..8, pos_offset device int32[B]
+ * or NULL.  The outputs feed attn_prefill (rope_theta 0 there: q and k are
+ * already rotated) and, as a cache, attn_decode.  The convolution and the
+ * channel mix are evaluated in fp32 (the mix on the matrix cores, with the
+ * convolution's output split into two bf16 parts) and each output is rounded
+ * once to bf16.  Outputs must not overlap inputs.  conv weights need 2-byte
+ * alignment, the other tensors 16 bytes.  One kernel is enqueued.
+ */
+int attn_cca_mix(void *q_out, void *k_out, void *v_out, const void *q, const void *k,
+                 const void *v, int dtype, int B, int Hq, int Hkv, int S, int D,
+                 const void *conv_q, const void *conv_k, int conv_width, const void *mix_q,
+                 const void *mix_k, const int32_t *pos_offset, double rope_theta, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *attn_status_string(int status);
 

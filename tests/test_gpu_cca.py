@@ -1,0 +1,166 @@
+"""GPU parity of the CCA pre-attention operations (attn_cca_mix), through the C
+ABI, against the fp64 CPU oracle on the same seeded inputs (marker `gpu`).
+
+The value shift only moves bf16 values, so v must match bit for bit.  q and k
+are the fp32-accurate value of the convolution, channel mix, mean and RoPE,
+rounded once to bf16: each output must equal the oracle's exact value rounded
+to nearest even, except where that value lies within the evaluation error
+bound of a rounding midpoint.  The bound is derived from the arithmetic (fp32
+convolution, the product with the convolution split into two bf16 parts, fp32
+accumulation, fp32 rotation): 2^-15 of the sum of the absolute terms of the
+output pair, which the oracle itself provides when fed absolute values.
+Attention on the mixed tensors is checked end to end against the oracle's
+pipeline at the benchmark spec's tolerances.
+"""
+import numpy as np
+import pytest
+import torch
+
+import compressed_latent_causal_amd as attn
+import oracle
+from compressed_latent_causal_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN = 2e-2, 2e-3
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    attn.lib()
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def bits(t):
+    return wl.to_numpy_bits(t)
+
+
+def _midpoint_distance(y):
+    a = np.abs(y)
+    _, e = np.frexp(a)
+    ulp = np.ldexp(1.0, e - 8)
+    frac = a / ulp - np.floor(a / ulp)
+    return np.abs(frac - 0.5) * ulp
+
+
+def _pair_bound(absval):
+    """2^-15 of the absolute terms of each output's channel pair (RoPE mixes
+    the two channels of a pair)."""
+    pair = absval[..., 0::2] + absval[..., 1::2]
+    return np.repeat(pair, 2, axis=-1) * 2.0 ** -15
+
+
+def assert_rounded(got_bits, ref, bound, what, max_frac=0.01):
+    want = oracle.round_bf16(ref)
+    mism = got_bits != want
+    n = int(mism.sum())
+    say(f"{what}: {n} of {got_bits.size} elements round the other way near a midpoint")
+    if n:
+        near = _midpoint_distance(ref[mism]) <= bound[mism]
+        assert near.all(), f"{what}: {int((~near).sum())} elements differ from RNE(oracle) away from a midpoint"
+        got = oracle.widen(got_bits[mism])
+        _, e = np.frexp(np.abs(got))
+        assert (np.abs(got - ref[mism]) <= bound[mism] + np.ldexp(1.0, e - 9)).all()
+    assert n <= max(2, int(got_bits.size * max_frac)), f"{what}: {n} mismatches"
+
+
+def _check_mix(w, width, theta, seed, pos=None):
+    q, k, v, cq, ck, mq, mk = wl.make_cca(w, seed=seed, width=width)
+    say(f"cca_mix B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.S} D={w.D} W={width} theta={theta} pos={pos}")
+    pd = None if pos is None else torch.tensor(pos, dtype=torch.int32, device=DEV)
+    qo, ko, vo = attn.cca_mix(*(t.to(DEV) for t in (q, k, v, cq, ck, mq, mk)), rope_theta=theta,
+                              pos_offset=pd)
+    torch.cuda.synchronize()
+    ins = [bits(t) for t in (q, k, v, cq, ck, mq, mk)]
+    rq, rk, rv = oracle.cca_mix(*ins, pos_offset=pos, theta=theta)
+    aq, ak, _ = oracle.cca_mix(*(np.abs(oracle.widen(x)) for x in ins))
+    assert np.array_equal(bits(vo), oracle.round_bf16(rv)), "value shift must be exact"
+    assert_rounded(bits(qo), rq, _pair_bound(aq), "q")
+    assert_rounded(bits(ko), rk, _pair_bound(ak), "k")
+    return (q, k, v, cq, ck, mq, mk), (qo, ko, vo)
+
+
+MIX_CASES = [  # B, Hq, Hkv, S, D, width, theta, pos_offset
+    (1, 8, 2, 200, 64, 4, 1e4, None),
+    (2, 8, 2, 130, 128, 4, 5e5, [0, 777]),
+    (1, 4, 4, 64, 128, 1, 0.0, None),      # MHA, single tap
+    (1, 4, 4, 65, 64, 8, 1e4, None),       # widest convolution, one token past a block
+    (1, 16, 1, 97, 64, 3, 1e4, [5]),       # MQA, G = 16
+    (2, 6, 2, 17, 128, 2, 0.0, None),      # G = 3, shorter than one workgroup
+    (1, 8, 2, 1, 64, 4, 1e4, None),        # one token
+    (1, 2, 1, 15, 128, 7, 5e5, [131000]),  # shorter than one wave, large positions
+]
+
+
+@pytest.mark.parametrize("case", MIX_CASES)
+def test_cca_mix_matches_oracle(case):
+    B, Hq, Hkv, S, D, width, theta, pos = case
+    _check_mix(wl.custom("prefill", "bf16", B, Hq, Hkv, D, S), width, theta, 100 + S, pos)
+
+
+@pytest.mark.parametrize("name", ["ccgqa_prefill", "llama8b_prefill"])
+def test_cca_mix_full_size(name):
+    """The two prefill workloads' shapes in the bench's launch configuration,
+    every output checked."""
+    w = wl.WORKLOADS[name]
+    _check_mix(w, wl.CCA_CONV_WIDTH, w.theta, 0)
+
+
+@pytest.mark.parametrize("case", [(1, 8, 2, 300, 64), (2, 8, 2, 130, 128), (1, 4, 1, 97, 64)])
+def test_ccgqa_attention_end_to_end(case):
+    """CCA mixing, then causal GQA prefill on its outputs (RoPE already
+    applied), against the oracle's pipeline: its mix rounded to bf16, then its
+    attention."""
+    B, Hq, Hkv, S, D = case
+    w = wl.custom("prefill", "bf16", B, Hq, Hkv, D, S, theta=1e4)
+    q, k, v, cq, ck, mq, mk = wl.make_cca(w, seed=7)
+    say(f"ccgqa end to end {case}")
+    qo, ko, vo = attn.cca_mix(*(t.to(DEV) for t in (q, k, v, cq, ck, mq, mk)), rope_theta=w.theta)
+    o = attn.prefill(qo, ko, vo, scale=w.scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.cca_mix(*(bits(t) for t in (q, k, v, cq, ck, mq, mk)), theta=w.theta)
+    ref = oracle.prefill(*(oracle.round_bf16(x) for x in (rq, rk, rv)), scale=w.scale)
+    diff = np.abs(o.cpu().double().numpy() - ref)
+    say(f"ccgqa end to end: max {diff.max():.3e} mean {diff.mean():.3e}")
+    assert np.isfinite(diff).all()
+    assert diff.max() <= BF16_MAX and diff.mean() <= BF16_MEAN
+
+
+def test_ccgqa_attention_full_size_sampled_rows():
+    """The compressed-latent workload (2 x 8/2 heads x 16384 x 64) through the
+    mix and the prefill, output rows sampled (edges of blocks and sequence
+    included) against the oracle's pipeline."""
+    w = wl.WORKLOADS["ccgqa_prefill"]
+    q, k, v, cq, ck, mq, mk = wl.make_cca(w, seed=0)
+    say("ccgqa full size end to end, sampled rows")
+    qo, ko, vo = attn.cca_mix(*(t.to(DEV) for t in (q, k, v, cq, ck, mq, mk)), rope_theta=w.theta)
+    o = attn.prefill(qo, ko, vo, scale=w.scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.cca_mix(*(bits(t) for t in (q, k, v, cq, ck, mq, mk)), theta=w.theta)
+    rng = np.random.default_rng(3)
+    S = w.S
+    pos = np.unique(np.concatenate([[0, 1, 63, 64, 65, S // 2, S - 2, S - 1],
+                                    rng.integers(0, S, 24)]))
+    rows = np.array([(b * w.Hq + h) * S + i for b in range(w.B) for h in (0, 3, 5, 7) for i in pos])
+    ref = oracle.prefill(*(oracle.round_bf16(x) for x in (rq, rk, rv)), scale=w.scale, rows=rows)
+    got = o.reshape(-1, w.D)[torch.from_numpy(rows).to(DEV)].cpu().double().numpy()
+    diff = np.abs(got - ref)
+    say(f"ccgqa full size: max {diff.max():.3e} mean {diff.mean():.3e}")
+    assert diff.max() <= BF16_MAX and diff.mean() <= BF16_MEAN
+
+
+def test_cca_mix_errors():
+    w = wl.custom("prefill", "bf16", 1, 4, 2, 64, 32)
+    q, k, v, cq, ck, mq, mk = (t.to(DEV) for t in wl.make_cca(w, seed=1))
+    with pytest.raises(attn.AttnError) as e:
+        attn.cca_mix(q.float(), k.float(), v.float(), cq.float(), ck.float(), mq.float(), mk.float())
+    assert e.value.status == 3
+    wide = torch.zeros(4, 64, 9, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(attn.AttnError) as e:
+        attn.cca_mix(q, k, v, wide, torch.zeros(2, 64, 9, dtype=torch.bfloat16, device=DEV), mq, mk)
+    assert e.value.status == 3
