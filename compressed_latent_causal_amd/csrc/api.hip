@@ -208,13 +208,15 @@ ATTN_API int attn_cca_mix(void* q_out, void* k_out, void* v_out, const void* q, 
     if (conv_width < 1 || conv_width > attn::cca_max_width()) return ATTN_ERR_UNSUPPORTED;
     if (!(rope_theta >= 0.0) || !isfinite(rope_theta)) return ATTN_ERR_UNSUPPORTED;
     if (B == 0 || S == 0) return ATTN_OK;
-    // one workgroup per (64-token block, sequence, KV head)
+    // one workgroup per (64-token block, sequence, KV head); a head's rows
+    // (plus a block past the end) are addressed with 32-bit byte offsets
     if ((long long)((S + 63) / 64) * B * Hkv >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    if ((long long)(S + 64) * D * 2 >= (1ll << 31)) return ATTN_ERR_SHAPE;
     if (!q_out || !k_out || !v_out || !q || !k || !v || !conv_q || !conv_k || !mix_q || !mix_k)
         return ATTN_ERR_NULL;
     if (!aligned16(q_out) || !aligned16(k_out) || !aligned16(v_out) || !aligned16(q) ||
         !aligned16(k) || !aligned16(v) || !aligned16(mix_q) || !aligned16(mix_k) ||
-        ((uintptr_t)conv_q & 1u) || ((uintptr_t)conv_k & 1u) || ((uintptr_t)pos_offset & 3u))
+        !aligned16(conv_q) || !aligned16(conv_k) || ((uintptr_t)pos_offset & 3u))
         return ATTN_ERR_ALIGN;
     return hip_status(attn::launch_cca_mix(q_out, k_out, v_out, q, k, v, B, Hq, Hkv, S, D, conv_q,
                                            conv_k, conv_width, mix_q, mix_k, pos_offset,

@@ -46,6 +46,9 @@ constexpr int CM_TW = 16;              // tokens per wave
 constexpr int CM_TB = CM_NW * CM_TW;   // tokens per workgroup
 constexpr int CM_MAXW = 8;             // widest sequence convolution
 
+// s_waitcnt immediate: vmcnt(n) and lgkmcnt(0)
+constexpr int wait_vmcnt_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
+
 // x of the lane SH places lower in the same 16-lane row; lanes with none keep `low`
 template <int SH>
 __device__ inline unsigned row_shift_in(unsigned x, unsigned low) {
@@ -57,12 +60,15 @@ __device__ inline unsigned row_rotate(unsigned x) {
     return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x120 + SH, 0xF, 0xF, false);
 }
 
-template <int D>
-struct CcaHeadIn {
-    u32x4_t cur[D / 32];  // row t (this lane's token), channels 32s + 8g .. +7
-    u32x4_t prv[D / 32];  // row t - 16, same channels (rows before the wave's first token)
-    unsigned wc[CM_MAXW / 2];  // conv taps 0..W-1 of channel tid (threads tid < D), bf16 pairs
+
+// Input rows of one head as one vector value (dword 4 s + e of k-step s), so
+// they stay in registers across the head loop.
+template <int N>
+struct DwordVec {
+    typedef unsigned type __attribute__((ext_vector_type(N)));
 };
+template <int D>
+using RowsVec = typename DwordVec<D / 8>::type;
 
 // Tap I of the sequence convolution for this lane's token t and channels
 // 32 s + 8 g + e: y += w[I][c] x[t - I, c].  Row t - I sits in lane r - I of
@@ -70,7 +76,8 @@ struct CcaHeadIn {
 // rows.
 template <int D, int I>
 __device__ __attribute__((always_inline)) inline void conv_tap(float (&y)[D / 32][8],
-                                                               const CcaHeadIn<D>& in,
+                                                               const RowsVec<D>& cur,
+                                                               const RowsVec<D>& prv,
                                                                const float* wsm, int g) {
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
@@ -78,9 +85,9 @@ __device__ __attribute__((always_inline)) inline void conv_tap(float (&y)[D / 32
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             if constexpr (I == 0)
-                x[e] = in.cur[s][e];
+                x[e] = cur[4 * s + e];
             else
-                x[e] = row_shift_in<I>(in.cur[s][e], row_rotate<I>(in.prv[s][e]));
+                x[e] = row_shift_in<I>(cur[4 * s + e], row_rotate<I>(prv[4 * s + e]));
         }
         const f32x4_t w0 = *(const f32x4_t*)(wsm + I * D + 32 * s + 8 * g);
         const f32x4_t w1 = *(const f32x4_t*)(wsm + I * D + 32 * s + 8 * g + 4);
@@ -123,7 +130,6 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
     const int NH = G + 1;  // the group's query heads, then its key head
     const int t0w = tblk * CM_TB + w * CM_TW;  // the wave's first token
     const int t = t0w + r;                     // this lane's token
-    const bool tok = t < S;
 
     auto head_rows = [&](int n) -> const uint16_t* {
         return n < G ? q + ((size_t)b * Hq + (size_t)j * G + n) * S * D
@@ -140,11 +146,21 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
         return n < G ? conv_q + ((size_t)j * G + n) * D * W : conv_k + (size_t)j * D * W;
     };
 
+    // This head's input rows and taps, replaced by the next head's once consumed:
+    // row t (this lane's token) and row t - 16 (rows before the wave's first
+    // token), channels 32 s + 8 g .. +7, and 16 bytes of the head's conv taps
+    // [D][W] (threads tid < D W / 8).
+    RowsVec<D> in_cur, in_prv;
+    u32x4_t in_wc;
+    auto put = [&](RowsVec<D>& dst, int s, u32x4_t x) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * s + e] = x[e];
+    };
     // Loads of head n: this wave's share of the mix matrix straight into LDS
     // (swz_k layout: instruction u puts lane l's 16 bytes at physical chunk
     // 64 (w MINST + u) + l, i.e. row pr, chunk pc, which holds logical chunk
     // pc ^ f(pr)), the conv taps of channel tid, and the lane's input rows.
-    auto issue = [&](int n, char* msm, CcaHeadIn<D>& in) __attribute__((always_inline)) {
+    auto issue_matrix = [&](int n, char* msm) __attribute__((always_inline)) {
         const uint16_t* const mx = head_mix(n);
 #pragma unroll
         for (int u = 0; u < MINST; ++u) {
@@ -155,24 +171,42 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
                                              (__attribute__((address_space(3))) void*)(msm + (w * MINST + u) * 1024),
                                              16, 0, 0);
         }
-        if (tid < D) {
-            const uint16_t* const cw = head_conv(n) + (size_t)tid * W;
-#pragma unroll
-            for (int i = 0; i < CM_MAXW / 2; ++i) {
-                const unsigned lo = 2 * i < W ? cw[2 * i] : 0u;
-                const unsigned hi = 2 * i + 1 < W ? cw[2 * i + 1] : 0u;
-                in.wc[i] = lo | (hi << 16);
-            }
-        }
-        const uint16_t* const xr = head_rows(n);
+    };
+    auto issue_rows = [&](int n) __attribute__((always_inline)) {
+        // Every load below is issued by every lane (buffer loads: an offset
+        // past the resource reads zeros), so the number of loads in flight is
+        // fixed and the waits can count them.  The taps come as raw bf16, 16
+        // bytes per thread (threads past D W / 8 read zeros), and are unpacked
+        // once they have landed.
+        const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(head_conv(n), D * W * 2);
+        in_wc = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, 16 * tid, 0, 0));
+        const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(head_rows(n), S * ROW);
+        // rows before the wave's first token: only the last W - 1 lanes of a
+        // row supply them, and none before the sequence's first token
+        const bool use_prv = t0w > 0 && r >= CM_TW - (W - 1);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            in.cur[s] = tok ? *(const u32x4_t*)(xr + (size_t)t * D + 32 * s + 8 * g) : u32x4_t{0, 0, 0, 0};
-            // only the last W - 1 lanes of a row supply earlier rows (rows that
-            // exist: a wave past the end of a short sequence reads none)
-            in.prv[s] = (t0w > 0 && r >= CM_TW - (W - 1) && t - CM_TW < S)
-                            ? *(const u32x4_t*)(xr + (size_t)(t - CM_TW) * D + 32 * s + 8 * g)
-                            : u32x4_t{0, 0, 0, 0};
+            const int cb = (32 * s + 8 * g) * 2;
+            put(in_cur, s, __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, t * ROW + cb, 0, 0)));
+            put(in_prv, s, __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, use_prv ? (t - CM_TW) * ROW + cb : -16, 0, 0)));
+        }
+    };
+
+    // Loads of the value shift, issued during the last head: the workgroup's
+    // 64 rows x D/8 chunks, KS per thread (zero for the row before the first)
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    static_assert(CM_TB * CPR == KS * CM_NW * 64, "value chunks per thread");
+    u32x4_t vsh[KS];
+    auto issue_vshift = [&]() __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(v + ((size_t)b * Hkv + j) * S * D, S * ROW);
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+            const int e = tid + u * CM_NW * 64;
+            const int tt = tblk * CM_TB + e / CPR, c = e % CPR;
+            const int src = c < CPR / 2 ? tt : tt - 1;  // row -1 lies outside: zeros
+            vsh[u] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, src >= 0 ? (src * D + 8 * c) * 2 : -16, 0, 0));
         }
     };
 
@@ -183,21 +217,31 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
         f32x4_t qs[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) qs[mt] = f32x4_t{0, 0, 0, 0};
-        if (tok) {
-            for (int h = 0; h < G; ++h) {
-                const uint16_t* const xr = head_rows(h) + (size_t)t * D + 4 * g;
+        // query heads four at a time, all loads of a batch issued before any
+        // is used (heads past G re-read the last one and weigh nothing)
+        const size_t trow = (size_t)min(t, S - 1) * D + 4 * g;
+        for (int h0 = 0; h0 < G; h0 += 4) {
+            u32x2_t x[4][MT];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const u32x2_t x = *(const u32x2_t*)(xr + 16 * mt);
-                    qs[mt] += f32x4_t{bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1])};
-                }
+            for (int u = 0; u < 4; ++u) {
+                const uint16_t* const xr = head_rows(min(h0 + u, G - 1)) + trow;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) x[u][mt] = *(const u32x2_t*)(xr + 16 * mt);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float f = h0 + u < G ? 1.f : 0.f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    qs[mt] += f * f32x4_t{bf16_lo(x[u][mt][0]), bf16_hi(x[u][mt][0]),
+                                          bf16_lo(x[u][mt][1]), bf16_hi(x[u][mt][1])};
             }
         }
         const float inv_g = 1.f / (float)G;
-        const uint16_t* const kr = head_rows(G) + (size_t)t * D + 4 * g;
+        const uint16_t* const kr = head_rows(G) + trow;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const u32x2_t x = tok ? *(const u32x2_t*)(kr + 16 * mt) : u32x2_t{0, 0};
+            const u32x2_t x = *(const u32x2_t*)(kr + 16 * mt);
             const f32x4_t kv = {bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1])};
             mean[mt] = 0.5f * (qs[mt] * inv_g + kv);
         }
@@ -205,27 +249,43 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
     float cs[MT][2], sn[MT][2];
     if (rope) {
         const long long p = (long long)(pos_offset ? pos_offset[b] : 0) + t;
+        double fq[MT][2];  // gathered first, so the loads overlap
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int e = 0; e < 2; ++e) rope_cos_sin(p, fr.f[8 * mt + 2 * g + e], cs[mt][e], sn[mt][e]);
+            for (int e = 0; e < 2; ++e) fq[mt][e] = fr.f[8 * mt + 2 * g + e];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) rope_cos_sin(p, fq[mt][e], cs[mt][e], sn[mt][e]);
     }
 
     // ---- one head: convolution, channel mix, mean, RoPE, store
-    auto body = [&](int n, const char* msm, float* wsm, const CcaHeadIn<D>& in, char* msm_next,
-                    float* wsm_next, CcaHeadIn<D>& in_next) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this head's loads landed
-        if (tid < D) {
+    auto body = [&](int n, const char* msm, float* wsm, char* msm_next) __attribute__((always_inline)) {
+        // This head's loads were issued before the previous head's MT result
+        // stores, the last vector-memory operations before this point (the
+        // stores are unconditional buffer stores, so their number is fixed);
+        // the first head waits for everything.
+        __builtin_amdgcn_sched_barrier(0);
+        if (n == 0)
+            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(MT));
+        __builtin_amdgcn_sched_barrier(0);
+        if (tid < D * W / 8) {
+            // taps element e of the thread's 8: channel (8 tid + e) / W, tap (8 tid + e) % W
 #pragma unroll
-            for (int i = 0; i < CM_MAXW / 2; ++i) {
-                wsm[(2 * i) * D + tid] = bf16_lo(in.wc[i]);
-                wsm[(2 * i + 1) * D + tid] = bf16_hi(in.wc[i]);
+            for (int e = 0; e < 8; ++e) {
+                const int idx = 8 * tid + e;
+                const unsigned wd = in_wc[e / 2];
+                wsm[(idx % W) * D + idx / W] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
             }
         }
         // every wave's share of the matrix and the taps are in LDS, and every
         // wave is done with head n - 1 (whose buffers the next loads reuse)
         __syncthreads();
-        if (n + 1 < NH) issue(n + 1, msm_next, in_next);
+        if (n + 1 < NH) issue_matrix(n + 1, msm_next);
+        __builtin_amdgcn_sched_barrier(0);  // the copy stays ahead of this head's work
 
         // S^T fragments: y[s][e] = channel 32 s + 8 g + e of token t
         float y[KS][8];
@@ -233,14 +293,14 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[s][e] = 0.f;
-        conv_tap<D, 0>(y, in, wsm, g);
-        if (W > 1) conv_tap<D, 1>(y, in, wsm, g);
-        if (W > 2) conv_tap<D, 2>(y, in, wsm, g);
-        if (W > 3) conv_tap<D, 3>(y, in, wsm, g);
-        if (W > 4) conv_tap<D, 4>(y, in, wsm, g);
-        if (W > 5) conv_tap<D, 5>(y, in, wsm, g);
-        if (W > 6) conv_tap<D, 6>(y, in, wsm, g);
-        if (W > 7) conv_tap<D, 7>(y, in, wsm, g);
+        conv_tap<D, 0>(y, in_cur, in_prv, wsm, g);
+        if (W > 1) conv_tap<D, 1>(y, in_cur, in_prv, wsm, g);
+        if (W > 2) conv_tap<D, 2>(y, in_cur, in_prv, wsm, g);
+        if (W > 3) conv_tap<D, 3>(y, in_cur, in_prv, wsm, g);
+        if (W > 4) conv_tap<D, 4>(y, in_cur, in_prv, wsm, g);
+        if (W > 5) conv_tap<D, 5>(y, in_cur, in_prv, wsm, g);
+        if (W > 6) conv_tap<D, 6>(y, in_cur, in_prv, wsm, g);
+        if (W > 7) conv_tap<D, 7>(y, in_cur, in_prv, wsm, g);
         // bf16 high and low parts of S^T
         bf16x8_t yh[KS], yl[KS];
 #pragma unroll
@@ -254,8 +314,19 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
             yh[s] = __builtin_bit_cast(bf16x8_t, h4);
             yl[s] = __builtin_bit_cast(bf16x8_t, l4);
         }
-        // Z^T = M S^T; lane gets channels 16 mt + 4 g + i of token t
-        uint16_t* const orow = head_out(n) + (size_t)t * D + 4 * g;
+        // the input registers are consumed: load the next head's rows (or,
+        // after the last head, the value shift's) while this head's products run
+        __builtin_amdgcn_sched_barrier(0);
+        if (n + 1 < NH)
+            issue_rows(n + 1);
+        else
+            issue_vshift();
+        __builtin_amdgcn_sched_barrier(0);
+        // Z^T = M S^T; lane gets channels 16 mt + 4 g + i of token t.  Stores
+        // go through a buffer resource over the head's rows, which drops those
+        // of tokens past the end, so every lane issues every store.
+        const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(head_out(n), S * ROW);
+        const int obyte = (t * D + 4 * g) * 2;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             f32x4_t acc = {0, 0, 0, 0};
@@ -272,35 +343,34 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
                 rope_rotate(acc[2], acc[3], cs[mt][1], sn[mt][1], y2, y3);
                 acc = f32x4_t{y0, y1, y2, y3};
             }
-            if (tok) *(u32x2_t*)(orow + 16 * mt) = u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])}, ors,
+                obyte + 32 * mt, 0, 0);
         }
     };
 
-    CcaHeadIn<D> inA, inB;
-    issue(0, msm0, inA);
+    issue_matrix(0, msm0);
+    issue_rows(0);
+    __builtin_amdgcn_sched_barrier(0);
     int n = 0;
-    // unrolled by two so each step names its buffers statically
+    // unrolled by two so each step names its LDS buffers statically
     for (; n + 1 < NH; n += 2) {
-        body(n, msm0, wsm0, inA, msm1, wsm1, inB);
-        body(n + 1, msm1, wsm1, inB, msm0, wsm0, inA);
+        body(n, msm0, wsm0, msm1);
+        body(n + 1, msm1, wsm1, msm0);
     }
-    if (n < NH) body(n, msm0, wsm0, inA, msm1, wsm1, inB);
+    if (n < NH) body(n, msm0, wsm0, msm1);
 
-    // ---- value shift of the block's rows: channels below D/2 from the token,
-    // the others from the token before it
-    const uint16_t* const vr = v + ((size_t)b * Hkv + j) * S * D;
-    uint16_t* const vw = vo + ((size_t)b * Hkv + j) * S * D;
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
-    for (int e = tid; e < CM_TB * CPR; e += CM_NW * 64) {
+    // ---- value shift of the block's rows: chunk c of row tt comes from row
+    // tt for channels below D/2 and from row tt - 1 above (stores past the
+    // end are dropped by the buffer resource)
+    const __amdgpu_buffer_rsrc_t vws = buffer_rsrc(vo + ((size_t)b * Hkv + j) * S * D, S * ROW);
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+        const int e = tid + u * CM_NW * 64;
         const int tt = tblk * CM_TB + e / CPR, c = e % CPR;
-        if (tt >= S) break;
-        u32x4_t x = {0, 0, 0, 0};
-        if (c < CPR / 2)
-            x = *(const u32x4_t*)(vr + (size_t)tt * D + 8 * c);
-        else if (tt > 0)
-            x = *(const u32x4_t*)(vr + (size_t)(tt - 1) * D + 8 * c);
-        *(u32x4_t*)(vw + (size_t)tt * D + 8 * c) = x;
+        __builtin_amdgcn_raw_buffer_store_b128(vsh[u], vws, (tt * D + 8 * c) * 2, 0, 0);
     }
+
 }
 
 template <int D>

@@ -290,8 +290,9 @@ int attn_decode_paged(void *o, const void *q, const void *k_pages, const void *v
  * already rotated) and, as a cache, attn_decode.  The convolution and the
  * channel mix are evaluated in fp32 (the mix on the matrix cores, with the
  * convolution's output split into two bf16 parts) and each output is rounded
- * once to bf16.  Outputs must not overlap inputs.  conv weights need 2-byte
- * alignment, the other tensors 16 bytes.  One kernel is enqueued.
+ * once to bf16.  Outputs must not overlap inputs.  Tensors are 16-byte
+ * aligned; one head's rows must span less than 2 GiB ((S + 64) D 2 < 2^31),
+ * else ATTN_ERR_SHAPE.  One kernel is enqueued.
  */
 int attn_cca_mix(void *q_out, void *k_out, void *v_out, const void *q, const void *k,
                  const void *v, int dtype, int B, int Hq, int Hkv, int S, int D,
