@@ -16,7 +16,8 @@ training backward pass of both prefill workloads, and `cpu_baseline` times
 the fp64 CPU oracle on a bounded sample of the same prefill workload (and on
 the gqa_decode batch).  `prefill_ccgqa` times the compressed-latent prefill
 (batch 2, 8 query heads, 2 KV heads, head dim 64, 16384 tokens) the same way
-as the headline step.  Prints one JSON line on stdout.
+as the headline step, and `ccgqa_cca_step` the same layer with the CCA
+pre-attention pass (convolutions, QK-mean, RoPE, value shift) before it.  Prints one JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -291,6 +292,64 @@ def prefill_line(w, steps, warmup):
             "step": "rope(K) + causal GQA prefill with the query RoPE fused"}
 
 
+def cca_bytes(w):
+    """Algorithmic HBM bytes of the CCA pre-attention pass: q, k and v read
+    once and written once (bf16); the per-head weights are negligible."""
+    return float(2 * 2 * w.B * w.S * w.D * (w.Hq + 2 * w.Hkv))
+
+
+def bench_cca_step(w, steps, warmup):
+    """The compressed-latent layer's attention step: the CCA pre-attention
+    pass (causal sequence convolution, channel mix, QK-mean, RoPE of q and k,
+    value shift), then causal GQA prefill on its outputs.  Each kernel is
+    timed with HIP events on the stream it runs on."""
+    import torch
+    import compressed_latent_causal_amd as attn
+    from compressed_latent_causal_amd import workloads as wl
+
+    ins = [t.cuda() for t in wl.make_cca(w, seed=0)]
+    qo, ko, vo = torch.empty_like(ins[0]), torch.empty_like(ins[1]), torch.empty_like(ins[2])
+    o = torch.empty_like(ins[0])
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        attn.cca_mix(*ins, rope_theta=w.theta, q_out=qo, k_out=ko, v_out=vo)
+        if ev is not None:
+            ev[1].record(stream)
+        attn.prefill(qo, ko, vo, w.scale, out=o)
+        if ev is not None:
+            ev[2].record(stream)
+
+    settle(step)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mix_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+    pre_ms = sum(b.elapsed_time(c) for _, b, c in evs) / steps
+    flops = prefill_flops(w.B, w.Hq, w.S, w.D)
+    gbs = cca_bytes(w) / (mix_ms * 1e-3) / 1e9
+    ms_step = wall * 1e3 / steps
+    return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+            "head_dim": w.D, "seq_len": w.S, "rope_theta": w.theta,
+            "conv_width": wl.CCA_CONV_WIDTH,
+            "cca_mix_ms_mean": round(mix_ms, 5), "cca_mix_bytes": cca_bytes(w),
+            "cca_mix_GB_per_s": round(gbs, 1), "cca_mix_frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "prefill_ms_mean": round(pre_ms, 5),
+            "prefill_TFLOP_per_s": round(flops / (pre_ms * 1e-3) / 1e12, 1),
+            "ms_per_step": round(ms_step, 5),
+            "step_TFLOP_per_s": round(flops / (ms_step * 1e-3) / 1e12, 1), "steps": steps,
+            "step": "CCA pre-attention pass (conv, channel mix, QK-mean, RoPE, value shift) + "
+                    "causal GQA prefill"}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -369,7 +428,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "gqa_decode", "long_decode", "gqa_decode_paged256",
-                                       "ccgqa_prefill", "backward_llama8b_prefill",
+                                       "ccgqa_prefill", "ccgqa_cca", "backward_llama8b_prefill",
                                        "backward_ccgqa_prefill", "copy"],
                     help="time one workload alone and print its line (profiling runs; `copy` is "
                          "the plain copy that calibrates the HBM byte counters)")
@@ -389,6 +448,10 @@ def main():
 
     if args.only == "copy":
         print(json.dumps(bench_copy()), flush=True)
+        return
+    if args.only == "ccgqa_cca":
+        print(json.dumps(bench_cca_step(wl.WORKLOADS["ccgqa_prefill"], args.steps, args.warmup)),
+              flush=True)
         return
     if args.only and args.only.startswith("backward_"):
         b = bench_backward(wl.WORKLOADS[args.only[len("backward_"):]], args.steps, args.warmup)
@@ -438,6 +501,10 @@ def main():
     log(f"prefill ccgqa_prefill: kernel mean {cc['kernel_ms_mean']:.4f} ms "
         f"({cc['TFLOP_per_s']:.1f} TFLOP/s), step {cc['ms_per_step']:.4f} ms")
     result["prefill_ccgqa"] = cc
+    ca = bench_cca_step(wl.WORKLOADS["ccgqa_prefill"], args.steps, args.warmup)
+    log(f"ccgqa with the CCA pass: mix {ca['cca_mix_ms_mean']:.4f} ms ({ca['cca_mix_GB_per_s']:.0f} GB/s), "
+        f"prefill {ca['prefill_ms_mean']:.4f} ms, step {ca['ms_per_step']:.4f} ms")
+    result["ccgqa_cca_step"] = ca
     if not args.no_decode:
         dec = {}
         for name, wname, page in DECODE_LINES:

@@ -19,13 +19,14 @@
 //  * Scores are formed transposed, S^T = K Q^T, with the 16x16x32 bf16 matrix
 //    core: each lane ends up holding one query and 4 keys per 16x16 tile, so the
 //    softmax row statistics are per-lane scalars (plus a 4-lane reduction).
-//  * Online softmax in fp32 in the exp2 domain.  Q is pre-scaled by
-//    scale * log2 e, and the score products start from the negated running
-//    reference instead of zero, so they produce the exponent itself: one exp2
-//    per score and no other arithmetic before it.  The reference moves only
-//    when a tile raises it by more than 2^8, so almost every tile skips
-//    rescaling O (the normalisation at the end is exact for any reference).  P is rounded to bf16 and fed
-//    straight from registers as the
+//  * Online softmax in fp32 in the exp2 domain.  Q enters the score products
+//    exactly (a copy pre-scaled by scale * log2 e and rounded to bf16 again
+//    would move each score by up to 2^-9 of its terms, which peaked softmaxes
+//    do not tolerate); one FMA per score then forms the exponent
+//    c s - reference, and one exp2 the probability.  The reference moves only
+//    when a tile's probabilities would sum past 2^16, so almost every tile
+//    skips rescaling O (the normalisation at the end is exact for any
+//    reference).  P is rounded to bf16 and fed straight from registers as the
 //    B operand of O^T = V^T P^T.  The A operand (V^T) comes from the row-major
 //    V tile through the LDS transpose read, so V is never transposed in memory.
 //  * K/V tiles are double-buffered in LDS and loaded with buffer loads that
@@ -157,10 +158,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                     x[e] = pack_bf16x2(y0, y1);
                 }
             }
-            // pre-scale by c = scale * log2(e) (rounded to bf16 once more), so
-            // the products are scores in the exp2 domain
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = pack_bf16x2(bf16_lo(x[e]) * c, bf16_hi(x[e]) * c);
+            // q enters the products exactly as given (or as rotated): a
+            // pre-scaled copy, rounded to bf16 once more, would move each
+            // score by up to 2^-9 of its terms, too much for peaked softmaxes
             qf[n][s] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
@@ -207,10 +207,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt][0] = oacc[dt][1] = f32x4_t{0, 0, 0, 0};
     // Running reference of each row in the exp2 domain (-inf before the first
-    // tile), and its negation as a 16x16 accumulator: the score products start
-    // from it, so they yield c * s - reference with no vector instruction.
+    // tile; 0 stands in for it until the first tile sets it).
     float m_run[2] = {-INFINITY, -INFINITY};
-    f32x4_t negm[2] = {f32x4_t{0, 0, 0, 0}, f32x4_t{0, 0, 0, 0}};
+    float mref[2] = {0.f, 0.f};
     // Row sums of P, formed on the matrix core: a tile of ones times P^T puts
     // each query's sum over the tile's keys in every element of its lane (no
     // lane reduction), and it sums exactly the bf16 values the P V product
@@ -238,10 +237,18 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
             if (f + PF_PD < NKF) kf[f + PF_PD] = kfrag(f + PF_PD);
             __builtin_amdgcn_sched_barrier(0);
             const int s = f / 4, mt = f % 4;
-            sacc[mt][0] = mfma16(kf[f], qf[0][s], s == 0 ? negm[0] : sacc[mt][0]);
-            sacc[mt][1] = mfma16(kf[f], qf[1][s], s == 0 ? negm[1] : sacc[mt][1]);
+            sacc[mt][0] = mfma16(kf[f], qf[0][s], s == 0 ? f32x4_t{0, 0, 0, 0} : sacc[mt][0]);
+            sacc[mt][1] = mfma16(kf[f], qf[1][s], s == 0 ? f32x4_t{0, 0, 0, 0} : sacc[mt][1]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // into the exp2 domain relative to the reference: c s - reference,
+        // one FMA per score
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sacc[mt][n][i] = fmaf(sacc[mt][n][i], c, -mref[n]);
 
         // ---- online softmax; lane holds query qw0 + 16n + lr and keys kv0 + 16mt + 4lg + i
         if (t == last && kv0 + PF_BN - 1 > qw0) {  // the diagonal tile: mask future keys
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                 // nothing is accumulated before the first tile
                 const float alpha = (m_run[n] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(-d);
                 if (up) m_run[n] = (m_run[n] == -INFINITY ? 0.f : m_run[n]) + d;
-                negm[n] = f32x4_t{-m_run[n], -m_run[n], -m_run[n], -m_run[n]};
+                mref[n] = m_run[n] == -INFINITY ? 0.f : m_run[n];
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) sacc[mt][n] -= d;
 #pragma unroll

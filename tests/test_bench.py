@@ -74,3 +74,10 @@ def test_cpu_baseline_decode_record_on_a_small_workload():
     assert r["kind"] == "oracle" and r["unit"] == "GB/s"
     assert r["value"] > 0 and r["cores"] >= 1
     assert "3 sequences" in r["sample"]
+
+
+def test_cca_bytes_read_and_write_q_k_v_once():
+    w = wl.WORKLOADS["ccgqa_prefill"]
+    per_tensor = lambda H: w.B * H * w.S * w.D * 2
+    assert bench.cca_bytes(w) == 2 * (per_tensor(w.Hq) + 2 * per_tensor(w.Hkv))
+    assert bench.cca_bytes(w) == 96 * 2 ** 20

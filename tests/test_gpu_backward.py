@@ -3,18 +3,17 @@ called through the C ABI, against the fp64 CPU oracle on the same seeded bf16
 inputs (marker `gpu`; needs an MI355X).
 
 Tolerances.  The log-normaliser is checked against a per-row bound: the
-forward rounds q * scale * log2(e) to bf16 (relative error <= 2^-8 per
-element), so each score moves by at most 2^-8 scale sum_d |q_d k_d|, and the
-row sum adds bf16-rounded probabilities (relative error <= 2^-8); lse moves by
-no more than the largest score error plus 2^-8.
+forward's scores are fp32 sums of exact bf16 products (error <= 2^-16 scale
+sum_d |q_d k_d| for D <= 128, with the exp2-domain FMA), and the row sum adds
+bf16-rounded probabilities (relative error <= 2^-8); lse moves by no more
+than the largest score error plus 2^-8.
 Gradients: the GPU rounds p, ds and the forward's o (which enters delta) to
-bf16, scores carry the forward's rounding of q * scale * log2(e) through lse,
-and each gradient is rounded once at the end; each is a relative error <=
-2^-8 on terms that add with random signs.  An element's error is therefore a
-few 2^-8 of the size of its own gradient row (rows differ a lot in size: a
-query that sees few keys has large gradients).  The bar: every element within
-2^-4 of max(rms of its row, rms of the tensor), and the mean error within
-2^-7 of the tensor's rms.  dq gets one more, separately derived allowance:
+bf16, and each gradient is rounded once at the end; each is a relative error
+<= 2^-8 on terms that add with random signs.  An element's error is
+therefore a few 2^-8 of the size of its own gradient row (rows differ a lot in
+size: a query that sees few keys has large gradients).  The bar: every
+element within 2^-5 of max(rms of its row, rms of the tensor), and the mean
+error within 2^-7 of the tensor's rms.  dq gets one more, separately derived allowance:
 delta = <dout_i, o_i> uses the forward's bf16 o (each element within 2^-8 of
 o's exact value), which moves every ds of row i by p times the same error and
 so dq_i by scale |delta error| |sum_t p_t k_t|; that is at most
@@ -34,7 +33,7 @@ from compressed_latent_causal_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-GRAD_MAX, GRAD_MEAN = 2.0 ** -4, 2.0 ** -7
+GRAD_MAX, GRAD_MEAN = 2.0 ** -5, 2.0 ** -7
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -59,7 +58,7 @@ def _lse_bound(q, k, scale):
     a = np.einsum("bhid,bhtd->bhit", np.abs(qf), kr) * scale
     S = qf.shape[2]
     a = np.where(np.tril(np.ones((S, S), dtype=bool)), a, 0.0)
-    return 2.0 ** -8 * (a.max(axis=-1) + 1.0) + 1e-5
+    return 2.0 ** -16 * a.max(axis=-1) + 2.0 ** -8 + 1e-5
 
 
 def _dq_delta_allowance(q, k, v, dout, scale, rows=None):

@@ -361,6 +361,47 @@ def test_prefill_scores_growing_along_the_keys(D):
                  what=f"growing scores D={D}")
 
 
+PEAKED = [  # B, Hq, Hkv, S, D, sigma of q and k, fused RoPE theta (0: none)
+    (1, 8, 2, 517, 64, 3.0, 0.0),
+    (1, 8, 2, 517, 128, 3.0, 0.0),
+    (2, 4, 1, 300, 64, 5.0, 1e4),
+    (1, 4, 2, 1000, 128, 5.0, 5e5),
+]
+
+
+@pytest.mark.parametrize("case", PEAKED)
+def test_prefill_peaked_softmax(case):
+    """q and k ~ N(0, sigma^2), so the scaled scores have a standard deviation
+    of sigma^2 (9 and 25): a row's weight sits on a few keys, and a score
+    error of a few hundredths of an exp2 unit shows in the output.  bf16
+    inputs must still meet the bf16 tolerance (the kernel multiplies the exact
+    q, never a rounded pre-scaled copy)."""
+    B, Hq, Hkv, S, D, sigma, theta = case
+    g = torch.Generator().manual_seed(int(100 * sigma) + D + S)
+    q = (torch.randn(B, Hq, S, D, generator=g) * sigma).to(torch.bfloat16)
+    k = (torch.randn(B, Hkv, S, D, generator=g) * sigma).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, S, D, generator=g).to(torch.bfloat16)
+    say(f"prefill peaked softmax {case}")
+    o = attn.prefill(dev(q), dev(k), dev(v), rope_theta=theta)
+    qb = bits(q) if theta == 0 else oracle.round_bf16(oracle.rope(bits(q), theta))
+    ref = oracle.prefill(qb, bits(k), bits(v))
+    assert_close(host_f64(o), ref, BF16_MAX, BF16_MEAN, what=f"peaked {case}")
+
+
+@pytest.mark.parametrize("sigma", [3.0, 5.0])
+def test_decode_peaked_softmax(sigma):
+    B, Hq, Hkv, S_cap, D = 4, 16, 2, 3000, 128
+    g = torch.Generator().manual_seed(int(10 * sigma))
+    q = (torch.randn(B, Hq, D, generator=g) * sigma).to(torch.bfloat16)
+    kc = (torch.randn(B, Hkv, S_cap, D, generator=g) * sigma).to(torch.bfloat16)
+    vc = torch.randn(B, Hkv, S_cap, D, generator=g).to(torch.bfloat16)
+    lens = torch.tensor([3000, 1700, 513, 31], dtype=torch.int32)
+    say(f"decode peaked softmax sigma={sigma}")
+    o = attn.decode(dev(q), dev(kc), dev(vc), dev(lens))
+    ref = oracle.decode(bits(q), bits(kc), bits(vc), lens.numpy())
+    assert_close(host_f64(o), ref, BF16_MAX, BF16_MEAN, what=f"decode peaked {sigma}")
+
+
 def _sample_rows(B, Hq, S, n_random, seed):
     """Row indices (b*Hq + h)*S + i: both ends of every head, tile edges and
     random interior rows."""
