@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void bwd_rowstats_kernel(const uint16_t* __res
 
 // ------------------------------------------------------------------ dK, dV
 template <int D, int NK, int NW>
-__global__ __launch_bounds__(NW * 64, (NK == 1 && NW == 4) ? 2 : 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(NW * 64, ((NK == 1 || D == 64) && NW == 4) ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float2* __restrict__ stats, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int B, int Hq, int Hkv, int S, int S_pad, float c, float scale) {
@@ -520,8 +520,13 @@ int pow2_divisor(int g, int cap) {
     return hp;
 }
 
-#ifndef BW_NK
-#define BW_NK 1
+// keys of 16 per wave in the dK/dV kernel, per head dim: each Q and dO
+// operand fragment read from LDS feeds NK products
+#ifndef BW_NK64
+#define BW_NK64 1
+#endif
+#ifndef BW_NK128
+#define BW_NK128 1
 #endif
 #ifndef BW_NW
 #define BW_NW 4
@@ -543,9 +548,10 @@ hipError_t launch_backward_d(void* dq, void* dk, void* dv, const void* q, const 
                            S, S_pad, rows);
     }
     {
-        constexpr int BK = 16 * BW_NK * BW_NW;
+        constexpr int NK = D == 64 ? BW_NK64 : BW_NK128;
+        constexpr int BK = 16 * NK * BW_NW;
         const long long nblk = (long long)ceil_div(S, BK) * B * Hkv;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, BW_NK, BW_NW>), dim3((unsigned)nblk),
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NK, BW_NW>), dim3((unsigned)nblk),
                            dim3(BW_NW * 64), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                            (const uint16_t*)v, (const uint16_t*)dout, (const float2*)stats,
                            (uint16_t*)dk, (uint16_t*)dv, B, Hq, Hkv, S, S_pad, c, scale);

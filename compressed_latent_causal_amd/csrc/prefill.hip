@@ -59,13 +59,30 @@ namespace {
 #define ATTN_PF_WAVES 4
 #endif
 constexpr int PF_BN = 64;                 // keys per K/V tile
-constexpr int PF_QW = 32;                 // queries per wave
+// Query tiles of 16 per wave (NQ): every K and V operand fragment read from
+// LDS feeds NQ products, so LDS bytes per product fall as 1 / NQ.
+#ifndef PF_NQ64
+#define PF_NQ64 2
+#endif
+#ifndef PF_NQ128
+#define PF_NQ128 2
+#endif
 constexpr int PF_NW = ATTN_PF_WAVES;      // waves per workgroup
 constexpr int PF_THREADS = PF_NW * 64;
 // LDS operand fragments read ahead of the products that use them
 #ifndef PF_PD
 #define PF_PD 2
 #endif
+// Issue priority of a wave's matrix-core phases over its softmax (experiment)
+#ifndef PF_PRIO
+#define PF_PRIO 0
+#endif
+__device__ __attribute__((always_inline)) inline void pf_prio_hi() {
+    if constexpr (PF_PRIO) __builtin_amdgcn_s_setprio(PF_PRIO);
+}
+__device__ __attribute__((always_inline)) inline void pf_prio_lo() {
+    if constexpr (PF_PRIO) __builtin_amdgcn_s_setprio(0);
+}
 
 // The online softmax keeps a per-row reference (a past tile maximum) and only
 // moves it when a tile's probabilities relative to it sum to more than this:
@@ -74,13 +91,14 @@ constexpr int PF_THREADS = PF_NW * 64;
 // a maximum nor a rescale of O.
 constexpr float PF_SUM_LIMIT = 65536.f;
 
-template <int D, int HPW>
-__global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
+template <int D, int HPW, int NQ>
+__global__ __launch_bounds__(PF_THREADS, (D == 64 || NQ == 2) ? 2 : 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int S, float c,
     int n_qblk, int n_hchunk, int rope, RopeFreqs fr) {
     constexpr int KSTEPS = D / 32;              // k-steps of S^T = K Q^T
     constexpr int DT = D / 16;                  // d tiles of O^T
+    constexpr int PF_QW = 16 * NQ;              // queries per wave
     constexpr int QPB = (PF_NW / HPW) * PF_QW;  // queries per head per workgroup
     constexpr int ROW = D * 2;                  // bytes per LDS row
     constexpr int TILE = PF_BN * ROW;
@@ -131,9 +149,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     }
 
     // Q^T fragments (B operand): query qw0 + 16n + lr, dims 32s + 8lg .. +7.
-    bf16x8_t qf[2][KSTEPS];
+    bf16x8_t qf[NQ][KSTEPS];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int n = 0; n < NQ; ++n) {
         const int row = qw0 + 16 * n + lr;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
@@ -147,8 +165,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
                     const int pr = 16 * s + 4 * lg + e;
                     float cs, sn, y0, y1;
                     if constexpr (kRopeTable) {
-                        const float2 t = *(const float2*)((w / HPW == 0 ? k1 : v1) +
-                                                          ((16 * n + lr) * (D / 2) + pr) * 8);
+                        const int tr = (w / HPW) * PF_QW + 16 * n + lr;  // table row
+                        const float2 t = *(const float2*)((tr < 32 ? k1 : v1) +
+                                                          ((tr & 31) * (D / 2) + pr) * 8);
                         cs = t.x;
                         sn = t.y;
                     } else {
@@ -203,19 +222,27 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     // last tile this wave needs (-1: none, the wave's queries are all past S)
     const int last = qw0 < S ? min(ntiles - 1, (qw0 + PF_QW - 1) / PF_BN) : -1;
 
-    f32x4_t oacc[DT][2];
+    f32x4_t oacc[DT][NQ];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt][0] = oacc[dt][1] = f32x4_t{0, 0, 0, 0};
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) oacc[dt][n] = f32x4_t{0, 0, 0, 0};
     // Running reference of each row in the exp2 domain (-inf before the first
     // tile; 0 stands in for it until the first tile sets it).
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float mref[2] = {0.f, 0.f};
+    float m_run[NQ], mref[NQ];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+        m_run[n] = -INFINITY;
+        mref[n] = 0.f;
+    }
     // Row sums of P, formed on the matrix core: a tile of ones times P^T puts
     // each query's sum over the tile's keys in every element of its lane (no
     // lane reduction), and it sums exactly the bf16 values the P V product
     // weights.  Four products per tile cost less than 32 vector adds, since
     // vector and matrix instructions share a SIMD's issue.
-    float lacc[2] = {0.f, 0.f};
+    float lacc[NQ];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) lacc[n] = 0.f;
     const bf16x8_t kOnes = __builtin_bit_cast(
         bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});  // bf16 1.0
 
@@ -228,8 +255,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         auto kfrag = [&](int f) __attribute__((always_inline)) {
             return *(const bf16x8_t*)(ks + koff[f / 4] + 16 * (f % 4) * ROW);
         };
-        f32x4_t sacc[4][2];
+        f32x4_t sacc[4][NQ];
         bf16x8_t kf[NKF];
+        pf_prio_hi();
 #pragma unroll
         for (int f = 0; f < PF_PD && f < NKF; ++f) kf[f] = kfrag(f);
 #pragma unroll
@@ -237,14 +265,16 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
             if (f + PF_PD < NKF) kf[f + PF_PD] = kfrag(f + PF_PD);
             __builtin_amdgcn_sched_barrier(0);
             const int s = f / 4, mt = f % 4;
-            sacc[mt][0] = mfma16(kf[f], qf[0][s], s == 0 ? f32x4_t{0, 0, 0, 0} : sacc[mt][0]);
-            sacc[mt][1] = mfma16(kf[f], qf[1][s], s == 0 ? f32x4_t{0, 0, 0, 0} : sacc[mt][1]);
+#pragma unroll
+            for (int n = 0; n < NQ; ++n)
+                sacc[mt][n] = mfma16(kf[f], qf[n][s], s == 0 ? f32x4_t{0, 0, 0, 0} : sacc[mt][n]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        pf_prio_lo();
         // into the exp2 domain relative to the reference: c s - reference,
         // one FMA per score
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < NQ; ++n)
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -253,7 +283,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         // ---- online softmax; lane holds query qw0 + 16n + lr and keys kv0 + 16mt + 4lg + i
         if (t == last && kv0 + PF_BN - 1 > qw0) {  // the diagonal tile: mask future keys
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
+            for (int n = 0; n < NQ; ++n) {
                 const int lim = qw0 + 16 * n + lr - kv0 - 4 * lg;  // key offsets above lim are masked
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
@@ -264,11 +294,11 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         }
         // ---- sacc = c * s - reference.  P = exp2(sacc) as bf16 fragments and
         // its row sums lt for this tile.
-        bf16x8_t pf[2][2];
-        f32x4_t lt[2];
+        bf16x8_t pf[NQ][2];
+        f32x4_t lt[NQ];
         auto exp_pack = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
+            for (int n = 0; n < NQ; ++n) {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     u32x4_t pw;
@@ -291,10 +321,10 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
         // (wave-uniform branch, taken on few tiles).
         bool redo = false;
 #pragma unroll
-        for (int n = 0; n < 2; ++n) redo |= (m_run[n] == -INFINITY) | !(lt[n][0] <= PF_SUM_LIMIT);
+        for (int n = 0; n < NQ; ++n) redo |= (m_run[n] == -INFINITY) | !(lt[n][0] <= PF_SUM_LIMIT);
         if (__any(redo)) {
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
+            for (int n = 0; n < NQ; ++n) {
                 // NaN-propagating maximum: one 3-input instruction per pair
                 float m = sacc[0][n][0];
 #pragma unroll
@@ -316,8 +346,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
             }
             exp_pack();
         }
-        lacc[0] += lt[0][0];
-        lacc[1] += lt[1][0];
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) lacc[n] += lt[n][0];
 
         // ---- O^T += V^T P^T, operand f = (d tile f / 2, key half f % 2) read
         // PF_PD operands ahead
@@ -326,6 +356,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
             return v_frag_at<D>(vs + voff[f / 2] + 32 * (f % 2) * ROW);
         };
         bf16x8_t vf[NVF];
+        pf_prio_hi();
 #pragma unroll
         for (int f = 0; f < PF_PD && f < NVF; ++f) vf[f] = vfrag(f);
 #pragma unroll
@@ -333,10 +364,11 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
             if (f + PF_PD < NVF) vf[f + PF_PD] = vfrag(f + PF_PD);
             __builtin_amdgcn_sched_barrier(0);
             const int dt = f / 2, kk = f % 2;
-            oacc[dt][0] = mfma16(vf[f], pf[0][kk], oacc[dt][0]);
-            oacc[dt][1] = mfma16(vf[f], pf[1][kk], oacc[dt][1]);
+#pragma unroll
+            for (int n = 0; n < NQ; ++n) oacc[dt][n] = mfma16(vf[f], pf[n][kk], oacc[dt][n]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        pf_prio_lo();
     };
 
     // Tile t sits in buffer t & 1.  Each step waits for its own share of tile
@@ -363,7 +395,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_bf16_kernel(
     // The row's probabilities are exp2(c s - m_run) / l, so its log-normaliser
     // (natural log, of the scaled scores) is ln 2 * (m_run + log2 l).
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int n = 0; n < NQ; ++n) {
         const float lt = lacc[n];
         const int qi = qw0 + 16 * n + lr;
         if (qi >= S) continue;
@@ -472,11 +504,12 @@ int largest_pow2_divisor(int g, int cap) {
 template <int D, int HPW>
 hipError_t launch_bf16(void* o, float* lse, const void* q, const void* k, const void* v, int B,
                        int Hq, int Hkv, int S, float c, double rope_theta, hipStream_t st) {
-    constexpr int QPB = (PF_NW / HPW) * PF_QW;
+    constexpr int NQ = D == 64 ? PF_NQ64 : PF_NQ128;
+    constexpr int QPB = (PF_NW / HPW) * 16 * NQ;
     const int G = Hq / Hkv;
     const int n_qblk = ceil_div(S, QPB), n_hchunk = G / HPW;
     const long long nblk = (long long)n_qblk * B * Hkv * n_hchunk;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW>), dim3((unsigned)nblk), dim3(PF_THREADS), 0, st,
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW, NQ>), dim3((unsigned)nblk), dim3(PF_THREADS), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
                        B, Hq, Hkv, S, c, n_qblk, n_hchunk, rope_theta > 0 ? 1 : 0,
                        rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D));
