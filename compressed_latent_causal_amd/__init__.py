@@ -314,18 +314,18 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, max_len: int | None 
 def cca_mix(q, k, v, conv_q, conv_k, mix_q, mix_k, rope_theta: float = 0.0, pos_offset=None,
             q_out=None, k_out=None, v_out=None):
     """CCA pre-attention operations on the compressed q [B,Hq,S,D], k, v
-    [B,Hkv,S,D] (bf16): causal depthwise sequence convolution (conv_q [Hq,D,W],
-    conv_k [Hkv,D,W]; tap i weighs the token i steps back), channel mix per
+    [B,Hkv,S,D] (bf16): causal depthwise sequence convolution (conv_q [Hq,W,D],
+    conv_k [Hkv,W,D]; tap i weighs the token i steps back), channel mix per
     head (mix_q [Hq,D,D], mix_k [Hkv,D,D]; row c = output channel c), plus the
     group's pre-convolution query/key mean; RoPE at position pos_offset[b] + t
     when rope_theta > 0; value shift (last D/2 channels from the previous
     token).  Returns (q_out, k_out, v_out), ready for prefill(..., rope_theta=0)."""
     torch = _torch()
     B, Hq, Hkv, S, D = _check_prefill_shapes(q, k, v)
-    W = conv_q.shape[-1] if conv_q.dim() == 3 else -1
-    if (conv_q.shape != (Hq, D, W) or conv_k.shape != (Hkv, D, W) or mix_q.shape != (Hq, D, D)
+    W = conv_q.shape[1] if conv_q.dim() == 3 else -1
+    if (conv_q.shape != (Hq, W, D) or conv_k.shape != (Hkv, W, D) or mix_q.shape != (Hq, D, D)
             or mix_k.shape != (Hkv, D, D)):
-        raise ValueError("conv_q [Hq,D,W], conv_k [Hkv,D,W], mix_q [Hq,D,D], mix_k [Hkv,D,D]")
+        raise ValueError("conv_q [Hq,W,D], conv_k [Hkv,W,D], mix_q [Hq,D,D], mix_k [Hkv,D,D]")
     if any(t.dtype != q.dtype for t in (conv_q, conv_k, mix_q, mix_k)):
         raise ValueError("weights must share the activations' dtype")
     q_out = torch.empty_like(q) if q_out is None else q_out

@@ -4,7 +4,7 @@
 // "Methodologie", items 2 to 4; the summary names the operations without
 // their sizes, so each is taken in its plainest form):
 //  * sequence mixing: a causal depthwise convolution of width W over the
-//    sequence, per channel of every head, s[t,c] = sum_{i<W} w[h,c,i] x[t-i,c]
+//    sequence, per channel of every head, s[t,c] = sum_{i<W} w[h,i,c] x[t-i,c]
 //    (tap i weighs the token i steps back; tokens before the first are zero);
 //  * channel mixing within a head: a dense D x D map per head,
 //    z[t,c] = sum_c' M[h,c,c'] s[t,c'] (row c of M is output channel c);
@@ -19,21 +19,23 @@
 // Design.  One workgroup = 4 waves = one (sequence, KV group, 64-token block);
 // wave w owns 16 tokens and walks the group's G query heads and its key head.
 // Per head and wave, the 16 x D result is one matrix-core product,
-// Z^T = M S^T with the 16x16x32 bf16 instruction: the A operand is M, staged in
-// LDS once per workgroup and head by buffer loads that write LDS directly
-// (double-buffered across heads, so head n+1's matrix streams in while head n
-// is computed); the B operand is S^T, the convolution's output, which each lane
-// forms in fp32 for its token and 8 channels per k-step.  The convolution's
-// earlier tokens come from the lanes below in the same 16-lane row (DPP row
-// shifts), the W - 1 rows before the wave's first token from a second load of
-// the previous 16 rows (DPP row rotates).  S is split into bf16 high and low
-// parts and both are multiplied, so the product is accurate to about 2^-17 of
-// its terms: the result is the fp32-accurate value, rounded once to bf16.
-// In the result layout each lane holds 4 consecutive channels of one token,
-// so the mean is added, channel pairs are rotated in registers and 8 bytes
-// are stored per lane.  The next head's input rows are loaded while the
-// current head is computed.  The kernel is bound by HBM (it reads and writes
-// q, k and v once) and by the vector work of the convolution.
+// Z^T = M S^T with the 16x16x32 bf16 instruction: the A operand is M, the B
+// operand S^T, the convolution's output, which each lane forms in fp32 for its
+// token and 8 channels per k-step.  Everything a head reads arrives by buffer
+// loads that write LDS directly, double-buffered across heads, so head n+1's
+// data streams in while head n is computed and no input lives in registers:
+// the mix matrix (swizzled for the operand reads), the conv taps, and each
+// wave's 16 rows plus the 8 before them (swizzled so that 16 lanes reading 16
+// consecutive rows hit distinct banks).  Every load is issued by every lane
+// (a buffer resource turns reads past a tensor into zeros), so each wave waits
+// for its own loads by count and one barrier per head publishes them.  S is
+// split into bf16 high and low parts and both are multiplied, so the product is
+// accurate to about 2^-17 of its terms: the result is the fp32-accurate value,
+// rounded once to bf16.  In the result layout each lane holds 4 consecutive
+// channels of one token, so the mean is added, channel pairs are rotated in
+// registers and 8 bytes are stored per lane (buffer stores, which drop tokens
+// past the end, so their number is fixed too).  The kernel is bound by HBM (it
+// reads and writes q, k and v once) and by the vector work of the convolution.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -45,57 +47,38 @@ constexpr int CM_NW = 4;               // waves per workgroup
 constexpr int CM_TW = 16;              // tokens per wave
 constexpr int CM_TB = CM_NW * CM_TW;   // tokens per workgroup
 constexpr int CM_MAXW = 8;             // widest sequence convolution
+constexpr int CM_PREV = 8;             // rows kept before a wave's first token (CM_MAXW - 1 needed)
 
 // s_waitcnt immediate: vmcnt(n) and lgkmcnt(0)
 constexpr int wait_vmcnt_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
 
-// x of the lane SH places lower in the same 16-lane row; lanes with none keep `low`
-template <int SH>
-__device__ inline unsigned row_shift_in(unsigned x, unsigned low) {
-    return (unsigned)__builtin_amdgcn_update_dpp((int)low, (int)x, 0x110 + SH, 0xF, 0xF, false);
-}
-// x of the lane SH places lower in the same 16-lane row, cyclically
-template <int SH>
-__device__ inline unsigned row_rotate(unsigned x) {
-    return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x120 + SH, 0xF, 0xF, false);
-}
-
-
-// Input rows of one head as one vector value (dword 4 s + e of k-step s), so
-// they stay in registers across the head loop.
-template <int N>
-struct DwordVec {
-    typedef unsigned type __attribute__((ext_vector_type(N)));
-};
 template <int D>
-using RowsVec = typename DwordVec<D / 8>::type;
+struct CcaLayout {
+    static constexpr int ROW = D * 2;                        // bytes per bf16 row
+    static constexpr int MBYTES = D * ROW;                   // one head's mix matrix
+    static constexpr int MINST = MBYTES / 1024 / CM_NW;      // its 1 KiB copies per wave
+    static constexpr int XBYTES = (CM_TW + CM_PREV) * ROW;   // one wave's input rows
+    static constexpr int XINST = XBYTES / 1024;              // their 1 KiB copies
+    static constexpr int CBYTES = CM_MAXW * ROW;             // one head's taps, at most
+    static constexpr int CINST = CBYTES / 1024;              // copies (one per wave)
+    static_assert(MINST >= 1 && XBYTES % 1024 == 0 && CBYTES % 1024 == 0 && CINST <= CM_NW,
+                  "copy split");
+};
 
-// Tap I of the sequence convolution for this lane's token t and channels
-// 32 s + 8 g + e: y += w[I][c] x[t - I, c].  Row t - I sits in lane r - I of
-// the same 16-lane row, or, for r < I, in lane r - I + 16 of the previous 16
-// rows.
+// Tap I of the sequence convolution for this lane's token (row CM_PREV + r of
+// the wave's rows) and channels 32 s + 8 g + e: y += w[I][c] x[t - I, c], with
+// the taps [W][D] and the rows (swz_k layout) in LDS.
 template <int D, int I>
-__device__ __attribute__((always_inline)) inline void conv_tap(float (&y)[D / 32][8],
-                                                               const RowsVec<D>& cur,
-                                                               const RowsVec<D>& prv,
-                                                               const float* wsm, int g) {
+__device__ __attribute__((always_inline)) inline void conv_tap(float (&y)[D / 32][8], const char* xs,
+                                                               const char* cs, int r, int g) {
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-        u32x4_t x;
+        const u32x4_t x = *(const u32x4_t*)(xs + swz_k<D>(CM_PREV + r - I, 4 * s + g));
+        const u32x4_t wv = *(const u32x4_t*)(cs + (I * D + 32 * s + 8 * g) * 2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if constexpr (I == 0)
-                x[e] = cur[4 * s + e];
-            else
-                x[e] = row_shift_in<I>(cur[4 * s + e], row_rotate<I>(prv[4 * s + e]));
-        }
-        const f32x4_t w0 = *(const f32x4_t*)(wsm + I * D + 32 * s + 8 * g);
-        const f32x4_t w1 = *(const f32x4_t*)(wsm + I * D + 32 * s + 8 * g + 4);
-        const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            y[s][2 * e] = fmaf(wv[2 * e], bf16_lo(x[e]), y[s][2 * e]);
-            y[s][2 * e + 1] = fmaf(wv[2 * e + 1], bf16_hi(x[e]), y[s][2 * e + 1]);
+            y[s][2 * e] = fmaf(bf16_lo(wv[e]), bf16_lo(x[e]), y[s][2 * e]);
+            y[s][2 * e + 1] = fmaf(bf16_hi(wv[e]), bf16_hi(x[e]), y[s][2 * e + 1]);
         }
     }
 }
@@ -108,17 +91,19 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
     const uint16_t* __restrict__ mix_q, const uint16_t* __restrict__ mix_k,
     const int32_t* __restrict__ pos_offset, int rope, RopeFreqs fr, int Hq, int Hkv, int S,
     int n_tblk) {
-    constexpr int KS = D / 32;          // k-steps of Z^T = M S^T
-    constexpr int MT = D / 16;          // 16-channel output tiles
-    constexpr int ROW = D * 2;          // bytes per bf16 row
-    constexpr int MBYTES = D * ROW;     // one head's mix matrix
-    constexpr int MINST = MBYTES / 1024 / CM_NW;  // 1 KiB LDS-DMA instructions per wave
-    static_assert(MINST >= 1, "mix matrix split");
+    using L = CcaLayout<D>;
+    constexpr int KS = D / 32;  // k-steps of Z^T = M S^T
+    constexpr int MT = D / 16;  // 16-channel output tiles
+    constexpr int ROW = L::ROW;
 
-    __shared__ __attribute__((aligned(1024))) char msm0[MBYTES];
-    __shared__ __attribute__((aligned(1024))) char msm1[MBYTES];
-    __shared__ float wsm0[CM_MAXW * D];  // conv taps as fp32, [tap][channel]
-    __shared__ float wsm1[CM_MAXW * D];
+    // two of each buffer (head n and head n + 1), as separate objects so the
+    // compiler can tell the buffer being filled from the one being read
+    __shared__ __attribute__((aligned(1024))) char msm0[L::MBYTES];
+    __shared__ __attribute__((aligned(1024))) char msm1[L::MBYTES];
+    __shared__ __attribute__((aligned(1024))) char xsm0[CM_NW * L::XBYTES];
+    __shared__ __attribute__((aligned(1024))) char xsm1[CM_NW * L::XBYTES];
+    __shared__ __attribute__((aligned(1024))) char csm0[L::CBYTES];
+    __shared__ __attribute__((aligned(1024))) char csm1[L::CBYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,57 +128,42 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
         return n < G ? mix_q + ((size_t)j * G + n) * D * D : mix_k + (size_t)j * D * D;
     };
     auto head_conv = [&](int n) -> const uint16_t* {
-        return n < G ? conv_q + ((size_t)j * G + n) * D * W : conv_k + (size_t)j * D * W;
+        return n < G ? conv_q + ((size_t)j * G + n) * W * D : conv_k + (size_t)j * W * D;
     };
 
-    // This head's input rows and taps, replaced by the next head's once consumed:
-    // row t (this lane's token) and row t - 16 (rows before the wave's first
-    // token), channels 32 s + 8 g .. +7, and 16 bytes of the head's conv taps
-    // [D][W] (threads tid < D W / 8).
-    RowsVec<D> in_cur, in_prv;
-    u32x4_t in_wc;
-    auto put = [&](RowsVec<D>& dst, int s, u32x4_t x) __attribute__((always_inline)) {
+    // Per-lane source offsets of the copies, the same for every head.  A copy
+    // puts lane l's 16 bytes at byte 16 l of a 1 KiB destination, i.e. at
+    // physical chunk pc of row pr; the swizzle is produced by fetching the
+    // logical chunk that belongs there (the XOR swizzle is its own inverse).
+    int moff[L::MINST], xoff[L::XINST];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[4 * s + e] = x[e];
-    };
-    // Loads of head n: this wave's share of the mix matrix straight into LDS
-    // (swz_k layout: instruction u puts lane l's 16 bytes at physical chunk
-    // 64 (w MINST + u) + l, i.e. row pr, chunk pc, which holds logical chunk
-    // pc ^ f(pr)), the conv taps of channel tid, and the lane's input rows.
-    auto issue_matrix = [&](int n, char* msm) __attribute__((always_inline)) {
-        const uint16_t* const mx = head_mix(n);
+    for (int u = 0; u < L::MINST; ++u) {
+        const int P = (w * L::MINST + u) * 64 + lane;
+        const int pr = P / (D / 8), pc = P % (D / 8);
+        moff[u] = swz_k<D>(pr, pc);
+    }
 #pragma unroll
-        for (int u = 0; u < MINST; ++u) {
-            const int P = (w * MINST + u) * 64 + lane;
-            const int pr = P / (D / 8), pc = P % (D / 8);
-            const int lc = (swz_k<D>(pr, pc) - pr * ROW) >> 4;  // the XOR swizzle is an involution
-            __builtin_amdgcn_global_load_lds((const void*)(mx + (size_t)pr * D + lc * 8),
-                                             (__attribute__((address_space(3))) void*)(msm + (w * MINST + u) * 1024),
-                                             16, 0, 0);
-        }
-    };
-    auto issue_rows = [&](int n) __attribute__((always_inline)) {
-        // Every load below is issued by every lane (buffer loads: an offset
-        // past the resource reads zeros), so the number of loads in flight is
-        // fixed and the waits can count them.  The taps come as raw bf16, 16
-        // bytes per thread (threads past D W / 8 read zeros), and are unpacked
-        // once they have landed.
-        const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(head_conv(n), D * W * 2);
-        in_wc = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, 16 * tid, 0, 0));
+    for (int u = 0; u < L::XINST; ++u) {
+        const int P = u * 64 + lane;
+        const int pr = P / (D / 8), pc = P % (D / 8);
+        const int tok = t0w - CM_PREV + pr;  // rows before the first token read zeros
+        xoff[u] = tok >= 0 ? tok * ROW + (swz_k<D>(pr, pc) - pr * ROW) : -16;
+    }
+
+    // ---- the copies of head n into the given buffers
+    auto issue = [&](int n, char* msm, char* xsm, char* csm) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t mrs = buffer_rsrc(head_mix(n), L::MBYTES);
+#pragma unroll
+        for (int u = 0; u < L::MINST; ++u) dma16(mrs, msm + (w * L::MINST + u) * 1024, moff[u], 0);
         const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(head_rows(n), S * ROW);
-        // rows before the wave's first token: only the last W - 1 lanes of a
-        // row supply them, and none before the sequence's first token
-        const bool use_prv = t0w > 0 && r >= CM_TW - (W - 1);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int cb = (32 * s + 8 * g) * 2;
-            put(in_cur, s, __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, t * ROW + cb, 0, 0)));
-            put(in_prv, s, __builtin_bit_cast(
-                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, use_prv ? (t - CM_TW) * ROW + cb : -16, 0, 0)));
+        for (int u = 0; u < L::XINST; ++u) dma16(xrs, xsm + w * L::XBYTES + u * 1024, xoff[u], 0);
+        if (w < L::CINST) {  // the taps [W][D]: past W * D they read zeros
+            const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(head_conv(n), W * D * 2);
+            dma16(crs, csm + w * 1024, lane * 16, w * 1024);
         }
     };
-
-    // Loads of the value shift, issued during the last head: the workgroup's
+    // the value shift's loads (issued during the last head): the workgroup's
     // 64 rows x D/8 chunks, KS per thread (zero for the row before the first)
     constexpr int CPR = D / 8;  // 16-byte chunks per row
     static_assert(CM_TB * CPR == KS * CM_NW * 64, "value chunks per thread");
@@ -209,6 +179,8 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
                 u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, src >= 0 ? (src * D + 8 * c) * 2 : -16, 0, 0));
         }
     };
+
+    issue(0, msm0, xsm0, csm0);
 
     // ---- the token's QK-mean (result layout: channels 16 mt + 4 g + i) and,
     // with RoPE, the cosines and sines of its channel pairs
@@ -261,46 +233,40 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
     }
 
     // ---- one head: convolution, channel mix, mean, RoPE, store
-    auto body = [&](int n, const char* msm, float* wsm, char* msm_next) __attribute__((always_inline)) {
-        // This head's loads were issued before the previous head's MT result
-        // stores, the last vector-memory operations before this point (the
-        // stores are unconditional buffer stores, so their number is fixed);
-        // the first head waits for everything.
+    auto body = [&](int n, const char* msm, const char* xsm, const char* csm, char* msm_next,
+                    char* xsm_next, char* csm_next) __attribute__((always_inline)) {
+        // This head's copies were issued before the previous head's MT result
+        // stores, the last vector-memory operations of each wave before this
+        // point; the first head waits for everything.  The barrier then
+        // publishes every wave's copies and frees the other buffers.
         __builtin_amdgcn_sched_barrier(0);
         if (n == 0)
             __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
         else
             __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(MT));
+        __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if (tid < D * W / 8) {
-            // taps element e of the thread's 8: channel (8 tid + e) / W, tap (8 tid + e) % W
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int idx = 8 * tid + e;
-                const unsigned wd = in_wc[e / 2];
-                wsm[(idx % W) * D + idx / W] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
-            }
-        }
-        // every wave's share of the matrix and the taps are in LDS, and every
-        // wave is done with head n - 1 (whose buffers the next loads reuse)
-        __syncthreads();
-        if (n + 1 < NH) issue_matrix(n + 1, msm_next);
-        __builtin_amdgcn_sched_barrier(0);  // the copy stays ahead of this head's work
+        if (n + 1 < NH)
+            issue(n + 1, msm_next, xsm_next, csm_next);
+        else
+            issue_vshift();
+        __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of this head's work
 
         // S^T fragments: y[s][e] = channel 32 s + 8 g + e of token t
+        const char* const xs = xsm + w * L::XBYTES;
         float y[KS][8];
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[s][e] = 0.f;
-        conv_tap<D, 0>(y, in_cur, in_prv, wsm, g);
-        if (W > 1) conv_tap<D, 1>(y, in_cur, in_prv, wsm, g);
-        if (W > 2) conv_tap<D, 2>(y, in_cur, in_prv, wsm, g);
-        if (W > 3) conv_tap<D, 3>(y, in_cur, in_prv, wsm, g);
-        if (W > 4) conv_tap<D, 4>(y, in_cur, in_prv, wsm, g);
-        if (W > 5) conv_tap<D, 5>(y, in_cur, in_prv, wsm, g);
-        if (W > 6) conv_tap<D, 6>(y, in_cur, in_prv, wsm, g);
-        if (W > 7) conv_tap<D, 7>(y, in_cur, in_prv, wsm, g);
+        conv_tap<D, 0>(y, xs, csm, r, g);
+        if (W > 1) conv_tap<D, 1>(y, xs, csm, r, g);
+        if (W > 2) conv_tap<D, 2>(y, xs, csm, r, g);
+        if (W > 3) conv_tap<D, 3>(y, xs, csm, r, g);
+        if (W > 4) conv_tap<D, 4>(y, xs, csm, r, g);
+        if (W > 5) conv_tap<D, 5>(y, xs, csm, r, g);
+        if (W > 6) conv_tap<D, 6>(y, xs, csm, r, g);
+        if (W > 7) conv_tap<D, 7>(y, xs, csm, r, g);
         // bf16 high and low parts of S^T
         bf16x8_t yh[KS], yl[KS];
 #pragma unroll
@@ -314,14 +280,6 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
             yh[s] = __builtin_bit_cast(bf16x8_t, h4);
             yl[s] = __builtin_bit_cast(bf16x8_t, l4);
         }
-        // the input registers are consumed: load the next head's rows (or,
-        // after the last head, the value shift's) while this head's products run
-        __builtin_amdgcn_sched_barrier(0);
-        if (n + 1 < NH)
-            issue_rows(n + 1);
-        else
-            issue_vshift();
-        __builtin_amdgcn_sched_barrier(0);
         // Z^T = M S^T; lane gets channels 16 mt + 4 g + i of token t.  Stores
         // go through a buffer resource over the head's rows, which drops those
         // of tokens past the end, so every lane issues every store.
@@ -349,16 +307,13 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
         }
     };
 
-    issue_matrix(0, msm0);
-    issue_rows(0);
-    __builtin_amdgcn_sched_barrier(0);
     int n = 0;
-    // unrolled by two so each step names its LDS buffers statically
+    // unrolled by two so each step names its buffers statically
     for (; n + 1 < NH; n += 2) {
-        body(n, msm0, wsm0, msm1);
-        body(n + 1, msm1, wsm1, msm0);
+        body(n, msm0, xsm0, csm0, msm1, xsm1, csm1);
+        body(n + 1, msm1, xsm1, csm1, msm0, xsm0, csm0);
     }
-    if (n < NH) body(n, msm0, wsm0, msm1);
+    if (n < NH) body(n, msm0, xsm0, csm0, msm1, xsm1, csm1);
 
     // ---- value shift of the block's rows: chunk c of row tt comes from row
     // tt for channels below D/2 and from row tt - 1 above (stores past the
@@ -370,7 +325,6 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
         const int tt = tblk * CM_TB + e / CPR, c = e % CPR;
         __builtin_amdgcn_raw_buffer_store_b128(vsh[u], vws, (tt * D + 8 * c) * 2, 0, 0);
     }
-
 }
 
 template <int D>

@@ -124,7 +124,7 @@ def make_cca(w: Workload, seed: int = 0, width: int = CCA_CONV_WIDTH):
     """Inputs of the CCA pre-attention operations (CPU, dtype of the workload):
     the compressed q~ [B,Hq,S,D], k~, v~ [B,Hkv,S,D] drawn as make_prefill
     draws q, k, v, then from the same generator the sequence-convolution taps
-    conv_q [Hq,D,width], conv_k [Hkv,D,width] ~ N(0, 1/width) and the
+    conv_q [Hq,width,D], conv_k [Hkv,width,D] ~ N(0, 1/width) and the
     channel-mixing matrices mix_q [Hq,D,D], mix_k [Hkv,D,D] ~ N(0, 1/D), so
     the mixed vectors keep about unit scale."""
     g = torch.Generator().manual_seed(seed)
@@ -136,8 +136,8 @@ def make_cca(w: Workload, seed: int = 0, width: int = CCA_CONV_WIDTH):
         x = torch.randn(*shape, generator=g, dtype=torch.float32) * s
         return x if w.torch_dtype == torch.float32 else x.to(w.torch_dtype)
 
-    conv_q = scaled((w.Hq, w.D, width), width ** -0.5)
-    conv_k = scaled((w.Hkv, w.D, width), width ** -0.5)
+    conv_q = scaled((w.Hq, width, w.D), width ** -0.5)
+    conv_k = scaled((w.Hkv, width, w.D), width ** -0.5)
     mix_q = scaled((w.Hq, w.D, w.D), w.D ** -0.5)
     mix_k = scaled((w.Hkv, w.D, w.D), w.D ** -0.5)
     return q, k, v, conv_q, conv_k, mix_q, mix_k

@@ -271,7 +271,7 @@ int attn_decode_paged(void *o, const void *q, const void *k_pages, const void *v
  * names the operations but not their sizes or exact form, so each is taken in
  * its plainest form):
  *   sequence mixing, a causal depthwise convolution of width W per channel:
- *     s[t,c] = sum_{i<W, t-i>=0} conv[h,c,i] x~[t-i,c]   (tap i: i tokens back)
+ *     s[t,c] = sum_{i<W, t-i>=0} conv[h,i,c] x~[t-i,c]   (tap i: i tokens back)
  *   channel mixing within a head, a dense D x D map (row c = output channel c):
  *     z[t,c] = sum_c' mix[h,c,c'] s[t,c']
  *   QK-mean, the mean of the token's pre-convolution query (the group's query
@@ -284,7 +284,8 @@ int attn_decode_paged(void *o, const void *q, const void *k_pages, const void *v
  *   value shift (item 3): v[t,c] = v~[t,c] for c < D/2, v~[t-1,c] for
  *   c >= D/2 (zero at t = 0).
  * q~, q_out: [B, Hq, S, D];  k~, v~, k_out, v_out: [B, Hkv, S, D];  conv_q
- * [Hq, D, W], conv_k [Hkv, D, W], mix_q [Hq, D, D], mix_k [Hkv, D, D]; all
+ * [Hq, W, D], conv_k [Hkv, W, D] (tap-major), mix_q [Hq, D, D], mix_k
+ * [Hkv, D, D]; all
  * bf16 (dtype BF16 only), W = conv_width in 1..8, pos_offset device int32[B]
  * or NULL.  The outputs feed attn_prefill (rope_theta 0 there: q and k are
  * already rotated) and, as a cache, attn_decode.  The convolution and the

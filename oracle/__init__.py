@@ -373,7 +373,7 @@ def cca_mix(q: np.ndarray, k: np.ndarray, v: np.ndarray, conv_q: np.ndarray, con
             mix_q: np.ndarray, mix_k: np.ndarray, pos_offset=None, theta: float = 0.0):
     """The compressed q~ [B,Hq,S,D], k~, v~ [B,Hkv,S,D] through the CCA
     pre-attention operations (oracle.c, oracle_cca_mix): a causal depthwise
-    sequence convolution of width W (conv_q [Hq,D,W], conv_k [Hkv,D,W]; tap i
+    sequence convolution of width W (conv_q [Hq,W,D], conv_k [Hkv,W,D]; tap i
     weighs the token i steps back), a dense channel mix per head (mix_q
     [Hq,D,D], mix_k [Hkv,D,D]; row c is output channel c), plus the group's
     pre-convolution query/key mean; RoPE of the result when theta > 0; and
@@ -384,9 +384,9 @@ def cca_mix(q: np.ndarray, k: np.ndarray, v: np.ndarray, conv_q: np.ndarray, con
                                              (q, k, v, conv_q, conv_k, mix_q, mix_k))
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
-    W = conv_q.shape[-1]
+    W = conv_q.shape[1]
     if (k.shape != (B, Hkv, S, D) or v.shape != k.shape or Hq % Hkv or D % 2
-            or conv_q.shape != (Hq, D, W) or conv_k.shape != (Hkv, D, W)
+            or conv_q.shape != (Hq, W, D) or conv_k.shape != (Hkv, W, D)
             or mix_q.shape != (Hq, D, D) or mix_k.shape != (Hkv, D, D)):
         raise ValueError("bad shapes")
     off = None

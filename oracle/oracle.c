@@ -609,7 +609,7 @@ int oracle_prefill_backward(double *dq, double *dk, double *dv, const void *q, c
  *
  *  (2a) sequence mixing: a causal depthwise convolution over the sequence, of
  *       width W, per channel c of every head:
- *           s[t, c] = sum_{i < W, t - i >= 0} conv[h, c, i] * x[t - i, c]
+ *           s[t, c] = sum_{i < W, t - i >= 0} conv[h, i, c] * x[t - i, c]
  *       (tap i weighs the token i steps back; tokens before the first are 0);
  *  (2b) channel mixing within a head: a dense D x D map per head,
  *           z[t, c] = sum_{c'} mix[h, c, c'] * s[t, c'];
@@ -624,7 +624,7 @@ int oracle_prefill_backward(double *dq, double *dk, double *dv, const void *q, c
  *  (3)  value shift: each head's values come half from the current token and
  *       half from the previous one: v[t, c] = v~[t, c] for c < D/2 and
  *       v~[t - 1, c] for c >= D/2 (0 at t = 0).
- * conv_q [Hq, D, W], conv_k [Hkv, D, W], mix_q [Hq, D, D], mix_k [Hkv, D, D]
+ * conv_q [Hq, W, D], conv_k [Hkv, W, D] (tap-major), mix_q [Hq, D, D], mix_k [Hkv, D, D]
  * (row c of mix is output channel c) share the inputs' element type dt.
  * Outputs are fp64 [B, Hq, S, D], [B, Hkv, S, D], [B, Hkv, S, D]. */
 int oracle_cca_mix(double *q_out, double *k_out, double *v_out, const void *q, const void *k,
@@ -672,7 +672,7 @@ int oracle_cca_mix(double *q_out, double *k_out, double *v_out, const void *q, c
                             int src = t - i;
                             if (src < 0)
                                 continue;
-                            acc += load(cw, ((size_t)h * D + c) * W + i, dt) *
+                            acc += load(cw, ((size_t)h * W + i) * D + c, dt) *
                                    load(x, (((size_t)b * H + h) * S + src) * D + c, dt);
                         }
                         conv[c] = acc;

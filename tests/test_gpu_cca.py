@@ -160,7 +160,7 @@ def test_cca_mix_errors():
     with pytest.raises(attn.AttnError) as e:
         attn.cca_mix(q.float(), k.float(), v.float(), cq.float(), ck.float(), mq.float(), mk.float())
     assert e.value.status == 3
-    wide = torch.zeros(4, 64, 9, dtype=torch.bfloat16, device=DEV)
+    wide = torch.zeros(4, 9, 64, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(attn.AttnError) as e:
-        attn.cca_mix(q, k, v, wide, torch.zeros(2, 64, 9, dtype=torch.bfloat16, device=DEV), mq, mk)
+        attn.cca_mix(q, k, v, wide, torch.zeros(2, 9, 64, dtype=torch.bfloat16, device=DEV), mq, mk)
     assert e.value.status == 3

@@ -59,8 +59,8 @@ MUTANTS = {
     "rope_transpose_is_the_rotation": ("out[at + 2 * j] = g0 * ca + g1 * sa;",
                                        "out[at + 2 * j] = g0 * ca - g1 * sa;"),
     "rope_transpose_ignores_offset": ("(double)(base + t) * pow", "(double)(t) * pow"),
-    "cca_conv_taps_reversed": ("acc += load(cw, ((size_t)h * D + c) * W + i, dt) *",
-                               "acc += load(cw, ((size_t)h * D + c) * W + (W - 1 - i), dt) *"),
+    "cca_conv_taps_reversed": ("acc += load(cw, ((size_t)h * W + i) * D + c, dt) *",
+                               "acc += load(cw, ((size_t)h * W + (W - 1 - i)) * D + c, dt) *"),
     "cca_conv_wraps_around": ("if (src < 0)\n                                continue;",
                               "if (src < 0)\n                                src += S;"),
     "cca_conv_looks_ahead": ("int src = t - i;", "int src = t + i < S ? t + i : -1;"),

@@ -742,8 +742,8 @@ def test_rope_transpose_turns_pair_zero_back_by_the_position():
 def _cca_inputs(B, Hq, Hkv, S, D, W, seed):
     g = np.random.default_rng(seed)
     return (g.standard_normal((B, Hq, S, D)), g.standard_normal((B, Hkv, S, D)),
-            g.standard_normal((B, Hkv, S, D)), g.standard_normal((Hq, D, W)),
-            g.standard_normal((Hkv, D, W)), g.standard_normal((Hq, D, D)),
+            g.standard_normal((B, Hkv, S, D)), g.standard_normal((Hq, W, D)),
+            g.standard_normal((Hkv, W, D)), g.standard_normal((Hq, D, D)),
             g.standard_normal((Hkv, D, D)))
 
 
@@ -751,13 +751,13 @@ def _cca_brute(q, k, v, cq, ck, mq, mk, theta=0.0):
     """The three operations written out in pure Python loops (no numpy in the
     arithmetic), RoPE with math.cos / math.sin on adjacent pairs."""
     B, Hq, S, D = q.shape
-    Hkv, W = k.shape[1], cq.shape[-1]
+    Hkv, W = k.shape[1], cq.shape[1]
     G = Hq // Hkv
     ql, kl, vl = q.tolist(), k.tolist(), v.tolist()
     cql, ckl, mql, mkl = cq.tolist(), ck.tolist(), mq.tolist(), mk.tolist()
 
     def head(x, cw, mw, mean, b, h, t):
-        s = [sum(cw[h][c][i] * x[b][h][t - i][c] for i in range(W) if t - i >= 0) for c in range(D)]
+        s = [sum(cw[h][i][c] * x[b][h][t - i][c] for i in range(W) if t - i >= 0) for c in range(D)]
         z = [sum(mw[h][c][c2] * s[c2] for c2 in range(D)) + mean[c] for c in range(D)]
         if theta > 0:
             for i in range(D // 2):
@@ -805,10 +805,10 @@ def test_cca_sequence_convolution_is_a_causal_depthwise_conv1d():
     qo, ko, _ = oracle.cca_mix(q, k, v, cq, ck, eye_q, eye_k)
     mean = 0.5 * (q + k)  # G = 1: each query head's own key head
 
-    def conv(x, w):  # x [B,H,S,D], w [H,D,W] -> [B,H,S,D]
+    def conv(x, w):  # x [B,H,S,D], w [H,W,D] -> [B,H,S,D]
         H = x.shape[1]
         xt = torch.from_numpy(x).permute(0, 1, 3, 2).reshape(B, H * D, S)
-        wt = torch.from_numpy(w).reshape(H * D, 1, W).flip(-1)
+        wt = torch.from_numpy(w).permute(0, 2, 1).reshape(H * D, 1, W).flip(-1)
         y = F.conv1d(xt, wt, groups=H * D, padding=W - 1)[..., :S]
         return y.reshape(B, H, D, S).permute(0, 1, 3, 2).numpy()
 
@@ -821,7 +821,7 @@ def test_cca_channel_mix_is_a_matrix_per_head_applied_to_each_token():
     # then q - mean = mix_q[h] @ q~[t] for every token (row c = output channel)
     B, Hq, Hkv, S, D = 1, 6, 2, 5, 8
     q, k, v, _, _, mq, mk = _cca_inputs(B, Hq, Hkv, S, D, 1, 62)
-    ones_q, ones_k = np.ones((Hq, D, 1)), np.ones((Hkv, D, 1))
+    ones_q, ones_k = np.ones((Hq, 1, D)), np.ones((Hkv, 1, D))
     qo, ko, _ = oracle.cca_mix(q, k, v, ones_q, ones_k, mq, mk)
     G = Hq // Hkv
     mean_k = 0.5 * (q.reshape(B, Hkv, G, S, D).mean(axis=2) + k)
