@@ -284,7 +284,7 @@ def prefill_line(w, steps, warmup):
     tk = flops / (ms_kern * 1e-3) / 1e12
     return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
             "head_dim": w.D, "seq_len": w.S, "rope_theta": w.theta,
-            "kernel": f"prefill_bf16_kernel<{w.D},4>", "flop_per_launch": flops,
+            "kernel": f"prefill_bf16_kernel<{w.D},4,2>", "flop_per_launch": flops,
             "kernel_ms_mean": round(ms_kern, 5), "kernel_ms_min": round(kern_sorted[0], 5),
             "TFLOP_per_s": round(tk, 1), "frac_of_mfma_peak": round(tk / PEAK_BF16_TFLOPS, 4),
             "ms_per_step": round(ms_step, 5),
@@ -481,7 +481,7 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "seq_len": w.S, "rope_theta": w.theta, "causal": True,
                    "step": "rope(K) + causal GQA prefill with the query RoPE fused"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,4>",
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,4,2>",
                      "achieved": round(tflops_kern, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops_kern / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "kernel_ms_mean": round(ms_kern, 5),
