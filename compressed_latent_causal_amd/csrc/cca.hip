@@ -24,11 +24,12 @@
 // token and 8 channels per k-step.  Everything a head reads arrives by buffer
 // loads that write LDS directly, double-buffered across heads, so head n+1's
 // data streams in while head n is computed and no input lives in registers:
-// the mix matrix (swizzled for the operand reads), the conv taps, and each
-// wave's 16 rows plus the 8 before them (swizzled so that 16 lanes reading 16
-// consecutive rows hit distinct banks).  Every load is issued by every lane
-// (a buffer resource turns reads past a tensor into zeros), so each wave waits
-// for its own loads by count and one barrier per head publishes them.  S is
+// the mix matrix (swizzled for the operand reads), the conv taps, and the
+// block's 64 rows plus the 8 before them (swizzled so that 16 lanes reading 16
+// consecutive rows hit distinct banks; the waves split the copies).  Every
+// load is issued by every lane of its wave (a buffer resource turns reads past
+// a tensor into zeros), so each wave waits for its own loads by count and one
+// barrier per head publishes them.  S is
 // split into bf16 high and low parts and both are multiplied, so the product is
 // accurate to about 2^-17 of its terms: the result is the fp32-accurate value,
 // rounded once to bf16.  In the result layout each lane holds 4 consecutive
@@ -47,7 +48,7 @@ constexpr int CM_NW = 4;               // waves per workgroup
 constexpr int CM_TW = 16;              // tokens per wave
 constexpr int CM_TB = CM_NW * CM_TW;   // tokens per workgroup
 constexpr int CM_MAXW = 8;             // widest sequence convolution
-constexpr int CM_PREV = 8;             // rows kept before a wave's first token (CM_MAXW - 1 needed)
+constexpr int CM_PREV = 8;             // rows kept before a block's first token (CM_MAXW - 1 needed)
 
 // s_waitcnt immediate: vmcnt(n) and lgkmcnt(0)
 constexpr int wait_vmcnt_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
@@ -57,8 +58,9 @@ struct CcaLayout {
     static constexpr int ROW = D * 2;                        // bytes per bf16 row
     static constexpr int MBYTES = D * ROW;                   // one head's mix matrix
     static constexpr int MINST = MBYTES / 1024 / CM_NW;      // its 1 KiB copies per wave
-    static constexpr int XBYTES = (CM_TW + CM_PREV) * ROW;   // one wave's input rows
+    static constexpr int XBYTES = (CM_TB + CM_PREV) * ROW;   // the block's input rows
     static constexpr int XINST = XBYTES / 1024;              // their 1 KiB copies
+    static constexpr int XPW = (XINST + CM_NW - 1) / CM_NW;  // copies per wave, at most
     static constexpr int CBYTES = CM_MAXW * ROW;             // one head's taps, at most
     static constexpr int CINST = CBYTES / 1024;              // copies (one per wave)
     static_assert(MINST >= 1 && XBYTES % 1024 == 0 && CBYTES % 1024 == 0 && CINST <= CM_NW,
@@ -66,7 +68,7 @@ struct CcaLayout {
 };
 
 // Tap I of the sequence convolution for this lane's token (row CM_PREV + r of
-// the wave's rows) and channels 32 s + 8 g + e: y += w[I][c] x[t - I, c], with
+// the block's rows) and channels 32 s + 8 g + e: y += w[I][c] x[t - I, c], with
 // the taps [W][D] and the rows (swz_k layout) in LDS.
 template <int D, int I>
 __device__ __attribute__((always_inline)) inline void conv_tap(float (&y)[D / 32][8], const char* xs,
@@ -83,8 +85,13 @@ __device__ __attribute__((always_inline)) inline void conv_tap(float (&y)[D / 32
     }
 }
 
+// Four workgroups share a CU at D = 64 (36 KiB of LDS each), so a launch over
+// 1024 blocks runs in one round.
 template <int D>
-__global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
+constexpr int cca_waves_per_simd() { return D == 64 ? 4 : 1; }
+
+template <int D>
+__global__ __launch_bounds__(CM_NW * 64, cca_waves_per_simd<D>()) void cca_mix_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ qo, uint16_t* __restrict__ ko, uint16_t* __restrict__ vo,
     const uint16_t* __restrict__ conv_q, const uint16_t* __restrict__ conv_k, int W,
@@ -100,8 +107,8 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
     // compiler can tell the buffer being filled from the one being read
     __shared__ __attribute__((aligned(1024))) char msm0[L::MBYTES];
     __shared__ __attribute__((aligned(1024))) char msm1[L::MBYTES];
-    __shared__ __attribute__((aligned(1024))) char xsm0[CM_NW * L::XBYTES];
-    __shared__ __attribute__((aligned(1024))) char xsm1[CM_NW * L::XBYTES];
+    __shared__ __attribute__((aligned(1024))) char xsm0[L::XBYTES];
+    __shared__ __attribute__((aligned(1024))) char xsm1[L::XBYTES];
     __shared__ __attribute__((aligned(1024))) char csm0[L::CBYTES];
     __shared__ __attribute__((aligned(1024))) char csm1[L::CBYTES];
 
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
     // puts lane l's 16 bytes at byte 16 l of a 1 KiB destination, i.e. at
     // physical chunk pc of row pr; the swizzle is produced by fetching the
     // logical chunk that belongs there (the XOR swizzle is its own inverse).
-    int moff[L::MINST], xoff[L::XINST];
+    int moff[L::MINST], xoff[L::XPW];
 #pragma unroll
     for (int u = 0; u < L::MINST; ++u) {
         const int P = (w * L::MINST + u) * 64 + lane;
@@ -143,10 +150,10 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
         moff[u] = swz_k<D>(pr, pc);
     }
 #pragma unroll
-    for (int u = 0; u < L::XINST; ++u) {
-        const int P = u * 64 + lane;
+    for (int u = 0; u < L::XPW; ++u) {  // copy w + CM_NW u of the block's rows
+        const int P = (w + CM_NW * u) * 64 + lane;
         const int pr = P / (D / 8), pc = P % (D / 8);
-        const int tok = t0w - CM_PREV + pr;  // rows before the first token read zeros
+        const int tok = tblk * CM_TB - CM_PREV + pr;  // rows before the first token read zeros
         xoff[u] = tok >= 0 ? tok * ROW + (swz_k<D>(pr, pc) - pr * ROW) : -16;
     }
 
@@ -157,7 +164,8 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
         for (int u = 0; u < L::MINST; ++u) dma16(mrs, msm + (w * L::MINST + u) * 1024, moff[u], 0);
         const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(head_rows(n), S * ROW);
 #pragma unroll
-        for (int u = 0; u < L::XINST; ++u) dma16(xrs, xsm + w * L::XBYTES + u * 1024, xoff[u], 0);
+        for (int u = 0; u < L::XPW; ++u)
+            if (w + CM_NW * u < L::XINST) dma16(xrs, xsm + (w + CM_NW * u) * 1024, xoff[u], 0);
         if (w < L::CINST) {  // the taps [W][D]: past W * D they read zeros
             const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(head_conv(n), W * D * 2);
             dma16(crs, csm + w * 1024, lane * 16, w * 1024);
@@ -253,20 +261,21 @@ __global__ __launch_bounds__(CM_NW * 64, 2) void cca_mix_kernel(
         __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of this head's work
 
         // S^T fragments: y[s][e] = channel 32 s + 8 g + e of token t
-        const char* const xs = xsm + w * L::XBYTES;
+        const char* const xs = xsm;
+        const int rb = CM_TW * w + r;  // the token's row among the block's
         float y[KS][8];
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[s][e] = 0.f;
-        conv_tap<D, 0>(y, xs, csm, r, g);
-        if (W > 1) conv_tap<D, 1>(y, xs, csm, r, g);
-        if (W > 2) conv_tap<D, 2>(y, xs, csm, r, g);
-        if (W > 3) conv_tap<D, 3>(y, xs, csm, r, g);
-        if (W > 4) conv_tap<D, 4>(y, xs, csm, r, g);
-        if (W > 5) conv_tap<D, 5>(y, xs, csm, r, g);
-        if (W > 6) conv_tap<D, 6>(y, xs, csm, r, g);
-        if (W > 7) conv_tap<D, 7>(y, xs, csm, r, g);
+        conv_tap<D, 0>(y, xs, csm, rb, g);
+        if (W > 1) conv_tap<D, 1>(y, xs, csm, rb, g);
+        if (W > 2) conv_tap<D, 2>(y, xs, csm, rb, g);
+        if (W > 3) conv_tap<D, 3>(y, xs, csm, rb, g);
+        if (W > 4) conv_tap<D, 4>(y, xs, csm, rb, g);
+        if (W > 5) conv_tap<D, 5>(y, xs, csm, rb, g);
+        if (W > 6) conv_tap<D, 6>(y, xs, csm, rb, g);
+        if (W > 7) conv_tap<D, 7>(y, xs, csm, rb, g);
         // bf16 high and low parts of S^T
         bf16x8_t yh[KS], yl[KS];
 #pragma unroll
