@@ -94,6 +94,8 @@ MIX_CASES = [  # B, Hq, Hkv, S, D, width, theta, pos_offset
     (2, 6, 2, 17, 128, 2, 0.0, None),      # G = 3, shorter than one workgroup
     (1, 8, 2, 1, 64, 4, 1e4, None),        # one token
     (1, 2, 1, 15, 128, 7, 5e5, [131000]),  # shorter than one wave, large positions
+    (1, 10, 2, 70, 64, 3, 1e4, None),      # G = 5
+    (1, 12, 2, 150, 64, 4, 1e4, [3]),      # G = 6, two query-head batches in the mean
 ]
 
 
