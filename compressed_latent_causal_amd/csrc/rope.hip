@@ -43,25 +43,40 @@ __global__ __launch_bounds__(256) void rope_kernel(T* out, const T* in, int H, i
     const int h_begin = blockIdx.z * HB, h_end = min(H, h_begin + HB);
     if (s >= S) return;
 
+    const size_t head_stride = (size_t)S * D;
+    const size_t off = ((size_t)b * H * S + s) * D + (size_t)c * EPT;
+    // Heads are processed in groups of eight whose loads are all issued before
+    // any store, so the loads overlap; each thread touches only its own chunk
+    // of each head, so this order is also correct when out == in.  The first
+    // group's loads are issued before the angles are formed, so the sine and
+    // cosine work overlaps their latency.
+    constexpr int HG = 8;
+    u32x4_t x[HG];
+    auto load = [&](int h0) __attribute__((always_inline)) {
+        // every lane issues all HG loads (heads past the block re-read its
+        // last head and are not stored), so the loads' count is fixed and the
+        // waits for them can be counted
+#pragma unroll
+        for (int u = 0; u < HG; ++u)
+            x[u] = *(const u32x4_t*)(in + off + (size_t)min(h0 + u, h_end - 1) * head_stride);
+    };
+    // the frequencies and the position first: their loads then complete
+    // before the data loads, and the angles need not wait for the data
+    double fq[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) fq[j] = fr.f[c * PPT + j];
     const long long p = (long long)(pos_offset ? pos_offset[b] : 0) + pos_shift + s;
+    load(h_begin);
+
     float cs[PPT], sn[PPT];
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-        rope_cos_sin(p, fr.f[c * PPT + j], cs[j], sn[j]);
+        rope_cos_sin(p, fq[j], cs[j], sn[j]);
         if (transpose) sn[j] = -sn[j];
     }
 
-    const size_t head_stride = (size_t)S * D;
-    const size_t off = ((size_t)b * H * S + s) * D + (size_t)c * EPT;
-    // Heads are processed in groups of four whose loads are all issued before
-    // any store, so the loads overlap; each thread touches only its own chunk
-    // of each head, so this order is also correct when out == in.
-    constexpr int HG = 4;
     for (int h0 = h_begin; h0 < h_end; h0 += HG) {
-        u32x4_t x[HG];
-#pragma unroll
-        for (int u = 0; u < HG; ++u)
-            if (h0 + u < h_end) x[u] = *(const u32x4_t*)(in + off + (size_t)(h0 + u) * head_stride);
+        if (h0 != h_begin) load(h0);
 #pragma unroll
         for (int u = 0; u < HG; ++u) {
             if (h0 + u >= h_end) break;
