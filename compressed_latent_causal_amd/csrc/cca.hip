@@ -111,6 +111,9 @@ __global__ __launch_bounds__(CM_NW * 64, cca_waves_per_simd<D>()) void cca_mix_k
     __shared__ __attribute__((aligned(1024))) char xsm1[L::XBYTES];
     __shared__ __attribute__((aligned(1024))) char csm0[L::CBYTES];
     __shared__ __attribute__((aligned(1024))) char csm1[L::CBYTES];
+    // destination of the copies a wave issues only so that every wave issues
+    // the same number (they read past their buffer: zeros, no memory access)
+    __shared__ __attribute__((aligned(1024))) char dummy[1024];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -164,12 +167,14 @@ __global__ __launch_bounds__(CM_NW * 64, cca_waves_per_simd<D>()) void cca_mix_k
         for (int u = 0; u < L::MINST; ++u) dma16(mrs, msm + (w * L::MINST + u) * 1024, moff[u], 0);
         const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(head_rows(n), S * ROW);
 #pragma unroll
-        for (int u = 0; u < L::XPW; ++u)
-            if (w + CM_NW * u < L::XINST) dma16(xrs, xsm + (w + CM_NW * u) * 1024, xoff[u], 0);
-        if (w < L::CINST) {  // the taps [W][D]: past W * D they read zeros
-            const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(head_conv(n), W * D * 2);
-            dma16(crs, csm + w * 1024, lane * 16, w * 1024);
+        for (int u = 0; u < L::XPW; ++u) {
+            const bool real = w + CM_NW * u < L::XINST;  // wave-uniform: a select, not a branch
+            dma16(xrs, real ? xsm + (w + CM_NW * u) * 1024 : dummy, real ? xoff[u] : -16, 0);
         }
+        // the taps [W][D] (past W * D they read zeros), CINST copies
+        const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(head_conv(n), W * D * 2);
+        const bool tap = w < L::CINST;
+        dma16(crs, tap ? csm + w * 1024 : dummy, tap ? lane * 16 : -16, tap ? w * 1024 : 0);
     };
     // the value shift's loads (issued during the last head): the workgroup's
     // 64 rows x D/8 chunks, KS per thread (zero for the row before the first)
@@ -188,56 +193,71 @@ __global__ __launch_bounds__(CM_NW * 64, cca_waves_per_simd<D>()) void cca_mix_k
         }
     };
 
+    // ---- prologue.  Loads in this order: the RoPE frequencies and the
+    // position, the first head's copies, the mean's rows; every one issued by
+    // every lane, so the count behind each is fixed and the angle arithmetic
+    // waits only for the frequencies, running while the rest is in flight.
+    double fq[MT][2];  // frequencies of the token's channel pairs 8 mt + 2 g + e
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) fq[mt][e] = fr.f[8 * mt + 2 * g + e];
+    const long long p = (long long)(pos_offset ? pos_offset[b] : 0) + t;
+
     issue(0, msm0, xsm0, csm0);
 
-    // ---- the token's QK-mean (result layout: channels 16 mt + 4 g + i) and,
-    // with RoPE, the cosines and sines of its channel pairs
-    f32x4_t mean[MT];
-    {
-        f32x4_t qs[MT];
+    // the token's rows of the group's first four query heads and of its key
+    // head (result layout: channels 16 mt + 4 g + i; heads past G re-read the
+    // last one and weigh nothing)
+    const size_t trow = (size_t)min(t, S - 1) * D + 4 * g;
+    u32x2_t xq[4][MT], xk[MT];
+    auto load_q = [&](int h0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) qs[mt] = f32x4_t{0, 0, 0, 0};
-        // query heads four at a time, all loads of a batch issued before any
-        // is used (heads past G re-read the last one and weigh nothing)
-        const size_t trow = (size_t)min(t, S - 1) * D + 4 * g;
-        for (int h0 = 0; h0 < G; h0 += 4) {
-            u32x2_t x[4][MT];
+        for (int u = 0; u < 4; ++u) {
+            const uint16_t* const xr = head_rows(min(h0 + u, G - 1)) + trow;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint16_t* const xr = head_rows(min(h0 + u, G - 1)) + trow;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) x[u][mt] = *(const u32x2_t*)(xr + 16 * mt);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float f = h0 + u < G ? 1.f : 0.f;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    qs[mt] += f * f32x4_t{bf16_lo(x[u][mt][0]), bf16_hi(x[u][mt][0]),
-                                          bf16_lo(x[u][mt][1]), bf16_hi(x[u][mt][1])};
-            }
+            for (int mt = 0; mt < MT; ++mt) xq[u][mt] = *(const u32x2_t*)(xr + 16 * mt);
         }
-        const float inv_g = 1.f / (float)G;
+    };
+    load_q(0);
+    {
         const uint16_t* const kr = head_rows(G) + trow;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const u32x2_t x = *(const u32x2_t*)(kr + 16 * mt);
-            const f32x4_t kv = {bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1])};
-            mean[mt] = 0.5f * (qs[mt] * inv_g + kv);
-        }
+        for (int mt = 0; mt < MT; ++mt) xk[mt] = *(const u32x2_t*)(kr + 16 * mt);
     }
+
+    // with RoPE, the cosines and sines of the token's channel pairs
     float cs[MT][2], sn[MT][2];
     if (rope) {
-        const long long p = (long long)(pos_offset ? pos_offset[b] : 0) + t;
-        double fq[MT][2];  // gathered first, so the loads overlap
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) fq[mt][e] = fr.f[8 * mt + 2 * g + e];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int e = 0; e < 2; ++e) rope_cos_sin(p, fq[mt][e], cs[mt][e], sn[mt][e]);
+    }
+
+    // the QK-mean
+    f32x4_t mean[MT];
+    {
+        auto widen = [](u32x2_t x) {
+            return f32x4_t{bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1])};
+        };
+        f32x4_t qs[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) qs[mt] = f32x4_t{0, 0, 0, 0};
+        for (int h0 = 0;;) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float f = h0 + u < G ? 1.f : 0.f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) qs[mt] += f * widen(xq[u][mt]);
+            }
+            h0 += 4;
+            if (h0 >= G) break;
+            load_q(h0);  // groups of more than four query heads
+        }
+        const float inv_g = 1.f / (float)G;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) mean[mt] = 0.5f * (qs[mt] * inv_g + widen(xk[mt]));
     }
 
     // ---- one head: convolution, channel mix, mean, RoPE, store
