@@ -17,6 +17,8 @@ fallback: calling into the library without the built ``libattn.so`` raises.
     decode_workspace_size(B, Hq, Hkv, max_len, D)
     cca_mix(q, k, v, conv_q, conv_k, mix_q, mix_k, rope_theta=0.0, pos_offset=None,
             q_out=None, k_out=None, v_out=None)
+    cca_mix_decode(q, k, v, conv_q, conv_k, mix_q, mix_k, t, q_state, k_state, v_state,
+                   rope_theta=0.0, pos_offset=None, q_out=None, k_out=None, v_out=None)
 
 Shapes follow the C ABI: x [B,H,S,D]; q/o [B,Hq,S,D], k/v [B,Hkv,S,D];
 decode q/o [B,Hq,D], caches [B,Hkv,S_cap,D], seqlens int32 [B] on the device.
@@ -344,4 +346,56 @@ def cca_mix(q, k, v, conv_q, conv_k, mix_q, mix_k, rope_theta: float = 0.0, pos_
           k.data_ptr(), v.data_ptr(), _dtype_code(q), B, Hq, Hkv, S, D, conv_q.data_ptr(),
           conv_k.data_ptr(), W, mix_q.data_ptr(), mix_k.data_ptr(), po, float(rope_theta),
           _stream(q))
+    return q_out, k_out, v_out
+
+
+def cca_mix_decode(q, k, v, conv_q, conv_k, mix_q, mix_k, t, q_state, k_state, v_state,
+                   rope_theta: float = 0.0, pos_offset=None, q_out=None, k_out=None, v_out=None):
+    """cca_mix for one new token per sequence (decode): q [B,Hq,D], k, v [B,Hkv,D]
+    (bf16) of token t[b] (int32 [B]), with the convolution's reach as state:
+    q_state [B,Hq,W-1,D] and k_state [B,Hkv,W-1,D] rings (token u in slot
+    u mod (W-1)), v_state [B,Hkv,D] (the previous token's v).  The state is read,
+    then updated in place with this token's rows.  Returns (q_out, k_out, v_out),
+    row t of cca_mix over the sequence."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q [B,Hq,D], k and v [B,Hkv,D]")
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != D:
+        raise ValueError("q [B,Hq,D], k and v [B,Hkv,D]")
+    W = conv_q.shape[1] if conv_q.dim() == 3 else -1
+    if (conv_q.shape != (Hq, W, D) or conv_k.shape != (Hkv, W, D) or mix_q.shape != (Hq, D, D)
+            or mix_k.shape != (Hkv, D, D)):
+        raise ValueError("conv_q [Hq,W,D], conv_k [Hkv,W,D], mix_q [Hq,D,D], mix_k [Hkv,D,D]")
+    if any(x.dtype != q.dtype for x in (k, v, conv_q, conv_k, mix_q, mix_k, v_state)):
+        raise ValueError("all tensors share one dtype")
+    if v_state.shape != (B, Hkv, D):
+        raise ValueError("v_state [B,Hkv,D]")
+    qs = ks = 0
+    if W > 1:
+        if q_state.shape != (B, Hq, W - 1, D) or k_state.shape != (B, Hkv, W - 1, D):
+            raise ValueError("q_state [B,Hq,W-1,D], k_state [B,Hkv,W-1,D]")
+        if q_state.dtype != q.dtype or k_state.dtype != q.dtype:
+            raise ValueError("all tensors share one dtype")
+        _check_dev(q_state, k_state)
+        qs, ks = q_state.data_ptr(), k_state.data_ptr()
+    if t.dtype != torch.int32 or t.shape != (B,):
+        raise ValueError("t must be int32 [B]")
+    po = 0
+    if pos_offset is not None:
+        if pos_offset.dtype != torch.int32 or pos_offset.shape != (B,):
+            raise ValueError("pos_offset must be int32 [B]")
+        _check_dev(pos_offset)
+        po = pos_offset.data_ptr()
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    v_out = torch.empty_like(v) if v_out is None else v_out
+    if q_out.shape != q.shape or k_out.shape != k.shape or v_out.shape != v.shape:
+        raise ValueError("outputs must match q, k, v")
+    _check_dev(q, k, v, conv_q, conv_k, mix_q, mix_k, v_state, t, q_out, k_out, v_out)
+    _call(lib().attn_cca_mix_decode, q_out.data_ptr(), k_out.data_ptr(), v_out.data_ptr(),
+          q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, Hq, Hkv, D,
+          conv_q.data_ptr(), conv_k.data_ptr(), W, mix_q.data_ptr(), mix_k.data_ptr(), qs, ks,
+          v_state.data_ptr(), t.data_ptr(), po, float(rope_theta), _stream(q))
     return q_out, k_out, v_out

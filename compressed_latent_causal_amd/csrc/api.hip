@@ -223,6 +223,34 @@ ATTN_API int attn_cca_mix(void* q_out, void* k_out, void* v_out, const void* q, 
                                            rope_theta, (hipStream_t)stream));
 }
 
+ATTN_API int attn_cca_mix_decode(void* q_out, void* k_out, void* v_out, const void* q,
+                                 const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
+                                 int D, const void* conv_q, const void* conv_k, int conv_width,
+                                 const void* mix_q, const void* mix_k, void* q_state,
+                                 void* k_state, void* v_state, const int32_t* t,
+                                 const int32_t* pos_offset, double rope_theta, void* stream) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_BF16 || !supported_dim(D)) return ATTN_ERR_UNSUPPORTED;
+    if (conv_width < 1 || conv_width > attn::cca_max_width()) return ATTN_ERR_UNSUPPORTED;
+    if (!(rope_theta >= 0.0) || !isfinite(rope_theta)) return ATTN_ERR_UNSUPPORTED;
+    // one workgroup per (sequence, KV group), the group's convolved rows in LDS
+    if (attn::cca_decode_lds_bytes(Hq / Hkv, D) > 64 * 1024) return ATTN_ERR_UNSUPPORTED;
+    if (B == 0) return ATTN_OK;
+    if ((long long)B * Hkv >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    if (!q_out || !k_out || !v_out || !q || !k || !v || !conv_q || !conv_k || !mix_q || !mix_k ||
+        !v_state || !t || (conv_width > 1 && (!q_state || !k_state)))
+        return ATTN_ERR_NULL;
+    if (!aligned16(q_out) || !aligned16(k_out) || !aligned16(v_out) || !aligned16(q) ||
+        !aligned16(k) || !aligned16(v) || !aligned16(mix_q) || !aligned16(mix_k) ||
+        !aligned16(conv_q) || !aligned16(conv_k) || !aligned16(q_state) || !aligned16(k_state) ||
+        !aligned16(v_state) || ((uintptr_t)t & 3u) || ((uintptr_t)pos_offset & 3u))
+        return ATTN_ERR_ALIGN;
+    return hip_status(attn::launch_cca_decode(q_out, k_out, v_out, q, k, v, B, Hq, Hkv, D, conv_q,
+                                              conv_k, conv_width, mix_q, mix_k, q_state, k_state,
+                                              v_state, t, pos_offset, rope_theta,
+                                              (hipStream_t)stream));
+}
+
 ATTN_API const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";

@@ -373,6 +373,131 @@ hipError_t launch_cca_mix_d(void* q_out, void* k_out, void* v_out, const void* q
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- decode step
+// The same operations for one new token per sequence (token index t[b] of its
+// sequence, RoPE position pos_offset[b] + t[b]), with the earlier tokens the
+// convolution reaches kept as state: the last W - 1 pre-convolution rows of
+// every q and k head, token u in ring slot u mod (W - 1), and the previous
+// token's v row.  The step reads the state, then writes this token's rows
+// into it, so the next step finds them.  Its output equals row t of the
+// prefill pass over the sequence.
+//
+// One workgroup per (sequence, KV group): first each thread convolves (head,
+// channel) pairs in fp32 into LDS, forms the group's mean, shifts v and
+// updates the state; then each thread takes (head, output channel pair)
+// items: the row of the mix matrix times the convolved vector in fp32, plus
+// the mean, rotated, rounded once to bf16.  A decode step moves a few
+// kilobytes per head, so the kernel is kept simple: its time is launch and
+// latency, far below the attention's cache read.
+constexpr int CD_THREADS = 256;
+
+template <int D>
+__global__ __launch_bounds__(CD_THREADS) void cca_decode_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ qo, uint16_t* __restrict__ ko, uint16_t* __restrict__ vo,
+    const uint16_t* __restrict__ conv_q, const uint16_t* __restrict__ conv_k, int W,
+    const uint16_t* __restrict__ mix_q, const uint16_t* __restrict__ mix_k,
+    uint16_t* __restrict__ q_state, uint16_t* __restrict__ k_state, uint16_t* __restrict__ v_state,
+    const int32_t* __restrict__ tok, const int32_t* __restrict__ pos_offset, int rope,
+    RopeFreqs fr, int Hq, int Hkv) {
+    extern __shared__ __attribute__((aligned(16))) float sm[];  // [NH][D] convolved, then [D] mean
+    const int tid = threadIdx.x;
+    const int b = (int)blockIdx.x / Hkv, j = (int)blockIdx.x % Hkv;
+    const int G = Hq / Hkv, NH = G + 1;
+    const int t = tok[b];
+    const int R = W - 1;  // state rows per head
+    float* const mean = sm + NH * D;
+
+    // head n of the group: its input row, state rows, taps and output row
+    auto in_row = [&](int n) -> const uint16_t* {
+        return n < G ? q + ((size_t)b * Hq + (size_t)j * G + n) * D : k + ((size_t)b * Hkv + j) * D;
+    };
+    auto state_rows = [&](int n) -> uint16_t* {
+        return n < G ? q_state + ((size_t)b * Hq + (size_t)j * G + n) * R * D
+                     : k_state + ((size_t)b * Hkv + j) * R * D;
+    };
+    auto taps = [&](int n) -> const uint16_t* {
+        return n < G ? conv_q + ((size_t)j * G + n) * W * D : conv_k + (size_t)j * W * D;
+    };
+    auto bf = [](uint16_t x) { return __uint_as_float((unsigned)x << 16); };
+
+    // ---- convolution of every (head, channel) and the state update.  Each
+    // element of the state is read and then rewritten by the same thread.
+    for (int e = tid; e < NH * D; e += CD_THREADS) {
+        const int n = e / D, c = e % D;
+        const uint16_t* const w = taps(n);
+        uint16_t* const st = state_rows(n);
+        const uint16_t x0 = in_row(n)[c];
+        float y = bf(w[c]) * bf(x0);
+        for (int i = 1; i < W; ++i)  // tap i: token t - i, none before the first
+            if (t - i >= 0) y = fmaf(bf(w[(size_t)i * D + c]), bf(st[(size_t)((t - i) % R) * D + c]), y);
+        if (R > 0) st[(size_t)(t % R) * D + c] = x0;
+        sm[e] = y;
+    }
+    // ---- the mean and the value shift (first half from this token, second
+    // half from the previous one, zero at t = 0)
+    const float inv_g = 1.f / (float)G;
+    for (int c = tid; c < D; c += CD_THREADS) {
+        float sq = 0.f;
+        for (int n = 0; n < G; ++n) sq += bf(in_row(n)[c]);
+        mean[c] = 0.5f * (sq * inv_g + bf(in_row(G)[c]));
+        const size_t vr = ((size_t)b * Hkv + j) * D + c;
+        const uint16_t cur = v[vr];
+        vo[vr] = c < D / 2 ? cur : (t >= 1 ? v_state[vr] : (uint16_t)0);
+        v_state[vr] = cur;
+    }
+    __syncthreads();
+
+    // ---- channel mix, mean, RoPE: item (head n, channel pair cp)
+    const long long p = (long long)(pos_offset ? pos_offset[b] : 0) + t;
+    for (int e = tid; e < NH * (D / 2); e += CD_THREADS) {
+        const int n = e / (D / 2), cp = e % (D / 2), c = 2 * cp;
+        const uint16_t* const m = n < G ? mix_q + ((size_t)j * G + n) * D * D : mix_k + (size_t)j * D * D;
+        const float* const sv = sm + n * D;
+        float z0 = 0.f, z1 = 0.f;
+        for (int c2 = 0; c2 < D; c2 += 8) {
+            const u32x4_t r0 = *(const u32x4_t*)(m + (size_t)c * D + c2);
+            const u32x4_t r1 = *(const u32x4_t*)(m + (size_t)(c + 1) * D + c2);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                z0 = fmaf(bf16_lo(r0[u]), sv[c2 + 2 * u], z0);
+                z0 = fmaf(bf16_hi(r0[u]), sv[c2 + 2 * u + 1], z0);
+                z1 = fmaf(bf16_lo(r1[u]), sv[c2 + 2 * u], z1);
+                z1 = fmaf(bf16_hi(r1[u]), sv[c2 + 2 * u + 1], z1);
+            }
+        }
+        z0 += mean[c];
+        z1 += mean[c + 1];
+        if (rope) {
+            float cs, sn, y0, y1;
+            rope_cos_sin(p, fr.f[cp], cs, sn);
+            rope_rotate(z0, z1, cs, sn, y0, y1);
+            z0 = y0;
+            z1 = y1;
+        }
+        uint16_t* const out = n < G ? qo + ((size_t)b * Hq + (size_t)j * G + n) * D
+                                    : ko + ((size_t)b * Hkv + j) * D;
+        *(uint32_t*)(out + c) = pack_bf16x2(z0, z1);
+    }
+}
+
+template <int D>
+hipError_t launch_cca_decode_d(void* q_out, void* k_out, void* v_out, const void* q, const void* k,
+                               const void* v, int B, int Hq, int Hkv, const void* conv_q,
+                               const void* conv_k, int W, const void* mix_q, const void* mix_k,
+                               void* q_state, void* k_state, void* v_state, const int32_t* tok,
+                               const int32_t* pos_offset, double rope_theta, hipStream_t st) {
+    const size_t lds = (size_t)(Hq / Hkv + 2) * D * sizeof(float);
+    hipLaunchKernelGGL((cca_decode_kernel<D>), dim3((unsigned)(B * Hkv)), dim3(CD_THREADS), lds, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)q_out,
+                       (uint16_t*)k_out, (uint16_t*)v_out, (const uint16_t*)conv_q,
+                       (const uint16_t*)conv_k, W, (const uint16_t*)mix_q, (const uint16_t*)mix_k,
+                       (uint16_t*)q_state, (uint16_t*)k_state, (uint16_t*)v_state, tok, pos_offset,
+                       rope_theta > 0 ? 1 : 0, rope_freqs(rope_theta > 0 ? rope_theta : 1.0, D), Hq,
+                       Hkv);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int cca_max_width() { return CM_MAXW; }
@@ -385,6 +510,21 @@ hipError_t launch_cca_mix(void* q_out, void* k_out, void* v_out, const void* q, 
                                           conv_k, W, mix_q, mix_k, pos_offset, rope_theta, st)
                    : launch_cca_mix_d<128>(q_out, k_out, v_out, q, k, v, B, Hq, Hkv, S, conv_q,
                                            conv_k, W, mix_q, mix_k, pos_offset, rope_theta, st);
+}
+
+size_t cca_decode_lds_bytes(int G, int D) { return (size_t)(G + 2) * D * sizeof(float); }
+
+hipError_t launch_cca_decode(void* q_out, void* k_out, void* v_out, const void* q, const void* k,
+                             const void* v, int B, int Hq, int Hkv, int D, const void* conv_q,
+                             const void* conv_k, int W, const void* mix_q, const void* mix_k,
+                             void* q_state, void* k_state, void* v_state, const int32_t* tok,
+                             const int32_t* pos_offset, double rope_theta, hipStream_t st) {
+    return D == 64 ? launch_cca_decode_d<64>(q_out, k_out, v_out, q, k, v, B, Hq, Hkv, conv_q, conv_k,
+                                             W, mix_q, mix_k, q_state, k_state, v_state, tok,
+                                             pos_offset, rope_theta, st)
+                   : launch_cca_decode_d<128>(q_out, k_out, v_out, q, k, v, B, Hq, Hkv, conv_q,
+                                              conv_k, W, mix_q, mix_k, q_state, k_state, v_state,
+                                              tok, pos_offset, rope_theta, st);
 }
 
 }  // namespace attn

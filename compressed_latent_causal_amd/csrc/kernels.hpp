@@ -65,7 +65,7 @@ hipError_t launch_decode_paged(void* o, const void* q, const void* k_pages, cons
                                void* workspace, hipStream_t st);
 
 // CCA pre-attention operations (bf16): causal depthwise sequence convolution
-// of width W (conv_q [Hq, D, W], conv_k [Hkv, D, W]), channel mix per head
+// of width W (conv_q [Hq, W, D], conv_k [Hkv, W, D]), channel mix per head
 // (mix_q [Hq, D, D], mix_k [Hkv, D, D]), the group's pre-convolution
 // query/key mean, RoPE when rope_theta > 0, and the value shift.
 int cca_max_width();
@@ -73,5 +73,14 @@ hipError_t launch_cca_mix(void* q_out, void* k_out, void* v_out, const void* q, 
                           const void* v, int B, int Hq, int Hkv, int S, int D, const void* conv_q,
                           const void* conv_k, int W, const void* mix_q, const void* mix_k,
                           const int32_t* pos_offset, double rope_theta, hipStream_t st);
+// The same for one new token per sequence, the convolution's reach kept as
+// state (q_state [B, Hq, W-1, D], k_state [B, Hkv, W-1, D] rings, v_state
+// [B, Hkv, D]); dynamic LDS of cca_decode_lds_bytes(G, D).
+size_t cca_decode_lds_bytes(int G, int D);
+hipError_t launch_cca_decode(void* q_out, void* k_out, void* v_out, const void* q, const void* k,
+                             const void* v, int B, int Hq, int Hkv, int D, const void* conv_q,
+                             const void* conv_k, int W, const void* mix_q, const void* mix_k,
+                             void* q_state, void* k_state, void* v_state, const int32_t* tok,
+                             const int32_t* pos_offset, double rope_theta, hipStream_t st);
 
 }  // namespace attn

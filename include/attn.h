@@ -1,7 +1,8 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) causal grouped-query attention
- * library: rotary position embedding, causal prefill (forward and backward)
- * and single-token decode over a contiguous or a paged KV cache.
+ * library: rotary position embedding, causal prefill (forward and backward),
+ * single-token decode over a contiguous or a paged KV cache, and CCA's
+ * pre-attention operations on the compressed q, k, v (prefill and decode step).
  *
  * What is computed (pages cited by title and section):
  *  - "Grouped Query Attention (GQA)" glossary, section "Cómo funciona GQA":
@@ -26,7 +27,8 @@
  *    is enqueued on it; calls return without synchronising.  The caller keeps
  *    every buffer alive until that work completes.
  *  - The library allocates and frees nothing and keeps no state between calls
- *    (apart from a process-wide sequence number that tags each decode call);
+ *    (apart from a process-wide sequence number that tags each decode call and
+ *    the static per-device scratch behind attn_decode_noalloc);
  *    calls on different streams may run concurrently on distinct buffers.
  *  - Arguments are validated on the host before any HIP call.  On a non-zero
  *    status nothing was enqueued.  ATTN_ERR_HIP reports a failed launch (the
@@ -299,6 +301,40 @@ int attn_cca_mix(void *q_out, void *k_out, void *v_out, const void *q, const voi
                  const void *v, int dtype, int B, int Hq, int Hkv, int S, int D,
                  const void *conv_q, const void *conv_k, int conv_width, const void *mix_q,
                  const void *mix_k, const int32_t *pos_offset, double rope_theta, void *stream);
+
+/*
+ * The CCA pre-attention operations of attn_cca_mix for one new token per
+ * sequence, as a decode step needs them ("Compressed Convolutional Attention"
+ * summary, "Methodologie", items 2 to 4, in the same readings).  Token t[b]
+ * (its index in sequence b, >= 0; RoPE position pos_offset[b] + t[b]) is
+ * mixed with the tokens before it that the width-W convolution reaches,
+ * which the caller keeps as state between steps:
+ *   q_state [B, Hq, W-1, D], k_state [B, Hkv, W-1, D]: the pre-convolution
+ *     q~ and k~ rows of the previous W - 1 tokens, token u in ring slot
+ *     u mod (W - 1) (unused, and may be NULL, when W == 1);
+ *   v_state [B, Hkv, D]: the previous token's v~ row.
+ * State rows of tokens before the first (u < 0) are never read, so a new
+ * sequence needs no initialisation; after a prefill of tokens 0 .. t - 1
+ * through attn_cca_mix, the caller copies their last W - 1 q~ and k~ rows
+ * into the rings and v~[t - 1] into v_state.  The call reads the state, then
+ * writes token t's rows into it (q~[t], k~[t] into slot t mod (W - 1), v~[t]
+ * into v_state), ready for token t + 1.
+ * q~, q_out: [B, Hq, D];  k~, v~, k_out, v_out: [B, Hkv, D]; conv, mix,
+ * conv_width and rope_theta as for attn_cca_mix; t and pos_offset device
+ * int32[B] (pos_offset may be NULL).  Outputs equal row t of attn_cca_mix
+ * over the sequence up to rounding: the convolution and the channel mix are
+ * evaluated in fp32 (plain fp32 arithmetic here) and each output is rounded
+ * once to bf16.  Outputs, inputs and state must not overlap.  bf16 only;
+ * groups of more than (65536 / (4 D) - 2) query heads per KV head return
+ * ATTN_ERR_UNSUPPORTED.  Tensors are 16-byte aligned.  One kernel is
+ * enqueued.
+ */
+int attn_cca_mix_decode(void *q_out, void *k_out, void *v_out, const void *q, const void *k,
+                        const void *v, int dtype, int B, int Hq, int Hkv, int D,
+                        const void *conv_q, const void *conv_k, int conv_width, const void *mix_q,
+                        const void *mix_k, void *q_state, void *k_state, void *v_state,
+                        const int32_t *t, const int32_t *pos_offset, double rope_theta,
+                        void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *attn_status_string(int status);

@@ -303,3 +303,59 @@ def test_decode_noalloc_validation(L):
     assert ws(1, 64, 8, 131072, 128) <= _lib.DECODE_SCRATCH_BYTES
     assert ws(64, 32, 8, 8192, 128) > _lib.DECODE_SCRATCH_BYTES
     assert d(*args(B=64, Hq=32, Hkv=8, S_cap=8192, max_len=8192)) == ESCRATCH
+
+
+def test_cca_mix_decode_validation(L):
+    """The decode step of the CCA pre-attention operations: bf16 only, widths
+    1 to 8, the group's convolved rows must fit 64 KiB of LDS, and the rings
+    may be NULL only for a width of 1."""
+    d = lambda *a: L.attn_cca_mix_decode(*a)
+    args = lambda **kw: [kw.get("qo", FAKE), kw.get("ko", FAKE), kw.get("vo", FAKE),
+                         kw.get("q", FAKE), kw.get("k", FAKE), kw.get("v", FAKE),
+                         kw.get("dt", BF16), kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 2),
+                         kw.get("D", 64), kw.get("cq", FAKE), kw.get("ck", FAKE), kw.get("W", 4),
+                         kw.get("mq", FAKE), kw.get("mk", FAKE), kw.get("qs", FAKE),
+                         kw.get("ks", FAKE), kw.get("vs", FAKE), kw.get("t", FAKE),
+                         kw.get("pos", None), kw.get("theta", 1e4), None]
+    assert d(*args(Hkv=3)) == ESHAPE
+    assert d(*args(B=-1)) == ESHAPE
+    assert d(*args(dt=F32)) == EUNSUP
+    assert d(*args(D=96)) == EUNSUP
+    assert d(*args(W=0)) == EUNSUP
+    assert d(*args(W=9)) == EUNSUP
+    assert d(*args(theta=-1.0)) == EUNSUP
+    assert d(*args(theta=float("inf"))) == EUNSUP
+    # (G + 2) D 4 bytes of LDS: G = 126 fits at D = 128, G = 127 does not
+    assert d(*args(Hq=126, Hkv=1, D=128, qo=None)) == ENULL
+    assert d(*args(Hq=127, Hkv=1, D=128)) == EUNSUP
+    for name in ("qo", "ko", "vo", "q", "k", "v", "cq", "ck", "mq", "mk", "qs", "ks", "vs", "t"):
+        assert d(*args(**{name: None})) == ENULL, name
+    assert d(*args(W=1, qs=None, ks=None, qo=None)) == ENULL  # rings optional at W = 1 only
+    assert d(*args(qs=FAKE + 8)) == EALIGN
+    assert d(*args(t=FAKE + 2)) == EALIGN
+    assert d(*args(pos=FAKE + 1)) == EALIGN
+    assert d(*args(B=0, qo=None, ko=None, vo=None, q=None, k=None, v=None, t=None)) == OK
+
+
+def test_cca_mix_validation(L):
+    d = lambda *a: L.attn_cca_mix(*a)
+    args = lambda **kw: [kw.get("qo", FAKE), kw.get("ko", FAKE), kw.get("vo", FAKE),
+                         kw.get("q", FAKE), kw.get("k", FAKE), kw.get("v", FAKE),
+                         kw.get("dt", BF16), kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 2),
+                         kw.get("S", 100), kw.get("D", 64), kw.get("cq", FAKE), kw.get("ck", FAKE),
+                         kw.get("W", 4), kw.get("mq", FAKE), kw.get("mk", FAKE),
+                         kw.get("pos", None), kw.get("theta", 1e4), None]
+    assert d(*args(Hkv=3)) == ESHAPE
+    assert d(*args(S=-1)) == ESHAPE
+    assert d(*args(S=(1 << 24) - 64 + 1, D=64)) == ESHAPE  # (S + 64) D 2 reaches 2^31
+    assert d(*args(dt=F32)) == EUNSUP
+    assert d(*args(D=32)) == EUNSUP
+    assert d(*args(W=0)) == EUNSUP
+    assert d(*args(W=9)) == EUNSUP
+    assert d(*args(theta=float("nan"))) == EUNSUP
+    for name in ("qo", "ko", "vo", "q", "k", "v", "cq", "ck", "mq", "mk"):
+        assert d(*args(**{name: None})) == ENULL, name
+    assert d(*args(cq=FAKE + 4)) == EALIGN
+    assert d(*args(pos=FAKE + 2)) == EALIGN
+    assert d(*args(S=0, qo=None, ko=None, vo=None, q=None, k=None, v=None)) == OK
+    assert d(*args(B=0, qo=None)) == OK

@@ -166,3 +166,112 @@ def test_cca_mix_errors():
     with pytest.raises(attn.AttnError) as e:
         attn.cca_mix(q, k, v, wide, torch.zeros(2, 9, 64, dtype=torch.bfloat16, device=DEV), mq, mk)
     assert e.value.status == 3
+
+
+def _decode_state(B, Hq, Hkv, W, D, fill):
+    qs = torch.full((B, Hq, max(W - 1, 1), D), fill, dtype=torch.bfloat16, device=DEV)
+    ks = torch.full((B, Hkv, max(W - 1, 1), D), fill, dtype=torch.bfloat16, device=DEV)
+    vs = torch.full((B, Hkv, D), fill, dtype=torch.bfloat16, device=DEV)
+    return qs, ks, vs
+
+
+def _check_decode_rows(outs, ref, absref, rows, what):
+    """outs: the step's (q, k, v) [B, H, D]; ref/absref: the oracle's full
+    sequences; rows: token index per sequence."""
+    b = np.arange(len(rows))
+    pick = lambda x: x[b, :, rows, :]  # [B, H, D]
+    (qo, ko, vo), (rq, rk, rv), (aq, ak) = outs, ref, absref
+    assert np.array_equal(bits(vo), oracle.round_bf16(pick(rv))), f"{what}: value shift must be exact"
+    assert_rounded(bits(qo), pick(rq), _pair_bound(pick(aq)), f"{what} q")
+    assert_rounded(bits(ko), pick(rk), _pair_bound(pick(ak)), f"{what} k")
+
+
+DECODE_CASES = [  # B, Hq, Hkv, T, D, width, theta
+    (2, 8, 2, 12, 64, 4, 1e4),
+    (3, 4, 2, 9, 128, 3, 5e5),
+    (1, 16, 1, 6, 64, 8, 1e4),   # MQA, widest convolution (longer than the sequence at first)
+    (2, 4, 4, 5, 128, 1, 0.0),   # MHA, a single tap: no ring
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES)
+def test_cca_mix_decode_steps_from_scratch(case):
+    """Token after token from the first, the state filled with NaN (rows of
+    tokens before the first must never be read): every step equals row t of
+    the oracle's pass over the sequence."""
+    B, Hq, Hkv, T, D, width, theta = case
+    w = wl.custom("prefill", "bf16", B, Hq, Hkv, D, T)
+    q, k, v, cq, ck, mq, mk = wl.make_cca(w, seed=40 + T, width=width)
+    pos = torch.tensor([3 * b + 11 for b in range(B)], dtype=torch.int32)
+    ins = [bits(x) for x in (q, k, v, cq, ck, mq, mk)]
+    ref = oracle.cca_mix(*ins, pos_offset=pos.numpy(), theta=theta)
+    aq, ak, _ = oracle.cca_mix(*(np.abs(oracle.widen(x)) for x in ins))
+    dq, dk, dv = (x.to(DEV) for x in (q, k, v))
+    wts = [x.to(DEV) for x in (cq, ck, mq, mk)]
+    qs, ks, vs = _decode_state(B, Hq, Hkv, width, D, float("nan"))
+    say(f"cca_mix_decode from scratch {case}")
+    for t in range(T):
+        tt = torch.full((B,), t, dtype=torch.int32, device=DEV)
+        outs = attn.cca_mix_decode(dq[:, :, t].contiguous(), dk[:, :, t].contiguous(),
+                                   dv[:, :, t].contiguous(), *wts, tt, qs, ks, vs,
+                                   rope_theta=theta, pos_offset=pos.to(DEV))
+        torch.cuda.synchronize()
+        _check_decode_rows(outs, ref, (aq, ak), np.full(B, t), f"step {t}")
+
+
+def test_cca_mix_decode_after_a_prefill_of_ragged_prompts():
+    """Prompts of different lengths go through attn_cca_mix, their last W - 1
+    rows and last v row become the state (token u in ring slot u mod (W - 1)),
+    and decode steps continue each sequence from its own length."""
+    B, Hq, Hkv, D, width, theta, T = 3, 8, 2, 64, 4, 1e4, 40
+    prompt = [5, 13, 2]
+    w = wl.custom("prefill", "bf16", B, Hq, Hkv, D, T)
+    q, k, v, cq, ck, mq, mk = wl.make_cca(w, seed=77, width=width)
+    ins = [bits(x) for x in (q, k, v, cq, ck, mq, mk)]
+    ref = oracle.cca_mix(*ins, theta=theta)
+    aq, ak, _ = oracle.cca_mix(*(np.abs(oracle.widen(x)) for x in ins))
+    dq, dk, dv = (x.to(DEV) for x in (q, k, v))
+    wts = [x.to(DEV) for x in (cq, ck, mq, mk)]
+    # the prefill pass over the longest prompt (rows past a shorter prompt are
+    # not used: the pass is causal, so a prompt's rows depend on it alone)
+    S0 = max(prompt)
+    po = attn.cca_mix(dq[:, :, :S0].contiguous(), dk[:, :, :S0].contiguous(),
+                      dv[:, :, :S0].contiguous(), *wts, rope_theta=theta)
+    torch.cuda.synchronize()
+    for b in range(B):  # each prompt's last row from the prefill pass
+        sub = lambda x: x[b:b + 1]
+        _check_decode_rows([x[b:b + 1, :, prompt[b] - 1] for x in po], [sub(x) for x in ref],
+                           [sub(aq), sub(ak)], np.array([prompt[b] - 1]),
+                           f"prefill row of sequence {b}")
+    qs, ks, vs = _decode_state(B, Hq, Hkv, width, D, float("nan"))
+    for b in range(B):
+        for u in range(max(0, prompt[b] - (width - 1)), prompt[b]):
+            qs[b, :, u % (width - 1)] = dq[b, :, u]
+            ks[b, :, u % (width - 1)] = dk[b, :, u]
+        vs[b] = dv[b, :, prompt[b] - 1]
+    say("cca_mix_decode after ragged prompts")
+    for step in range(6):
+        rows = np.array(prompt) + step
+        tt = torch.tensor(rows, dtype=torch.int32, device=DEV)
+        sel = lambda x: torch.stack([x[b, :, rows[b]] for b in range(B)])
+        outs = attn.cca_mix_decode(sel(dq), sel(dk), sel(dv), *wts, tt, qs, ks, vs,
+                                   rope_theta=theta)
+        torch.cuda.synchronize()
+        _check_decode_rows(outs, ref, (aq, ak), rows, f"decode step {step}")
+
+
+def test_cca_mix_decode_errors():
+    q = torch.zeros(2, 8, 64, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(2, 2, 64, dtype=torch.bfloat16, device=DEV)
+    cq = torch.zeros(8, 4, 64, dtype=torch.bfloat16, device=DEV)
+    ck = torch.zeros(2, 4, 64, dtype=torch.bfloat16, device=DEV)
+    mq = torch.zeros(8, 64, 64, dtype=torch.bfloat16, device=DEV)
+    mk = torch.zeros(2, 64, 64, dtype=torch.bfloat16, device=DEV)
+    qs, ks, vs = _decode_state(2, 8, 2, 4, 64, 0.0)
+    t = torch.zeros(2, dtype=torch.int32, device=DEV)
+    with pytest.raises(attn.AttnError) as e:
+        attn.cca_mix_decode(q.float(), k.float(), k.float(), cq.float(), ck.float(), mq.float(),
+                            mk.float(), t, qs.float(), ks.float(), vs.float())
+    assert e.value.status == 3
+    with pytest.raises(ValueError):
+        attn.cca_mix_decode(q, k, k, cq, ck, mq, mk, t, qs[:, :, :2], ks, vs)
