@@ -337,6 +337,42 @@ def bench_cca_step(w, steps, warmup):
     flops = prefill_flops(w.B, w.Hq, w.S, w.D)
     gbs = cca_bytes(w) / (mix_ms * 1e-3) / 1e9
     ms_step = wall * 1e3 / steps
+
+    # the decode step's counterpart: one new token for each of 32 sequences
+    # of the same geometry, at token indices drawn from 1024..8192
+    Bd, Wd = 32, wl.CCA_CONV_WIDTH
+    g = torch.Generator().manual_seed(0)
+    qd = torch.randn(Bd, w.Hq, w.D, generator=g).to(torch.bfloat16).cuda()
+    kd = torch.randn(Bd, w.Hkv, w.D, generator=g).to(torch.bfloat16).cuda()
+    vd = torch.randn(Bd, w.Hkv, w.D, generator=g).to(torch.bfloat16).cuda()
+    tok = torch.randint(1024, 8193, (Bd,), generator=g, dtype=torch.int32).cuda()
+    qs = torch.randn(Bd, w.Hq, Wd - 1, w.D, generator=g).to(torch.bfloat16).cuda()
+    ks = torch.randn(Bd, w.Hkv, Wd - 1, w.D, generator=g).to(torch.bfloat16).cuda()
+    vs = torch.randn(Bd, w.Hkv, w.D, generator=g).to(torch.bfloat16).cuda()
+    douts = [torch.empty_like(x) for x in (qd, kd, vd)]
+
+    def dstep():
+        attn.cca_mix_decode(qd, kd, vd, *ins[3:], tok, qs, ks, vs, rope_theta=w.theta,
+                            q_out=douts[0], k_out=douts[1], v_out=douts[2])
+
+    # 100 steps captured in a HIP graph and replayed, so the time is the GPU's
+    # and not the host's per-call overhead (the step itself is a few us)
+    for _ in range(20):
+        dstep()
+    torch.cuda.synchronize()
+    graph, gs = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(graph, stream=gs):
+            for _ in range(100):
+                dstep()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_us = e0.elapsed_time(e1) / 100 * 1e3
     return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
             "head_dim": w.D, "seq_len": w.S, "rope_theta": w.theta,
             "conv_width": wl.CCA_CONV_WIDTH,
@@ -347,7 +383,10 @@ def bench_cca_step(w, steps, warmup):
             "ms_per_step": round(ms_step, 5),
             "step_TFLOP_per_s": round(flops / (ms_step * 1e-3) / 1e12, 1), "steps": steps,
             "step": "CCA pre-attention pass (conv, channel mix, QK-mean, RoPE, value shift) + "
-                    "causal GQA prefill"}
+                    "causal GQA prefill",
+            "cca_decode_step_us": round(dec_us, 2),
+            "cca_decode_step": f"attn_cca_mix_decode: one new token for each of {Bd} sequences "
+                               f"(token indices 1024..8192), 100 steps replayed from a HIP graph"}
 
 
 def cpu_model():
@@ -503,7 +542,8 @@ def main():
     result["prefill_ccgqa"] = cc
     ca = bench_cca_step(wl.WORKLOADS["ccgqa_prefill"], args.steps, args.warmup)
     log(f"ccgqa with the CCA pass: mix {ca['cca_mix_ms_mean']:.4f} ms ({ca['cca_mix_GB_per_s']:.0f} GB/s), "
-        f"prefill {ca['prefill_ms_mean']:.4f} ms, step {ca['ms_per_step']:.4f} ms")
+        f"prefill {ca['prefill_ms_mean']:.4f} ms, step {ca['ms_per_step']:.4f} ms; "
+        f"decode step {ca['cca_decode_step_us']:.1f} us")
     result["ccgqa_cca_step"] = ca
     if not args.no_decode:
         dec = {}
