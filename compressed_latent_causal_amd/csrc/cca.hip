@@ -404,7 +404,7 @@ __global__ __launch_bounds__(CD_THREADS) void cca_decode_kernel(
     const int tid = threadIdx.x;
     const int b = (int)blockIdx.x / Hkv, j = (int)blockIdx.x % Hkv;
     const int G = Hq / Hkv, NH = G + 1;
-    const int t = tok[b];
+    const int t = max(tok[b], 0);  // a negative index (a caller error) is taken as 0
     const int R = W - 1;  // state rows per head
     float* const mean = sm + NH * D;
 

@@ -306,7 +306,8 @@ int attn_cca_mix(void *q_out, void *k_out, void *v_out, const void *q, const voi
  * The CCA pre-attention operations of attn_cca_mix for one new token per
  * sequence, as a decode step needs them ("Compressed Convolutional Attention"
  * summary, "Methodologie", items 2 to 4, in the same readings).  Token t[b]
- * (its index in sequence b, >= 0; RoPE position pos_offset[b] + t[b]) is
+ * (its index in sequence b, >= 0; a negative value, a caller error, is taken
+ * as 0 on the device; RoPE position pos_offset[b] + t[b]) is
  * mixed with the tokens before it that the width-W convolution reaches,
  * which the caller keeps as state between steps:
  *   q_state [B, Hq, W-1, D], k_state [B, Hkv, W-1, D]: the pre-convolution

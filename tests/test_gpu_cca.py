@@ -275,3 +275,25 @@ def test_cca_mix_decode_errors():
     assert e.value.status == 3
     with pytest.raises(ValueError):
         attn.cca_mix_decode(q, k, k, cq, ck, mq, mk, t, qs[:, :, :2], ks, vs)
+
+
+def test_cca_mix_decode_negative_index_is_taken_as_zero():
+    """A negative token index (a caller error) is clamped on the device: the
+    step is that of the first token, and no state row is read or written out
+    of place (the NaN-filled state stays NaN outside slot 0)."""
+    B, Hq, Hkv, D, width, theta = 2, 8, 2, 64, 4, 1e4
+    w = wl.custom("prefill", "bf16", B, Hq, Hkv, D, 1)
+    q, k, v, cq, ck, mq, mk = (x.to(DEV) for x in wl.make_cca(w, seed=5, width=width))
+    wts = (cq, ck, mq, mk)
+    outs = []
+    for tval in (0, -5):
+        qs, ks, vs = _decode_state(B, Hq, Hkv, width, D, float("nan"))
+        tt = torch.full((B,), tval, dtype=torch.int32, device=DEV)
+        outs.append(attn.cca_mix_decode(q[:, :, 0].contiguous(), k[:, :, 0].contiguous(),
+                                        v[:, :, 0].contiguous(), *wts, tt, qs, ks, vs,
+                                        rope_theta=theta))
+        torch.cuda.synchronize()
+        assert torch.isnan(qs[:, :, 1:].float()).all() and torch.isnan(ks[:, :, 1:].float()).all()
+        assert torch.equal(qs[:, :, 0], q[:, :, 0]) and torch.equal(vs, v[:, :, 0])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
