@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.hip", "rope.hip", "prefill.hip", "decode.hip", "backward.hip", "cca.hip"]
+SOURCES = ["api.hip", "rope.hip", "prefill.hip", "decode.hip", "decode_f32.hip", "backward.hip",
+           "cca.hip"]
 ARCH = "gfx950"
 
 

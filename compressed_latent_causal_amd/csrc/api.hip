@@ -118,15 +118,19 @@ namespace {
 // workspace).  *empty is set when there is nothing to do.
 int decode_checks(void* o, const void* q, const void* k_cache, const void* v_cache, int dtype,
                   int B, int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens, int max_len,
-                  float scale, double rope_theta, bool* empty) {
+                  float scale, double rope_theta, bool* empty, bool allow_f32 = false) {
     *empty = false;
     if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_cap < 1 || max_len < 0 || max_len > S_cap)
         return ATTN_ERR_SHAPE;
-    if (dtype != ATTN_BF16 || !supported_dim(D) || !good_scale(scale)) return ATTN_ERR_UNSUPPORTED;
+    const bool f32 = allow_f32 && dtype == ATTN_F32;
+    if ((dtype != ATTN_BF16 && !f32) || !supported_dim(D) || !good_scale(scale))
+        return ATTN_ERR_UNSUPPORTED;
+    if (f32 && !attn::decode_f32_supported(Hq / Hkv, D)) return ATTN_ERR_UNSUPPORTED;
     if (!(rope_theta >= 0.0) || !isfinite(rope_theta)) return ATTN_ERR_UNSUPPORTED;
     if (B > kMaxGridYZ || (long long)Hkv * ((Hq / Hkv + 15) / 16) > kMaxGridYZ) return ATTN_ERR_SHAPE;
+    if (f32 && (long long)B * Hkv > kMaxGridYZ) return ATTN_ERR_SHAPE;  // its grid's y extent
     // a group's partial results are addressed with 32-bit byte offsets
-    if ((long long)max_len * D * 2 >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    if ((long long)max_len * D * (f32 ? 4 : 2) >= (1ll << 31)) return ATTN_ERR_SHAPE;
     if (B == 0) {
         *empty = true;
         return ATTN_OK;
@@ -145,11 +149,15 @@ ATTN_API int attn_decode(void* o, const void* q, const void* k_cache, const void
                          size_t workspace_bytes, void* stream) {
     bool empty = false;
     const int rc = decode_checks(o, q, k_cache, v_cache, dtype, B, Hq, Hkv, S_cap, D, seqlens,
-                                 max_len, scale, rope_theta, &empty);
+                                 max_len, scale, rope_theta, &empty, /*allow_f32=*/true);
     if (rc != ATTN_OK || empty) return rc;
     const size_t need = attn::decode_workspace_bytes(B, Hq, Hkv, max_len, D);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+    if (dtype == ATTN_F32)
+        return hip_status(attn::launch_decode_f32(o, q, k_cache, v_cache, B, Hq, Hkv, S_cap, D,
+                                                  seqlens, max_len, scale, rope_theta, workspace,
+                                                  (hipStream_t)stream));
     return hip_status(attn::launch_decode(o, q, k_cache, v_cache, B, Hq, Hkv, S_cap, D, seqlens,
                                           max_len, scale, rope_theta, workspace,
                                           (hipStream_t)stream));

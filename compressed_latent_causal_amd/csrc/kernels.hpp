@@ -64,6 +64,15 @@ hipError_t launch_decode_paged(void* o, const void* q, const void* k_pages, cons
                                int max_len, int window, float scale, double rope_theta,
                                void* workspace, hipStream_t st);
 
+// fp32 decode over a contiguous cache (accuracy path): chunk partials into
+// the decode workspace, then a merge; groups with G * D <= 4096.
+bool decode_f32_supported(int G, int D);
+size_t decode_f32_lds_bytes(int G, int D);
+hipError_t launch_decode_f32(void* o, const void* q, const void* k_cache, const void* v_cache,
+                             int B, int Hq, int Hkv, int S_cap, int D, const int32_t* seqlens,
+                             int max_len, float scale, double rope_theta, void* workspace,
+                             hipStream_t st);
+
 // CCA pre-attention operations (bf16): causal depthwise sequence convolution
 // of width W (conv_q [Hq, W, D], conv_k [Hkv, W, D]), channel mix per head
 // (mix_q [Hq, D, D], mix_k [Hkv, D, D]), the group's pre-convolution

@@ -201,10 +201,15 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int D);
  * epoch kept in the workspace and advanced on the device, so the tags also
  * differ between replays of one call captured in a HIP graph), and it must
  * not be shared by calls that may overlap.  The call enqueues no memset or
- * copy, so it may be captured in a graph.  dtype: BF16 only.  scale > 0 and finite.  One kernel is enqueued:
- * its workgroups read the lengths and split the batch's keys into nearly
- * equal parts (a sequence's keys go to one or more workgroups), and one that
- * finds all partial results of its (sequence, KV head) written merges them.
+ * copy, so it may be captured in a graph.  scale > 0 and finite.
+ * dtype BF16: one kernel is enqueued: its workgroups read the lengths and
+ * split the batch's keys into nearly equal parts (a sequence's keys go to one
+ * or more workgroups), and one that finds all partial results of its
+ * (sequence, KV head) written merges them.
+ * dtype F32: the accuracy path, fp32 throughout (within 1e-5 of the exact
+ * result), not a performance path: two kernels, one writing the partial
+ * result of every 512-key chunk into the same workspace, one merging them.
+ * Groups with (Hq / Hkv) * D > 4096 return ATTN_ERR_UNSUPPORTED on this path.
  */
 int attn_decode(void *o, const void *q, const void *k_cache, const void *v_cache, int dtype,
                 int B, int Hq, int Hkv, int S_cap, int D, const int32_t *seqlens,
@@ -215,7 +220,8 @@ int attn_decode(void *o, const void *q, const void *k_cache, const void *v_cache
  * attn_decode without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Arguments, results and errors are those of
- * attn_decode; the split pass's partial results live instead in a static
+ * attn_decode with dtype BF16 (F32 returns ATTN_ERR_UNSUPPORTED); the split
+ * pass's partial results live instead in a static
  * array of ATTN_DECODE_SCRATCH_BYTES (16 MiB) that every device the library
  * runs on holds until the process ends.  The call allocates and frees nothing.
  * The problem must fit that array: attn_decode_workspace_size(B, Hq, Hkv,

@@ -192,7 +192,12 @@ def test_decode_validation(L):
     assert d(*args(max_len=65)) == ESHAPE
     assert d(*args(max_len=-1)) == ESHAPE
     assert d(*args(S_cap=0, max_len=0)) == ESHAPE
-    assert d(*args(dt=F32)) == EUNSUP
+    # fp32 caches take the accuracy path, for groups with G * D <= 4096
+    assert d(*args(dt=F32, o=None)) == ENULL
+    assert d(*args(dt=F32, Hq=64, Hkv=1, D=128)) == EUNSUP
+    assert d(*args(dt=F32, Hq=32, Hkv=1, D=128, o=None)) == ENULL
+    assert d(*args(dt=F32, B=70000, Hkv=1, Hq=1, S_cap=64)) == ESHAPE
+    assert d(*args(dt=2)) == EUNSUP
     assert d(*args(D=80)) == EUNSUP
     assert d(*args(scale=0.0)) == EUNSUP
     assert d(*args(theta=-1.0)) == EUNSUP

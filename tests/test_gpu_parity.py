@@ -748,10 +748,44 @@ def test_decode_matches_last_prefill_row():
     assert_close(host_f64(dec), host_f64(pre[:, :, S - 1]), BF16_MAX, BF16_MEAN, what="dec vs pre")
 
 
-def test_decode_rejects_fp32_and_small_workspace():
-    q = torch.zeros(1, 4, 128, device=DEV)
-    kc = torch.zeros(1, 2, 16, 128, device=DEV)
-    with pytest.raises(attn.AttnError) as e:
+F32_DECODE_CASES = [  # B, Hq, Hkv, S_cap, D, lengths, theta
+    (3, 8, 2, 1500, 128, [1500, 1, 700], 5e5),      # chunks of 512 with a ragged tail
+    (2, 4, 4, 600, 64, [0, 513], 0.0),              # MHA, an empty sequence
+    (1, 16, 1, 2049, 64, [2049], 1e4),              # MQA, five chunks
+    (4, 32, 1, 100, 128, [1, 31, 32, 100], 5e5),    # G * D = 4096, the largest group
+]
+
+
+@pytest.mark.parametrize("case", F32_DECODE_CASES)
+def test_decode_fp32_matches_oracle(case):
+    """fp32 caches take the accuracy path (chunk partials and a merge, fp32
+    throughout): within 1e-5 of the fp64 oracle, the query rotated at len - 1
+    when theta > 0, a NaN-poisoned tail never read."""
+    B, Hq, Hkv, S_cap, D, lens, theta = case
+    g = torch.Generator().manual_seed(S_cap + D)
+    q = torch.randn(B, Hq, D, generator=g)
+    kc = torch.randn(B, Hkv, S_cap, D, generator=g)
+    vc = torch.randn(B, Hkv, S_cap, D, generator=g)
+    L = torch.tensor(lens, dtype=torch.int32)
+    wl.poison_cache_tail(kc, L)
+    wl.poison_cache_tail(vc, L)
+    say(f"decode fp32 {case}")
+    o = attn.decode(dev(q), dev(kc), dev(vc), dev(L), rope_theta=theta)
+    qr = q.numpy().astype(np.float64)
+    if theta > 0:
+        qr = oracle.rope(q.numpy()[:, :, None, :], theta, (L.numpy() - 1))[:, :, 0, :]
+    ref = oracle.decode(qr, kc.numpy().astype(np.float64), vc.numpy().astype(np.float64), L.numpy())
+    got = host_f64(o)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    say(f"decode fp32 max err {err:.2e}")
+    assert err <= 1e-5
+
+
+def test_decode_rejects_large_fp32_groups_and_small_workspace():
+    q = torch.zeros(1, 64, 128, device=DEV)
+    kc = torch.zeros(1, 1, 16, 128, device=DEV)
+    with pytest.raises(attn.AttnError) as e:  # G * D = 8192 is past the fp32 path
         attn.decode(q, kc, kc, torch.ones(1, dtype=torch.int32, device=DEV))
     assert e.value.status == 3
     qb, kb = q.bfloat16(), kc.bfloat16()
