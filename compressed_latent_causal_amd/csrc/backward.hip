@@ -45,14 +45,15 @@ constexpr int BW_BN = 64;  // keys per K/V tile (dQ kernel)
 
 // The 8-wide slice of each 32-wide k-step that lane group lg supplies to the
 // products whose A operand is read directly from a swz_v tile.  The same
-// permutation on both operands leaves a product unchanged; at D = 128 the
-// order (0, 2, 1, 3) makes the two lane groups that the LDS serves together
-// read chunks in disjoint bank sets (measured: 2.67 instead of 4 LDS cycles per
-// 16-byte read, no bank conflicts).  At D = 64 the natural order is already
-// conflict-free.
-template <int D>
+// permutation on both operands leaves a product unchanged.  The order
+// (0, 2, 1, 3) removes the LDS bank conflicts of these reads at both head
+// dims: measured over five layouts, a 16-byte-per-lane read is served in four
+// passes whose lanes agree in (lane bit 3 xor bit 4, bit 5), i.e. lanes
+// {0-7, 24-31}, {8-15, 16-23}, {32-39, 56-63}, {40-47, 48-55}; in the natural
+// order two lanes of a pass share banks (2-way conflicts, a third more LDS
+// cycles), in this order none do.
 __device__ inline int kslice(int lg) {
-    return D == 128 ? (((lg & 1) << 1) | (lg >> 1)) : lg;
+    return ((lg & 1) << 1) | (lg >> 1);
 }
 
 // Rows of row statistics per head: whole Q tiles plus one (the stats of a tile
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(NW * 64, ((NK == 1 || D == 64) && NW == 4) ? 2 : 1)
     // K and V rows of the wave's keys as B operands: key kw0 + 16nk + lr, dims
     // 32s + 8 kslice(lg) .. +7
     const size_t kv_base = (size_t)(b * Hkv + kvh) * S * D;
-    const int ks8 = 8 * kslice<D>(lg);
+    const int ks8 = 8 * kslice(lg);
     bf16x8_t kf[NK][KSTEPS], vf[NK][KSTEPS];
 #pragma unroll
     for (int nk = 0; nk < NK; ++nk) {
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(NW * 64, ((NK == 1 || D == 64) && NW == 4) ? 2 : 1)
     // of d tile dt (the A operand of dV^T and dK^T).
     int aoff[KSTEPS], toff[DT];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) aoff[s] = swz_v<D>(lr, 4 * s + kslice<D>(lg));
+    for (int s = 0; s < KSTEPS; ++s) aoff[s] = swz_v<D>(lr, 4 * s + kslice(lg));
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) toff[dt] = v_frag_off<D>(dt, lane);
     int vo[NI];
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         for (int s = 0; s < KSTEPS; ++s) {
             u32x4_t xq = {0, 0, 0, 0}, xg = {0, 0, 0, 0};
             if (row < S) {  // Q^T in the k order of the K tile's direct reads
-                xq = *(const u32x4_t*)(q + qo_base + (size_t)row * D + 32 * s + 8 * kslice<D>(lg));
+                xq = *(const u32x4_t*)(q + qo_base + (size_t)row * D + 32 * s + 8 * kslice(lg));
                 xg = *(const u32x4_t*)(dout + qo_base + (size_t)row * D + 32 * s + 8 * lg);
             }
             qf[n][s] = __builtin_bit_cast(bf16x8_t, xq);
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     int koff[KSTEPS], voff[KSTEPS], toff[DT];
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-        koff[s] = swz_v<D>(lr, 4 * s + kslice<D>(lg));
+        koff[s] = swz_v<D>(lr, 4 * s + kslice(lg));
         voff[s] = swz_k<D>(lr, 4 * s + lg);
     }
 #pragma unroll

@@ -136,14 +136,20 @@ __global__ __launch_bounds__(PF_THREADS, (D == 64 || NQ == 2) ? 2 : 1) void pref
     // positions are formed once into a table shared by its heads (rows 0..31
     // in the not yet used k1, rows 32..63 in v1: 32 rows x D/2 pairs x 8 bytes
     // fill one tile buffer).  Workgroups of 128 queries (one head each) form
-    // them per lane instead.
+    // them per lane instead.  A lane reads the 4 pairs it rotates as two
+    // 16-byte units; unit u of row r is stored at u ^ swz(r) with the swz_v
+    // row permutation, so the 16 rows one lane group reads fall in distinct
+    // banks (unswizzled, rows 256 or 512 bytes apart share them all).
     constexpr bool kRopeTable = QPB <= 64;
+    auto rope_slot = [&](int r, int u) __attribute__((always_inline)) {
+        return (r < 32 ? k1 : v1) + (r & 31) * (4 * D) + 16 * (u ^ (((r & 7) << 1) | ((r >> 3) & 1)));
+    };
     if (rope && kRopeTable) {
         for (int idx = tid; idx < QPB * (D / 2); idx += PF_THREADS) {
             const int r = idx / (D / 2), pr = idx % (D / 2);
             float cs, sn;
             rope_cos_sin(q0 + r, fr.f[pr], cs, sn);
-            *(float2*)((r < 32 ? k1 : v1) + ((r & 31) * (D / 2) + pr) * 8) = float2{cs, sn};
+            *(float2*)(rope_slot(r, pr >> 1) + 8 * (pr & 1)) = float2{cs, sn};
         }
         __syncthreads();
     }
@@ -160,16 +166,20 @@ __global__ __launch_bounds__(PF_THREADS, (D == 64 || NQ == 2) ? 2 : 1) void pref
             if (rope) {
                 // query `row` sits at position row; word e of x holds channel
                 // pair 16s + 4lg + e (the same arithmetic as the RoPE kernel)
+                f32x4_t tu[2];
+                if constexpr (kRopeTable) {
+                    const int tr = (w / HPW) * PF_QW + 16 * n + lr;  // table row
+#pragma unroll
+                    for (int hu = 0; hu < 2; ++hu)
+                        tu[hu] = *(const f32x4_t*)rope_slot(tr, 8 * s + 2 * lg + hu);
+                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int pr = 16 * s + 4 * lg + e;
                     float cs, sn, y0, y1;
                     if constexpr (kRopeTable) {
-                        const int tr = (w / HPW) * PF_QW + 16 * n + lr;  // table row
-                        const float2 t = *(const float2*)((tr < 32 ? k1 : v1) +
-                                                          ((tr & 31) * (D / 2) + pr) * 8);
-                        cs = t.x;
-                        sn = t.y;
+                        cs = tu[e >> 1][2 * (e & 1)];
+                        sn = tu[e >> 1][2 * (e & 1) + 1];
                     } else {
                         rope_cos_sin(row, fr.f[pr], cs, sn);
                     }
