@@ -69,6 +69,28 @@ constexpr int PF_BN = 64;                 // keys per K/V tile
 #endif
 constexpr int PF_NW = ATTN_PF_WAVES;      // waves per workgroup
 constexpr int PF_THREADS = PF_NW * 64;
+
+// Workgroup order.  Workgroups go to the 8 XCDs (each with its own L2) in
+// turn, so workgroup i runs on XCD i % 8.  With per = (sequence, KV head,
+// head chunk) combinations a multiple of 8, XCD x serves the combinations
+// rem = x (mod 8) for every query block; in plain order it runs them
+// interleaved, heaviest query blocks first, and the K/V of per/8 KV heads
+// compete for its L2.  Here each XCD takes its combinations one after the
+// other, each from its heaviest query block down, so the workgroups resident
+// on an XCD mostly share one KV head's K/V.  Every XCD keeps the same work.
+// Other shapes keep the plain order.  Returns the query-block rank qbi (0 =
+// heaviest) and the combination rem.
+__device__ inline void xcd_block_order(int i, int per, int n_qblk, int& qbi, int& rem) {
+    if (per % 8 == 0) {
+        const int j = i / 8, m = j / n_qblk;  // m-th combination of this XCD
+        qbi = j % n_qblk;
+        rem = (i % 8) + 8 * m;
+    } else {
+        qbi = i / per;
+        rem = i % per;
+    }
+}
+
 // LDS operand fragments read ahead of the products that use them
 #ifndef PF_PD
 #define PF_PD 2
@@ -116,8 +138,9 @@ __global__ __launch_bounds__(PF_THREADS, (D == 64 || NQ == 2) ? 2 : 1) void pref
 
     const int G = Hq / Hkv;
     const int per = B * Hkv * n_hchunk;
-    const int qb = n_qblk - 1 - (int)blockIdx.x / per;  // heaviest query blocks first
-    const int rem = (int)blockIdx.x % per;
+    int qbi, rem;
+    xcd_block_order((int)blockIdx.x, per, n_qblk, qbi, rem);
+    const int qb = n_qblk - 1 - qbi;  // heaviest query blocks first
     const int bkv = rem % (B * Hkv), hc = rem / (B * Hkv);
     const int b = bkv / Hkv, kvh = bkv % Hkv;
 
