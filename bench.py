@@ -235,7 +235,7 @@ def bench_backward(w, iters, warmup):
 
     q, k, v, dout = (t.cuda() for t in wl.make_backward(w, seed=0))
     o, lse = attn.prefill_lse(q, k, v, scale=w.scale)
-    ws = torch.empty(attn.prefill_backward_workspace_size(w.B, w.Hq, w.S), dtype=torch.uint8,
+    ws = torch.empty(attn.prefill_backward_workspace_size(w.B, w.Hq, w.Hkv, w.S, w.D), dtype=torch.uint8,
                      device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     stream = torch.cuda.current_stream()

@@ -10,7 +10,7 @@ fallback: calling into the library without the built ``libattn.so`` raises.
     prefill(q, k, v, scale=None, out=None, rope_theta=0.0)
     prefill_lse(q, k, v, scale=None, out=None, lse=None, rope_theta=0.0)
     prefill_backward(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None, workspace=None)
-    prefill_backward_workspace_size(B, Hq, S)
+    prefill_backward_workspace_size(B, Hq, Hkv, S, D)
     decode(q, k_cache, v_cache, seqlens, max_len=None, scale=None, rope_theta=0.0, out=None,
            workspace=None)
     decode_noalloc(q, k_cache, v_cache, seqlens, out, max_len=None, scale=None, rope_theta=0.0)
@@ -169,8 +169,8 @@ def prefill_lse(q, k, v, scale: float | None = None, out=None, lse=None, rope_th
     return out, lse
 
 
-def prefill_backward_workspace_size(B: int, Hq: int, S: int) -> int:
-    return int(lib().attn_prefill_backward_workspace_size(B, Hq, S))
+def prefill_backward_workspace_size(B: int, Hq: int, Hkv: int, S: int, D: int) -> int:
+    return int(lib().attn_prefill_backward_workspace_size(B, Hq, Hkv, S, D))
 
 
 def prefill_backward(q, k, v, o, dout, lse, scale: float | None = None, dq=None, dk=None, dv=None,
@@ -193,7 +193,7 @@ def prefill_backward(q, k, v, o, dout, lse, scale: float | None = None, dq=None,
     if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
         raise ValueError("dq, dk, dv must match q, k, v")
     if workspace is None:
-        workspace = torch.empty(max(1, prefill_backward_workspace_size(B, Hq, S)),
+        workspace = torch.empty(max(1, prefill_backward_workspace_size(B, Hq, Hkv, S, D)),
                                 dtype=torch.uint8, device=q.device)
     _check_dev(q, k, v, o, dout, lse, dq, dk, dv, workspace)
     _call(lib().attn_prefill_backward, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), q.data_ptr(),

@@ -31,7 +31,7 @@ SIGNATURES = {
     "attn_rope_backward": (I, [P, P, I, I, I, I, I, P, I, D, P]),
     "attn_prefill": (I, [P, P, P, P, I, I, I, I, I, I, F, D, P]),
     "attn_prefill_lse": (I, [P, P, P, P, P, I, I, I, I, I, I, F, D, P]),
-    "attn_prefill_backward_workspace_size": (SZ, [I, I, I]),
+    "attn_prefill_backward_workspace_size": (SZ, [I, I, I, I, I]),
     "attn_prefill_backward": (I, [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P]),
     "attn_decode_workspace_size": (SZ, [I, I, I, I, I]),
     "attn_decode": (I, [P, P, P, P, I, I, I, I, I, I, P, I, F, D, P, SZ, P]),

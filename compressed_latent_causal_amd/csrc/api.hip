@@ -80,9 +80,9 @@ ATTN_API int attn_prefill_lse(void* o, float* lse, const void* q, const void* k,
                                            rope_theta, (hipStream_t)stream));
 }
 
-ATTN_API size_t attn_prefill_backward_workspace_size(int B, int Hq, int S) {
-    if (B < 1 || Hq < 1 || S < 1) return 0;
-    return attn::prefill_backward_workspace_bytes(B, Hq, S);
+ATTN_API size_t attn_prefill_backward_workspace_size(int B, int Hq, int Hkv, int S, int D) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S < 1 || !supported_dim(D)) return 0;
+    return attn::prefill_backward_workspace_bytes(B, Hq, Hkv, S, D);
 }
 
 ATTN_API int attn_prefill_backward(void* dq, void* dk, void* dv, const void* q, const void* k,
@@ -100,7 +100,7 @@ ATTN_API int attn_prefill_backward(void* dq, void* dk, void* dv, const void* q, 
     if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(q) || !aligned16(k) ||
         !aligned16(v) || !aligned16(o) || !aligned16(dout) || ((uintptr_t)lse & 3u))
         return ATTN_ERR_ALIGN;
-    if (!workspace || workspace_bytes < attn::prefill_backward_workspace_bytes(B, Hq, S))
+    if (!workspace || workspace_bytes < attn::prefill_backward_workspace_bytes(B, Hq, Hkv, S, D))
         return ATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
     return hip_status(attn::launch_prefill_backward(dq, dk, dv, q, k, v, o, dout, lse, B, Hq, Hkv,

@@ -9,7 +9,8 @@
 // dk_t = scale sum ds q_i and dv_t = sum p dout_i, the last two over every
 // query head of the group and every query i >= t.
 //
-// Three kernels, all bf16 in and out with fp32 accumulation:
+// Three kernels (four for split launches, below), bf16 in and out with fp32
+// accumulation:
 //  * row statistics: per query row the log-normaliser in the exp2 domain and
 //    delta = <dout, o> (from the forward's bf16 output), padded per head to
 //    whole tiles plus one (padding rows give p = 0 and ds = 0);
@@ -22,6 +23,12 @@
 //    rounded to bf16, then dV^T += dO^T P and dK^T += Q^T dS, with the A operand
 //    read transposed from the same LDS tiles.  The group's heads are summed in
 //    the accumulators, so dK and dV are written once, with no atomics.
+//    Workgroups that start at the first key blocks see every query and run
+//    longest; when a launch would give the GPU fewer than three rounds of
+//    workgroups, those few long ones decide its time.  Then the group's heads
+//    are split over hs workgroups per key block (and at D = 64 each wave takes
+//    32 keys), each writing its fp32 dK^T, dV^T partial sums to the workspace,
+//    and a fourth kernel adds the hs partials and rounds them once to bf16.
 //  * dQ: the forward's work split (one workgroup per query block and head
 //    slice of a KV group, K/V tiles of 64 keys through LDS); per tile S^T =
 //    K Q^T and dP^T - delta = V dO^T, dS^T in fp32 then bf16, and
@@ -29,6 +36,8 @@
 // S and dP are formed in both the dK/dV and the dQ kernel (seven products per
 // score tile instead of five): the price of writing every gradient once
 // without atomics or an fp32 dQ buffer.
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -98,7 +107,8 @@ template <int D, int NK, int NW>
 __global__ __launch_bounds__(NW * 64, ((NK == 1 || D == 64) && NW == 4) ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float2* __restrict__ stats, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int B, int Hq, int Hkv, int S, int S_pad, float c, float scale) {
+    uint16_t* __restrict__ dv, float* __restrict__ part, int B, int Hq, int Hkv, int S, int S_pad,
+    float c, float scale, int hsplit) {
     constexpr int KSTEPS = D / 32;  // k-steps of S = Q K^T
     constexpr int DT = D / 16;      // d tiles of dK^T, dV^T
     constexpr int ROW = D * 2;
@@ -117,9 +127,13 @@ __global__ __launch_bounds__(NW * 64, ((NK == 1 || D == 64) && NW == 4) ? 2 : 1)
 
     const int G = Hq / Hkv;
     const int per = B * Hkv;
-    const int kb = (int)blockIdx.x / per;  // first key blocks see the most queries: dispatched first
+    // workgroup = (key block, head slice, batch and KV head); the first key
+    // blocks see the most queries: dispatched first
+    const int kb = (int)blockIdx.x / (per * hsplit);
+    const int hs = (int)blockIdx.x / per % hsplit;
     const int bkv = (int)blockIdx.x % per;
     const int b = bkv / Hkv, kvh = bkv % Hkv;
+    const int Gs = G / hsplit;  // query heads of this workgroup: kvh G + hs Gs ..
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
@@ -167,13 +181,13 @@ __global__ __launch_bounds__(NW * 64, ((NK == 1 || D == 64) && NW == 4) ? 2 : 1)
         vo[i] = r * ROW + ((swz_v<D>(r, pc) - r * ROW) & ~15);
     }
 
-    // Work items: (query head of the group, Q tile), tiles from the one holding
+    // Work items: (query head of the slice, Q tile), tiles from the one holding
     // the workgroup's first key to the end of the sequence.
     const int t0 = k0 / BW_BQ;
     const int nt = ceil_div(S, BW_BQ) - t0;
-    const int n_it = nt > 0 ? G * nt : 0;
+    const int n_it = nt > 0 ? Gs * nt : 0;
     auto issue = [&](int it, char* qb, char* gb, char* sb) __attribute__((always_inline)) {
-        const int h = kvh * G + it / nt, t = t0 + it % nt;
+        const int h = kvh * G + hs * Gs + it / nt, t = t0 + it % nt;
         const size_t hb = (size_t)(b * Hq + h);
         const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(q + hb * S * D, S * ROW);
         const __amdgpu_buffer_rsrc_t grs = buffer_rsrc(dout + hb * S * D, S * ROW);
@@ -308,6 +322,22 @@ __global__ __launch_bounds__(NW * 64, ((NK == 1 || D == 64) && NW == 4) ? 2 : 1)
     }
 
     // ---- dK = scale dK^T, dV = dV^T; lane holds key kw0 + 16nk + lr, dims 16dt + 4lg .. +3
+    if (hsplit > 1) {  // this slice's fp32 partial sums: part[hs][K or V][b, kvh, key, d]
+        const size_t plane = (size_t)B * Hkv * S * D;
+        float* const pk = part + (size_t)hs * 2 * plane + kv_base;
+        float* const pv = pk + plane;
+#pragma unroll
+        for (int nk = 0; nk < NK; ++nk) {
+            const int key = kw0 + 16 * nk + lr;
+            if (key >= S) continue;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                *(f32x4_t*)(pk + (size_t)key * D + 16 * dt + 4 * lg) = dka[dt][nk];
+                *(f32x4_t*)(pv + (size_t)key * D + 16 * dt + 4 * lg) = dva[dt][nk];
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int nk = 0; nk < NK; ++nk) {
         const int key = kw0 + 16 * nk + lr;
@@ -325,6 +355,37 @@ __global__ __launch_bounds__(NW * 64, ((NK == 1 || D == 64) && NW == 4) ? 2 : 1)
             *(u32x2_t*)(vrow + 16 * dt) = e;
         }
     }
+}
+
+// dk = scale sum_hs part[hs][K], dv = sum_hs part[hs][V], rounded once to bf16;
+// one thread per 8 consecutive elements of the [B, Hkv, S, D] planes.
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ part,
+                                                              uint16_t* __restrict__ dk,
+                                                              uint16_t* __restrict__ dv,
+                                                              long long plane, int hsplit,
+                                                              float scale) {
+    const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= plane) return;
+    f32x4_t ka = {0, 0, 0, 0}, kb = {0, 0, 0, 0}, va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+    for (int hs = 0; hs < hsplit; ++hs) {
+        const float* const pk = part + (size_t)hs * 2 * plane + i;
+        const float* const pv = pk + plane;
+        ka += *(const f32x4_t*)pk;
+        kb += *(const f32x4_t*)(pk + 4);
+        va += *(const f32x4_t*)pv;
+        vb += *(const f32x4_t*)(pv + 4);
+    }
+    u32x4_t ko, vo;
+    ko[0] = pack_bf16x2(ka[0] * scale, ka[1] * scale);
+    ko[1] = pack_bf16x2(ka[2] * scale, ka[3] * scale);
+    ko[2] = pack_bf16x2(kb[0] * scale, kb[1] * scale);
+    ko[3] = pack_bf16x2(kb[2] * scale, kb[3] * scale);
+    vo[0] = pack_bf16x2(va[0], va[1]);
+    vo[1] = pack_bf16x2(va[2], va[3]);
+    vo[2] = pack_bf16x2(vb[0], vb[1]);
+    vo[3] = pack_bf16x2(vb[2], vb[3]);
+    *(u32x4_t*)(dk + i) = ko;
+    *(u32x4_t*)(dv + i) = vo;
 }
 
 // ------------------------------------------------------------------ dQ
@@ -535,17 +596,71 @@ int pow2_divisor(int g, int cap) {
     return hp;
 }
 
-// keys of 16 per wave in the dK/dV kernel, per head dim: each Q and dO
-// operand fragment read from LDS feeds NK products
-#ifndef BW_NK64
-#define BW_NK64 1
-#endif
-#ifndef BW_NK128
-#define BW_NK128 1
-#endif
 #ifndef BW_NW
 #define BW_NW 4
 #endif
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    const int slot = dev & 63;
+    int n = cache[slot].load(std::memory_order_relaxed);
+    if (n < 1) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        cache[slot].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+template <int D, int NK>
+int dkdv_blocks_per_cu() {
+    static const int n = [] {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, bwd_dkdv_kernel<D, NK, BW_NW>,
+                                                         BW_NW * 64, 0) != hipSuccess || b < 1)
+            b = 1;
+        return b;
+    }();
+    return n;
+}
+
+// How the dK/dV kernel is launched: keys of 16 per wave (nk) and head slices
+// per key block (hs).  One slice and 16 keys while the launch fills the GPU
+// at least three times over (the heaviest-first order then balances it);
+// otherwise the fewest slices (1, 2 or 4, dividing G) that reach three rounds,
+// with 32 keys per wave at D = 64, where each LDS operand then feeds two
+// products.
+struct BwdPlan {
+    int nk, hs;
+};
+template <int D>
+BwdPlan bwd_plan(int B, int Hq, int Hkv, int S) {
+    const int G = Hq / Hkv;
+    const long long cus = device_cus();
+    const long long nblk1 = (long long)ceil_div(S, 16 * BW_NW) * B * Hkv;
+    if (G == 1 || nblk1 >= 3 * cus * dkdv_blocks_per_cu<D, 1>()) return {1, 1};
+    constexpr int NK2 = D == 64 ? 2 : 1;
+    const long long nblk = (long long)ceil_div(S, 16 * NK2 * BW_NW) * B * Hkv;
+    const long long slots = cus * dkdv_blocks_per_cu<D, NK2>();
+    int hs = 1;
+    while (hs * 2 <= 4 && G % (hs * 2) == 0 && nblk * hs < 3 * slots) hs *= 2;
+    if (hs == 1) return {1, 1};
+    return {NK2, hs};
+}
+
+size_t stats_bytes(int B, int Hq, int S) {
+    return ((size_t)B * Hq * stats_rows(S) * sizeof(float2) + 255) & ~(size_t)255;
+}
+
+template <int D>
+size_t backward_workspace_d(int B, int Hq, int Hkv, int S) {
+    const BwdPlan pl = bwd_plan<D>(B, Hq, Hkv, S);
+    const size_t part = pl.hs > 1 ? (size_t)pl.hs * 2 * B * Hkv * S * D * sizeof(float) : 0;
+    return stats_bytes(B, Hq, S) + part;
+}
 
 template <int D>
 hipError_t launch_backward_d(void* dq, void* dk, void* dv, const void* q, const void* k,
@@ -563,13 +678,24 @@ hipError_t launch_backward_d(void* dq, void* dk, void* dv, const void* q, const 
                            S, S_pad, rows);
     }
     {
-        constexpr int NK = D == 64 ? BW_NK64 : BW_NK128;
-        constexpr int BK = 16 * NK * BW_NW;
-        const long long nblk = (long long)ceil_div(S, BK) * B * Hkv;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NK, BW_NW>), dim3((unsigned)nblk),
-                           dim3(BW_NW * 64), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                           (const uint16_t*)v, (const uint16_t*)dout, (const float2*)stats,
-                           (uint16_t*)dk, (uint16_t*)dv, B, Hq, Hkv, S, S_pad, c, scale);
+        const BwdPlan pl = bwd_plan<D>(B, Hq, Hkv, S);
+        float* const part = pl.hs > 1 ? (float*)((char*)workspace + stats_bytes(B, Hq, S)) : nullptr;
+        auto go = [&](auto kern, int bk) {
+            const long long nblk = (long long)ceil_div(S, bk) * B * Hkv * pl.hs;
+            hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(BW_NW * 64), 0, st,
+                               (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                               (const uint16_t*)dout, (const float2*)stats, (uint16_t*)dk,
+                               (uint16_t*)dv, part, B, Hq, Hkv, S, S_pad, c, scale, pl.hs);
+        };
+        constexpr int NK2 = D == 64 ? 2 : 1;
+        if (pl.nk == NK2) go(bwd_dkdv_kernel<D, NK2, BW_NW>, 16 * NK2 * BW_NW);
+        else go(bwd_dkdv_kernel<D, 1, BW_NW>, 16 * BW_NW);
+        if (pl.hs > 1) {
+            const long long plane = (long long)B * Hkv * S * D;
+            hipLaunchKernelGGL(bwd_dkdv_reduce_kernel, dim3((unsigned)ceil_div(plane / 8, 256LL)),
+                               dim3(256), 0, st, (const float*)part, (uint16_t*)dk, (uint16_t*)dv,
+                               plane, pl.hs, scale);
+        }
     }
     {
         const int G = Hq / Hkv;
@@ -592,8 +718,8 @@ hipError_t launch_backward_d(void* dq, void* dk, void* dv, const void* q, const 
 
 }  // namespace
 
-size_t prefill_backward_workspace_bytes(int B, int Hq, int S) {
-    return (size_t)B * Hq * stats_rows(S) * sizeof(float2);
+size_t prefill_backward_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
+    return D == 64 ? backward_workspace_d<64>(B, Hq, Hkv, S) : backward_workspace_d<128>(B, Hq, Hkv, S);
 }
 
 hipError_t launch_prefill_backward(void* dq, void* dk, void* dv, const void* q, const void* k,

@@ -31,8 +31,10 @@ hipError_t launch_prefill(void* o, float* lse, const void* q, const void* k, con
 
 // Backward pass of causal grouped-query prefill (bf16): gradients dq, dk, dv
 // of sum <dout, o>, from q, k, v, the forward output o, dout and the forward's
-// lse.  workspace: prefill_backward_workspace_bytes(B, Hq, S) bytes.
-size_t prefill_backward_workspace_bytes(int B, int Hq, int S);
+// lse.  workspace: prefill_backward_workspace_bytes(B, Hq, Hkv, S, D) bytes
+// (row statistics, and the dK/dV partial sums when the launch splits the
+// group's heads; sized for the current device).
+size_t prefill_backward_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
 hipError_t launch_prefill_backward(void* dq, void* dk, void* dv, const void* q, const void* k,
                                    const void* v, const void* o, const void* dout,
                                    const float* lse, int B, int Hq, int Hkv, int S, int D,

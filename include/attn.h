@@ -135,11 +135,16 @@ int attn_prefill_lse(void *o, float *lse, const void *q, const void *k, const vo
                      double rope_theta, void *stream);
 
 /*
- * Bytes of device workspace attn_prefill_backward needs (0 on invalid sizes):
- * two fp32 row statistics per query row, each head padded to whole 64-row
- * tiles plus one.
+ * Bytes of device workspace attn_prefill_backward needs for these sizes on the
+ * current device (0 on invalid sizes): two fp32 row statistics per query row,
+ * each head padded to whole 64-row tiles plus one, and, when the dk/dv pass
+ * splits the group's query heads over hs = 2 or 4 workgroups per key block
+ * (shapes that would not fill the device three times over), hs fp32 partial
+ * sums of dk and dv ([hs][2][B, Hkv, S, D]).  The split depends on the
+ * device's compute-unit count, so a workspace sized on one device is only
+ * guaranteed for that device.
  */
-size_t attn_prefill_backward_workspace_size(int B, int Hq, int S);
+size_t attn_prefill_backward_workspace_size(int B, int Hq, int Hkv, int S, int D);
 
 /*
  * Backward pass of causal grouped-query prefill ("Compressed Convolutional
@@ -156,10 +161,13 @@ size_t attn_prefill_backward_workspace_size(int B, int Hq, int S);
  * rotation).  bf16 only: bf16 matrix-core products with fp32
  * accumulation, p and ds rounded to bf16 before their products, each
  * gradient rounded once to bf16.  Outputs must not overlap inputs.
- * workspace: at least attn_prefill_backward_workspace_size(B, Hq, S) bytes,
- * 16-byte aligned, contents on entry irrelevant, not shared by calls that may
- * overlap.  Three kernels are enqueued (row statistics, dk/dv, dq); dk and dv
- * sum the group's query heads in registers, so every gradient is written once.
+ * workspace: at least attn_prefill_backward_workspace_size(B, Hq, Hkv, S, D)
+ * bytes (ATTN_ERR_WORKSPACE otherwise), 16-byte aligned, contents on entry
+ * irrelevant, not shared by calls that may overlap.  Three kernels are
+ * enqueued (row statistics, dk/dv, dq); dk and dv sum the group's query heads
+ * in registers and are written once, except for split launches, which write
+ * fp32 partial sums to the workspace and add a fourth kernel that sums them
+ * and rounds once to bf16.
  */
 int attn_prefill_backward(void *dq, void *dk, void *dv, const void *q, const void *k,
                           const void *v, const void *o, const void *dout, const float *lse,

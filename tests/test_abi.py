@@ -131,11 +131,20 @@ def test_prefill_lse_validation(L):
 
 def test_prefill_backward_workspace_and_validation(L):
     ws = L.attn_prefill_backward_workspace_size
-    # two fp32 per row, each head padded to whole 64-row tiles plus one
-    assert ws(2, 8, 100) == 2 * 8 * (128 + 64) * 8
-    assert ws(1, 1, 64) == (64 + 64) * 8
-    assert ws(0, 8, 100) == 0 and ws(1, 0, 5) == 0 and ws(1, 1, 0) == 0
-    need = ws(1, 8, 16)
+    # two fp32 per row, each head padded to whole 64-row tiles plus one (MHA
+    # never splits its heads)
+    assert ws(2, 8, 8, 100, 64) == 2 * 8 * (128 + 64) * 8
+    assert ws(1, 1, 1, 64, 128) == (64 + 64) * 8
+    # a launch far too small to fill a device splits the group's 4 heads over
+    # 4 workgroups per key block: 4 fp32 partial sums of dk and dv follow the
+    # statistics (rounded up to 256 bytes)
+    stats = 1 * 8 * (64 + 64) * 8
+    assert ws(1, 8, 2, 16, 64) == stats + 4 * 2 * (1 * 2 * 16 * 64) * 4
+    # groups of 3 heads have no slicing into 2 or 4: statistics only
+    assert ws(1, 6, 2, 16, 128) == 1 * 6 * (64 + 64) * 8
+    assert ws(0, 8, 2, 100, 64) == 0 and ws(1, 0, 1, 5, 64) == 0 and ws(1, 1, 1, 0, 64) == 0
+    assert ws(1, 8, 3, 16, 64) == 0 and ws(1, 8, 2, 16, 96) == 0 and ws(1, 8, 0, 16, 64) == 0
+    need = ws(1, 8, 2, 16, 64)
     p = lambda *a: L.attn_prefill_backward(*a)
     names = ["dq", "dk", "dv", "q", "k", "v", "o", "dout"]
     args = lambda **kw: [kw.get(n, FAKE) for n in names] + [

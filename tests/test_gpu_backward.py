@@ -213,6 +213,36 @@ def test_prefill_backward_full_size_sampled_rows():
     _assert_grad(dv.reshape(-1, w.D)[kr].double().numpy(), rv, "dv rows")
 
 
+def test_prefill_backward_ccgqa_full_size_sampled_rows():
+    """ccgqa_prefill (2 x 8/2 heads x 16384 x 64) in the launch configuration
+    the benchmark times, where the dK/dV pass splits each group's 4 query heads
+    over 4 workgroups per key block (32 keys per wave) and a fourth kernel sums
+    their fp32 partials: sampled rows against the oracle."""
+    w = wl.WORKLOADS["ccgqa_prefill"]
+    say("backward ccgqa_prefill sampled rows")
+    n_split = attn.prefill_backward_workspace_size(w.B, w.Hq, w.Hkv, w.S, w.D)
+    stats = w.B * w.Hq * (-(-w.S // 64) * 64 + 64) * 8
+    assert n_split == stats + 4 * 2 * w.B * w.Hkv * w.S * w.D * 4  # the split this test is for
+    q, k, v, dout = wl.make_backward(w, seed=5)
+    _, _, dq, dk, dv = _run(q, k, v, dout, w.scale)
+    g = np.random.default_rng(4)
+    S = w.S
+    qr = np.concatenate([g.integers(0, w.B * w.Hq * S, 24),
+                         np.array([0, S - 1, S, 127, 128, w.B * w.Hq * S - 1])])
+    kr = []
+    for b, j in [(0, 0), (w.B - 1, w.Hkv - 1)]:
+        base = (b * w.Hkv + j) * S
+        kr += [base + t for t in (0, 1, 127, 128, S // 2, S - 129, S - 1)]
+        kr += list(base + g.integers(0, S, 5))
+    kr = np.array(kr)
+    rq, rk, rv = oracle.prefill_backward(_bits(q), _bits(k), _bits(v), _bits(dout), q_rows=qr,
+                                         k_rows=kr)
+    allow = _dq_delta_allowance(_bits(q), _bits(k), _bits(v), _bits(dout), w.scale, rows=qr)
+    _assert_grad(dq.reshape(-1, w.D)[qr].double().numpy(), rq, "dq rows", allow)
+    _assert_grad(dk.reshape(-1, w.D)[kr].double().numpy(), rk, "dk rows")
+    _assert_grad(dv.reshape(-1, w.D)[kr].double().numpy(), rv, "dv rows")
+
+
 def test_training_step_with_rope_end_to_end():
     """Forward with the query RoPE fused and K rotated by attn_rope, backward
     on the rotated q and k, then attn_rope_backward for dq and dk: the
@@ -251,7 +281,7 @@ def test_prefill_backward_ignores_workspace_contents():
     q, k, v, dout = (t.cuda() for t in wl.make_backward(w, seed=16))
     say("backward with a NaN-filled workspace")
     o, lse = attn.prefill_lse(q, k, v)
-    n = attn.prefill_backward_workspace_size(w.B, w.Hq, w.S)
+    n = attn.prefill_backward_workspace_size(w.B, w.Hq, w.Hkv, w.S, w.D)
     ws = torch.full((n // 4,), float("nan"), dtype=torch.float32, device="cuda")
     a = attn.prefill_backward(q, k, v, o, dout, lse, workspace=ws)
     b = attn.prefill_backward(q, k, v, o, dout, lse, workspace=ws)
