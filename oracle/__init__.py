@@ -87,6 +87,9 @@ def _load():
             lib.oracle_cca_mix.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, P, P, i, P, P, P,
                                            ctypes.c_double]
             lib.oracle_cca_mix.restype = i
+            lib.oracle_cca_mix_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, i, i, i, i,
+                                                    i, i, P, P, i, P, P, P, ctypes.c_double]
+            lib.oracle_cca_mix_backward.restype = i
             lib.oracle_round_bf16.argtypes = [P, P, ctypes.c_size_t]
             lib.oracle_round_bf16.restype = None
             lib.oracle_round_f32.argtypes = [P, P, ctypes.c_size_t]
@@ -403,3 +406,44 @@ def cca_mix(q: np.ndarray, k: np.ndarray, v: np.ndarray, conv_q: np.ndarray, con
     if rc:
         raise RuntimeError(f"oracle_cca_mix failed ({rc})")
     return qo, ko, vo
+
+
+def cca_mix_backward(gq: np.ndarray, gk: np.ndarray, gv: np.ndarray, q: np.ndarray, k: np.ndarray,
+                     conv_q: np.ndarray, conv_k: np.ndarray, mix_q: np.ndarray, mix_k: np.ndarray,
+                     pos_offset=None, theta: float = 0.0):
+    """Gradients of the CCA pre-attention operations (oracle.c,
+    oracle_cca_mix_backward): given gq [B,Hq,S,D], gk, gv [B,Hkv,S,D], the
+    gradients of a loss with respect to cca_mix's outputs (q and k as rotated),
+    and the latent q~, k~ and the weights that produced them, returns fp64
+    (dq~, dk~, dv~, dconv_q, dconv_k, dmix_q, dmix_k); the weight gradients are
+    summed over the batch and the tokens.  All inputs share one dtype."""
+    dt = _dtype_of(gq)
+    gq, gk, gv, q, k, conv_q, conv_k, mix_q, mix_k = (
+        _as_input(t, dt) for t in (gq, gk, gv, q, k, conv_q, conv_k, mix_q, mix_k))
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    W = conv_q.shape[1]
+    if (gq.shape != q.shape or k.shape != (B, Hkv, S, D) or gk.shape != k.shape
+            or gv.shape != k.shape or Hq % Hkv or D % 2
+            or conv_q.shape != (Hq, W, D) or conv_k.shape != (Hkv, W, D)
+            or mix_q.shape != (Hq, D, D) or mix_k.shape != (Hkv, D, D)):
+        raise ValueError("bad shapes")
+    off = None
+    if pos_offset is not None:
+        off = np.ascontiguousarray(pos_offset, dtype=np.int32)
+        if off.shape != (B,):
+            raise ValueError("pos_offset must have shape [B]")
+    dq = np.empty((B, Hq, S, D), dtype=np.float64)
+    dk = np.empty((B, Hkv, S, D), dtype=np.float64)
+    dv = np.empty((B, Hkv, S, D), dtype=np.float64)
+    dcq = np.empty((Hq, W, D), dtype=np.float64)
+    dck = np.empty((Hkv, W, D), dtype=np.float64)
+    dmq = np.empty((Hq, D, D), dtype=np.float64)
+    dmk = np.empty((Hkv, D, D), dtype=np.float64)
+    rc = _load().oracle_cca_mix_backward(
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dcq), _ptr(dck), _ptr(dmq), _ptr(dmk), _ptr(gq),
+        _ptr(gk), _ptr(gv), _ptr(q), _ptr(k), _DT_CODE[dt], B, Hq, Hkv, S, D, _ptr(conv_q),
+        _ptr(conv_k), W, _ptr(mix_q), _ptr(mix_k), _ptr(off), float(theta))
+    if rc:
+        raise RuntimeError(f"oracle_cca_mix_backward failed ({rc})")
+    return dq, dk, dv, dcq, dck, dmq, dmk

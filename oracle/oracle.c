@@ -715,3 +715,151 @@ int oracle_cca_mix(double *q_out, double *k_out, double *v_out, const void *q, c
     }
     return 0;
 }
+
+/* Gradients of the CCA pre-attention operations (oracle_cca_mix) by the chain
+ * rule, taken through its steps in reverse order.  Given gq = dL/dq, gk =
+ * dL/dk (with respect to the rotated outputs) and gv = dL/dv:
+ *   (4)  a_q = R_t^T gq, a_k = R_t^T gk (the transposed rotation at the same
+ *        positions; a = g when theta == 0);
+ *   (2c) the mean reaches every query head of the group and its key head, so
+ *        dm[t, j] = sum_{h in group j} a_q[t, h] + a_k[t, j], and
+ *        dq~[t, h] += dm[t, j] / (2 G),  dk~[t, j] += dm[t, j] / 2;
+ *   (2b) z = M s:  ds[t, c'] = sum_c mix[h, c, c'] a[t, c]   (M^T a),
+ *        dmix[h, c, c'] += sum_{b, t} a[t, c] s[t, c'];
+ *   (2a) s[t] = sum_i conv[h, i] x[t - i]:
+ *        dx[t, c] += sum_{i < W, t + i < S} conv[h, i, c] ds[t + i, c],
+ *        dconv[h, i, c] += sum_{b, t >= i} ds[t, c] x[t - i, c];
+ *   (3)  dv~[t, c] = gv[t, c] for c < D/2, gv[t + 1, c] for c >= D/2 (0 at
+ *        the last token).
+ * Weight gradients sum over the batch and every token.  Inputs (gradients,
+ * latent q~, k~, weights) share the element type dt; outputs are fp64:
+ * dq [B, Hq, S, D], dk and dv [B, Hkv, S, D], dconv_q [Hq, W, D], dconv_k
+ * [Hkv, W, D], dmix_q [Hq, D, D], dmix_k [Hkv, D, D]. */
+int oracle_cca_mix_backward(double *dq, double *dk, double *dv, double *dconv_q, double *dconv_k,
+                            double *dmix_q, double *dmix_k, const void *gq, const void *gk,
+                            const void *gv, const void *q, const void *k, int dt, int B, int Hq,
+                            int Hkv, int S, int D, const void *conv_q, const void *conv_k, int W,
+                            const void *mix_q, const void *mix_k, const int32_t *pos_offset,
+                            double theta)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || W <= 0 || Hq % Hkv != 0 || D % 2)
+        return 1;
+    const int G = Hq / Hkv;
+    const size_t nq = (size_t)B * Hq * S * D, nk = (size_t)B * Hkv * S * D;
+    /* (4) back through the rotation */
+    double *aq = (double *)malloc(sizeof(double) * nq);
+    double *ak = (double *)malloc(sizeof(double) * nk);
+    double *dm = (double *)malloc(sizeof(double) * nk);
+    if (!aq || !ak || !dm) {
+        free(aq);
+        free(ak);
+        free(dm);
+        return 2;
+    }
+    if (theta > 0.0) {
+        oracle_rope_transpose(aq, gq, dt, B, Hq, S, D, pos_offset, theta);
+        oracle_rope_transpose(ak, gk, dt, B, Hkv, S, D, pos_offset, theta);
+    } else {
+        for (size_t i = 0; i < nq; ++i)
+            aq[i] = load(gq, i, dt);
+        for (size_t i = 0; i < nk; ++i)
+            ak[i] = load(gk, i, dt);
+    }
+    /* (2c) the mean's gradient per (b, j, t) */
+    for (int b = 0; b < B; ++b)
+        for (int j = 0; j < Hkv; ++j)
+            for (int t = 0; t < S; ++t)
+                for (int c = 0; c < D; ++c) {
+                    const size_t at = (((size_t)b * Hkv + j) * S + t) * D + c;
+                    double sum = ak[at];
+                    for (int r = 0; r < G; ++r)
+                        sum += aq[(((size_t)b * Hq + (size_t)j * G + r) * S + t) * D + c];
+                    dm[at] = sum;
+                }
+    int bad = 0;
+    /* (2b), (2a) per head: one head per thread, so each weight gradient is summed
+     * by one thread in a fixed order */
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)S * D);
+        double *ds = (double *)malloc(sizeof(double) * (size_t)S * D);
+        if (!s || !ds) {
+#pragma omp atomic write
+            bad = 2;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int n = 0; n < Hq + Hkv; ++n) {
+                const int isq = n < Hq;
+                const int h = isq ? n : n - Hq;
+                const int H = isq ? Hq : Hkv;
+                const void *x = isq ? q : k;
+                const void *cw = isq ? conv_q : conv_k;
+                const void *mw = isq ? mix_q : mix_k;
+                const double *a = isq ? aq : ak;
+                double *dx = isq ? dq : dk;
+                double *dconv = (isq ? dconv_q : dconv_k) + (size_t)h * W * D;
+                double *dmix = (isq ? dmix_q : dmix_k) + (size_t)h * D * D;
+                const int j = isq ? h / G : h;
+                const double mean_w = isq ? 0.5 / G : 0.5;
+                for (size_t i = 0; i < (size_t)W * D; ++i)
+                    dconv[i] = 0.0;
+                for (size_t i = 0; i < (size_t)D * D; ++i)
+                    dmix[i] = 0.0;
+                for (int b = 0; b < B; ++b) {
+                    const size_t row0 = ((size_t)b * H + h) * S; /* first row of this head */
+                    /* the forward's convolution output s, and ds = M^T a */
+                    for (int t = 0; t < S; ++t)
+                        for (int c = 0; c < D; ++c) {
+                            double acc = 0.0;
+                            for (int i = 0; i < W && t - i >= 0; ++i) {
+                                const double tap = load(cw, ((size_t)h * W + i) * D + c, dt);
+                                acc += tap * load(x, (row0 + t - i) * D + c, dt);
+                            }
+                            s[(size_t)t * D + c] = acc;
+                            double g = 0.0;
+                            for (int c2 = 0; c2 < D; ++c2)
+                                g += load(mw, ((size_t)h * D + c2) * D + c, dt) *
+                                     a[(row0 + t) * D + c2];
+                            ds[(size_t)t * D + c] = g;
+                        }
+                    for (int t = 0; t < S; ++t)
+                        for (int c = 0; c < D; ++c) {
+                            /* mix gradient: a (output channel c) times s (input c2) */
+                            const double av = a[(row0 + t) * D + c];
+                            for (int c2 = 0; c2 < D; ++c2)
+                                dmix[(size_t)c * D + c2] += av * s[(size_t)t * D + c2];
+                            /* input gradient: the convolution's taps run forward in time */
+                            double acc = 0.0;
+                            for (int i = 0; i < W && t + i < S; ++i) {
+                                const double tap = load(cw, ((size_t)h * W + i) * D + c, dt);
+                                acc += tap * ds[(size_t)(t + i) * D + c];
+                            }
+                            const size_t mat = (((size_t)b * Hkv + j) * S + t) * D + c;
+                            dx[(row0 + t) * D + c] = acc + mean_w * dm[mat];
+                            /* tap gradient */
+                            for (int i = 0; i < W && t - i >= 0; ++i)
+                                dconv[(size_t)i * D + c] +=
+                                    ds[(size_t)t * D + c] * load(x, (row0 + t - i) * D + c, dt);
+                        }
+                }
+            }
+        }
+        free(s);
+        free(ds);
+    }
+    /* (3) value shift */
+    for (int b = 0; b < B; ++b)
+        for (int j = 0; j < Hkv; ++j)
+            for (int t = 0; t < S; ++t)
+                for (int c = 0; c < D; ++c) {
+                    const size_t at = (((size_t)b * Hkv + j) * S + t) * D + c;
+                    if (c < D / 2)
+                        dv[at] = load(gv, at, dt);
+                    else
+                        dv[at] = t + 1 < S ? load(gv, at + (size_t)D, dt) : 0.0;
+                }
+    free(aq);
+    free(ak);
+    free(dm);
+    return bad;
+}

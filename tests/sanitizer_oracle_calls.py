@@ -93,5 +93,10 @@ for dt in ("f64", "bf16"):
         oracle.cca_mix(q, k, v, cq, ck, mq, mk)
         oracle.cca_mix(q, k, v, cq, ck, mq, mk, pos_offset=np.arange(B, dtype=np.int32) * 7,
                        theta=1e4)
+        # and its backward, with gradients drawn like the inputs
+        gq, gk, gv = draw((B, Hq, S, D), dt), draw((B, Hkv, S, D), dt), draw((B, Hkv, S, D), dt)
+        oracle.cca_mix_backward(gq, gk, gv, q, k, cq, ck, mq, mk)
+        oracle.cca_mix_backward(gq, gk, gv, q, k, cq, ck, mq, mk,
+                                pos_offset=np.arange(B, dtype=np.int32) * 7, theta=1e4)
 
 print("all oracle calls done", flush=True)

@@ -78,6 +78,19 @@ MUTANTS = {
                                   "val = t + 1 < S ? load(v, at + (size_t)D, dt) : 0.0;"),
     "cca_rope_misses_keys": ("oracle_rope(k_out, tmp, OR_F64, B, Hkv, S, D, pos_offset, theta);",
                              "memcpy(k_out, tmp, sizeof(double) * (size_t)B * Hkv * S * D);"),
+    "cca_bwd_mix_not_transposed": ("g += load(mw, ((size_t)h * D + c2) * D + c, dt) *",
+                                   "g += load(mw, ((size_t)h * D + c) * D + c2, dt) *"),
+    "cca_bwd_conv_not_reversed": ("acc += tap * ds[(size_t)(t + i) * D + c];",
+                                  "acc += tap * (t - i >= 0 ? ds[(size_t)(t - i) * D + c] : 0.0);"),
+    "cca_bwd_mean_weight_without_group": ("const double mean_w = isq ? 0.5 / G : 0.5;",
+                                          "const double mean_w = 0.5;"),
+    "cca_bwd_shift_from_previous_token": ("dv[at] = t + 1 < S ? load(gv, at + (size_t)D, dt) : 0.0;",
+                                          "dv[at] = t > 0 ? load(gv, at - (size_t)D, dt) : 0.0;"),
+    "cca_bwd_no_rope_transpose": ("if (theta > 0.0) {\n        oracle_rope_transpose(aq",
+                                  "if (0) {\n        oracle_rope_transpose(aq"),
+    "cca_bwd_dmix_transposed": ("dmix[(size_t)c * D + c2] += av *", "dmix[(size_t)c2 * D + c] += av *"),
+    "cca_bwd_dconv_unshifted": ("ds[(size_t)t * D + c] * load(x, (row0 + t - i) * D + c, dt);",
+                                "ds[(size_t)t * D + c] * load(x, (row0 + t) * D + c, dt);"),
 }
 
 

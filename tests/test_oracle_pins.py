@@ -912,3 +912,85 @@ def test_cca_mix_widens_bf16_inputs_exactly():
     ref = oracle.cca_mix(*(oracle.widen(b) for b in bits), theta=500.0)
     for g_, r_ in zip(got, ref):
         assert np.array_equal(g_, r_)
+
+
+# ---------------------------------------------------------------------------
+# CCA backward (oracle_cca_mix_backward).  The forward map is linear in each
+# of q~, k~, v~, conv and mix when the others are held fixed, so for any
+# direction u the exact directional derivative of L = <gq, q> + <gk, k> +
+# <gv, v> is L(argument = u) - L(argument = 0): the pins below use only the
+# pinned forward oracle, never a gradient formula.
+# ---------------------------------------------------------------------------
+def _cca_loss(grads, args, pos_offset, theta):
+    outs = oracle.cca_mix(*args, pos_offset=pos_offset, theta=theta)
+    return sum(float((g * o).sum()) for g, o in zip(grads, outs))
+
+
+CCA_BWD_GEOMS = [  # B, Hq, Hkv, S, D, W
+    (2, 4, 2, 7, 8, 3),
+    (1, 3, 1, 5, 6, 4),    # MQA, G = 3, W close to S
+    (1, 2, 2, 6, 4, 1),    # MHA, one tap
+    (1, 4, 2, 2, 8, 4),    # fewer tokens than taps
+]
+
+
+@pytest.mark.parametrize("geom", CCA_BWD_GEOMS)
+@pytest.mark.parametrize("theta", [0.0, 100.0])
+def test_cca_backward_is_the_derivative_of_the_forward(geom, theta):
+    B, Hq, Hkv, S, D, W = geom
+    args = list(_cca_inputs(B, Hq, Hkv, S, D, W, 70 + S))
+    g = np.random.default_rng(90 + D)
+    grads = [g.standard_normal((B, Hq, S, D)), g.standard_normal((B, Hkv, S, D)),
+             g.standard_normal((B, Hkv, S, D))]
+    off = np.arange(B, dtype=np.int32) * 3 + 1
+    q, k, v, cq, ck, mq, mk = args
+    got = oracle.cca_mix_backward(*grads, q, k, cq, ck, mq, mk, pos_offset=off, theta=theta)
+    # argument ai of cca_mix (q~, k~, v~, conv_q, conv_k, mix_q, mix_k) has its
+    # gradient at position ai of the result
+    for ai in range(7):
+        for trial in range(2):
+            u = g.standard_normal(args[ai].shape)
+            with_u = list(args)
+            with_u[ai] = u
+            zero = list(args)
+            zero[ai] = np.zeros_like(args[ai])
+            ref = _cca_loss(grads, with_u, off, theta) - _cca_loss(grads, zero, off, theta)
+            val = float((got[ai] * u).sum())
+            assert abs(val - ref) <= 1e-9 * (1.0 + abs(ref)), (ai, val, ref)
+
+
+def test_cca_backward_with_identity_weights_is_plain_algebra():
+    # one unit tap, identity mix, no rotation: q = q~ + m, k = k~ + m, so
+    # dq~ = gq + dm / (2G), dk~ = gk + dm / 2 with dm the group's gq sum plus gk;
+    # the mix gradient is sum_t gq s^T with s = q~; the tap gradient sum_t ds x
+    B, Hq, Hkv, S, D = 2, 4, 2, 5, 6
+    G = Hq // Hkv
+    g = np.random.default_rng(5)
+    q, k = g.standard_normal((B, Hq, S, D)), g.standard_normal((B, Hkv, S, D))
+    gq, gk, gv = (g.standard_normal(s) for s in [(B, Hq, S, D), (B, Hkv, S, D), (B, Hkv, S, D)])
+    cq, ck = np.ones((Hq, 1, D)), np.ones((Hkv, 1, D))
+    mq, mk = np.tile(np.eye(D), (Hq, 1, 1)), np.tile(np.eye(D), (Hkv, 1, 1))
+    dq, dk, dv, dcq, dck, dmq, dmk = oracle.cca_mix_backward(gq, gk, gv, q, k, cq, ck, mq, mk)
+    dm = gq.reshape(B, Hkv, G, S, D).sum(2) + gk
+    assert np.allclose(dq, gq + np.repeat(dm, G, axis=1) / (2 * G), atol=1e-12)
+    assert np.allclose(dk, gk + dm / 2, atol=1e-12)
+    assert np.allclose(dmq, np.einsum("bhtc,bhtd->hcd", gq, q), atol=1e-12)
+    assert np.allclose(dcq[:, 0, :], (gq * q).sum(axis=(0, 2)), atol=1e-12)
+    assert np.allclose(dck[:, 0, :], (gk * k).sum(axis=(0, 2)), atol=1e-12)
+    # the shift: the first half in place, the second half from the next token
+    assert np.array_equal(dv[..., : D // 2], gv[..., : D // 2])
+    assert np.array_equal(dv[..., :-1, D // 2:], gv[..., 1:, D // 2:])
+    assert not dv[..., -1, D // 2:].any()
+
+
+def test_cca_backward_widens_bf16_inputs_exactly():
+    B, Hq, Hkv, S, D, W = 1, 4, 2, 6, 8, 2
+    q, k, v, cq, ck, mq, mk = _cca_inputs(B, Hq, Hkv, S, D, W, 71)
+    g = np.random.default_rng(72)
+    grads = [g.standard_normal((B, Hq, S, D)), g.standard_normal((B, Hkv, S, D)),
+             g.standard_normal((B, Hkv, S, D))]
+    ins = [oracle.round_bf16(a) for a in grads + [q, k, cq, ck, mq, mk]]
+    got = oracle.cca_mix_backward(*ins, theta=500.0)
+    ref = oracle.cca_mix_backward(*(oracle.widen(b) for b in ins), theta=500.0)
+    for g_, r_ in zip(got, ref):
+        assert np.array_equal(g_, r_)
