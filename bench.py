@@ -298,6 +298,13 @@ def cca_bytes(w):
     return float(2 * 2 * w.B * w.S * w.D * (w.Hq + 2 * w.Hkv))
 
 
+def cca_backward_bytes(w):
+    """Algorithmic HBM bytes of the CCA backward: the gradients gq, gk, gv and
+    the latent q~, k~ read once, dq~, dk~, dv~ written once (bf16); the
+    weights and their fp32 gradients are negligible."""
+    return float(2 * w.B * w.S * w.D * (2 * (w.Hq + 2 * w.Hkv) + w.Hq + w.Hkv))
+
+
 def bench_cca_step(w, steps, warmup):
     """The compressed-latent layer's attention step: the CCA pre-attention
     pass (causal sequence convolution, channel mix, QK-mean, RoPE of q and k,
@@ -373,6 +380,27 @@ def bench_cca_step(w, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     dec_us = e0.elapsed_time(e1) / 100 * 1e3
+
+    # the backward of the pass, given gradients of its outputs
+    grads = [t.cuda() for t in wl.make_cca_grads(w, seed=1)]
+    bws = torch.empty(attn.cca_mix_backward_workspace_size(w.B, w.Hq, w.Hkv, w.S, w.D,
+                                                           wl.CCA_CONV_WIDTH),
+                      dtype=torch.uint8, device="cuda")
+
+    def bstep():
+        attn.cca_mix_backward(*grads, ins[0], ins[1], *ins[3:], rope_theta=w.theta, workspace=bws)
+
+    for _ in range(warmup + 2):
+        bstep()
+    torch.cuda.synchronize()
+    bevs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(steps)]
+    for i in range(steps):
+        bevs[i][0].record(stream)
+        bstep()
+        bevs[i][1].record(stream)
+    torch.cuda.synchronize()
+    bwd_ms = sum(a.elapsed_time(b) for a, b in bevs) / steps
+    bwd_gbs = cca_backward_bytes(w) / (bwd_ms * 1e-3) / 1e9
     return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
             "head_dim": w.D, "seq_len": w.S, "rope_theta": w.theta,
             "conv_width": wl.CCA_CONV_WIDTH,
@@ -384,6 +412,10 @@ def bench_cca_step(w, steps, warmup):
             "step_TFLOP_per_s": round(flops / (ms_step * 1e-3) / 1e12, 1), "steps": steps,
             "step": "CCA pre-attention pass (conv, channel mix, QK-mean, RoPE, value shift) + "
                     "causal GQA prefill",
+            "cca_backward_ms_mean": round(bwd_ms, 5), "cca_backward_bytes": cca_backward_bytes(w),
+            "cca_backward_GB_per_s": round(bwd_gbs, 1),
+            "cca_backward": "attn_cca_mix_backward: input gradients (bf16) and weight gradients "
+                            "(fp32, summed over the batch and tokens) of the pass, three kernels",
             "cca_decode_step_us": round(dec_us, 2),
             "cca_decode_step": f"attn_cca_mix_decode: one new token for each of {Bd} sequences "
                                f"(token indices 1024..8192), 100 steps replayed from a HIP graph"}
@@ -543,7 +575,8 @@ def main():
     ca = bench_cca_step(wl.WORKLOADS["ccgqa_prefill"], args.steps, args.warmup)
     log(f"ccgqa with the CCA pass: mix {ca['cca_mix_ms_mean']:.4f} ms ({ca['cca_mix_GB_per_s']:.0f} GB/s), "
         f"prefill {ca['prefill_ms_mean']:.4f} ms, step {ca['ms_per_step']:.4f} ms; "
-        f"decode step {ca['cca_decode_step_us']:.1f} us")
+        f"decode step {ca['cca_decode_step_us']:.1f} us; backward {ca['cca_backward_ms_mean']:.4f} ms "
+        f"({ca['cca_backward_GB_per_s']:.0f} GB/s)")
     result["ccgqa_cca_step"] = ca
     if not args.no_decode:
         dec = {}

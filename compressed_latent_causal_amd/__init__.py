@@ -17,6 +17,9 @@ fallback: calling into the library without the built ``libattn.so`` raises.
     decode_workspace_size(B, Hq, Hkv, max_len, D)
     cca_mix(q, k, v, conv_q, conv_k, mix_q, mix_k, rope_theta=0.0, pos_offset=None,
             q_out=None, k_out=None, v_out=None)
+    cca_mix_backward(gq, gk, gv, q, k, conv_q, conv_k, mix_q, mix_k, rope_theta=0.0,
+                     pos_offset=None, workspace=None)
+    cca_mix_backward_workspace_size(B, Hq, Hkv, S, D, W)
     cca_mix_decode(q, k, v, conv_q, conv_k, mix_q, mix_k, t, q_state, k_state, v_state,
                    rope_theta=0.0, pos_offset=None, q_out=None, k_out=None, v_out=None)
 
@@ -33,7 +36,8 @@ from ._lib import (  # noqa: F401
 
 __all__ = ["rope", "rope_backward", "prefill", "prefill_lse", "prefill_backward", "prefill_backward_workspace_size",
            "decode", "decode_noalloc", "decode_paged", "decode_workspace_size", "AttnError",
-           "lib_path", "DECODE_SCRATCH_BYTES", "cca_mix"]
+           "lib_path", "DECODE_SCRATCH_BYTES", "cca_mix", "cca_mix_decode", "cca_mix_backward",
+           "cca_mix_backward_workspace_size"]
 
 
 def _torch():
@@ -347,6 +351,50 @@ def cca_mix(q, k, v, conv_q, conv_k, mix_q, mix_k, rope_theta: float = 0.0, pos_
           conv_k.data_ptr(), W, mix_q.data_ptr(), mix_k.data_ptr(), po, float(rope_theta),
           _stream(q))
     return q_out, k_out, v_out
+
+
+def cca_mix_backward_workspace_size(B: int, Hq: int, Hkv: int, S: int, D: int, W: int) -> int:
+    return int(lib().attn_cca_mix_backward_workspace_size(B, Hq, Hkv, S, D, W))
+
+
+def cca_mix_backward(gq, gk, gv, q, k, conv_q, conv_k, mix_q, mix_k, rope_theta: float = 0.0,
+                     pos_offset=None, workspace=None):
+    """Gradients of cca_mix: given gq [B,Hq,S,D], gk, gv [B,Hkv,S,D] (bf16), the
+    gradients with respect to cca_mix's outputs (q and k as rotated), and the
+    latent q, k and the weights of that call, returns (dq, dk, dv) (bf16, like
+    the latent inputs) and (dconv_q, dconv_k, dmix_q, dmix_k) (fp32, like the
+    weights' shapes), the weight gradients summed over the batch and tokens."""
+    torch = _torch()
+    B, Hq, Hkv, S, D = _check_prefill_shapes(q, k, k)
+    W = conv_q.shape[1] if conv_q.dim() == 3 else -1
+    if (conv_q.shape != (Hq, W, D) or conv_k.shape != (Hkv, W, D) or mix_q.shape != (Hq, D, D)
+            or mix_k.shape != (Hkv, D, D)):
+        raise ValueError("conv_q [Hq,W,D], conv_k [Hkv,W,D], mix_q [Hq,D,D], mix_k [Hkv,D,D]")
+    if gq.shape != q.shape or gk.shape != k.shape or gv.shape != k.shape:
+        raise ValueError("gq like q, gk and gv like k")
+    if any(t.dtype != q.dtype for t in (gq, gk, gv, k, conv_q, conv_k, mix_q, mix_k)):
+        raise ValueError("all tensors share one dtype")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dcq, dck = torch.empty((Hq, W, D), **f32), torch.empty((Hkv, W, D), **f32)
+    dmq, dmk = torch.empty((Hq, D, D), **f32), torch.empty((Hkv, D, D), **f32)
+    po = 0
+    if pos_offset is not None:
+        if pos_offset.dtype != torch.int32 or pos_offset.shape != (B,):
+            raise ValueError("pos_offset must be int32 [B]")
+        _check_dev(pos_offset)
+        po = pos_offset.data_ptr()
+    if workspace is None:
+        workspace = torch.empty(max(1, cca_mix_backward_workspace_size(B, Hq, Hkv, S, D, W)),
+                                dtype=torch.uint8, device=q.device)
+    _check_dev(gq, gk, gv, q, k, conv_q, conv_k, mix_q, mix_k, workspace)
+    _call(lib().attn_cca_mix_backward, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+          dcq.data_ptr(), dck.data_ptr(), dmq.data_ptr(), dmk.data_ptr(), gq.data_ptr(),
+          gk.data_ptr(), gv.data_ptr(), q.data_ptr(), k.data_ptr(), _dtype_code(q), B, Hq, Hkv, S,
+          D, conv_q.data_ptr(), conv_k.data_ptr(), W, mix_q.data_ptr(), mix_k.data_ptr(), po,
+          float(rope_theta), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+          _stream(q))
+    return (dq, dk, dv), (dcq, dck, dmq, dmk)
 
 
 def cca_mix_decode(q, k, v, conv_q, conv_k, mix_q, mix_k, t, q_state, k_state, v_state,

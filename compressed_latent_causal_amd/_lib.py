@@ -38,6 +38,9 @@ SIGNATURES = {
     "attn_decode_noalloc": (I, [P, P, P, P, I, I, I, I, I, I, P, I, F, D, P]),
     "attn_decode_paged": (I, [P, P, P, P, I, I, I, I, I, I, I, P, I, P, I, I, F, D, P, SZ, P]),
     "attn_cca_mix": (I, [P, P, P, P, P, P, I, I, I, I, I, I, P, P, I, P, P, P, D, P]),
+    "attn_cca_mix_backward_workspace_size": (SZ, [I, I, I, I, I, I]),
+    "attn_cca_mix_backward": (I, [P, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, I, P, P,
+                                  P, D, P, SZ, P]),
     "attn_cca_mix_decode": (I, [P, P, P, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, P, P, P, D,
                                 P]),
     "attn_status_string": (ctypes.c_char_p, [I]),

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["api.hip", "rope.hip", "prefill.hip", "decode.hip", "decode_f32.hip", "backward.hip",
-           "cca.hip"]
+           "cca.hip", "cca_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -231,6 +231,53 @@ ATTN_API int attn_cca_mix(void* q_out, void* k_out, void* v_out, const void* q, 
                                            rope_theta, (hipStream_t)stream));
 }
 
+ATTN_API size_t attn_cca_mix_backward_workspace_size(int B, int Hq, int Hkv, int S, int D,
+                                                     int conv_width) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S < 1 || !supported_dim(D)) return 0;
+    if (conv_width < 1 || conv_width > attn::cca_bwd_max_width()) return 0;
+    return attn::cca_bwd_workspace_bytes(B, Hq, Hkv, S, D, conv_width);
+}
+
+ATTN_API int attn_cca_mix_backward(void* dq, void* dk, void* dv, float* dconv_q, float* dconv_k,
+                                   float* dmix_q, float* dmix_k, const void* gq, const void* gk,
+                                   const void* gv, const void* q, const void* k, int dtype, int B,
+                                   int Hq, int Hkv, int S, int D, const void* conv_q,
+                                   const void* conv_k, int conv_width, const void* mix_q,
+                                   const void* mix_k, const int32_t* pos_offset,
+                                   double rope_theta, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    if (B < 0 || S < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_BF16 || !supported_dim(D)) return ATTN_ERR_UNSUPPORTED;
+    if (conv_width < 1 || conv_width > attn::cca_bwd_max_width()) return ATTN_ERR_UNSUPPORTED;
+    if (!(rope_theta >= 0.0) || !isfinite(rope_theta)) return ATTN_ERR_UNSUPPORTED;
+    // one workgroup per (sequence, head, 256-token chunk)
+    if ((long long)B * (Hq + Hkv) * ((S + 255) / 256) >= (1ll << 31)) return ATTN_ERR_SHAPE;
+    if (!dconv_q || !dconv_k || !dmix_q || !dmix_k) return ATTN_ERR_NULL;
+    if (((uintptr_t)dconv_q & 3u) || ((uintptr_t)dconv_k & 3u) || ((uintptr_t)dmix_q & 3u) ||
+        ((uintptr_t)dmix_k & 3u))
+        return ATTN_ERR_ALIGN;
+    if (B > 0 && S > 0) {
+        if (!dq || !dk || !dv || !gq || !gk || !gv || !q || !k || !conv_q || !conv_k || !mix_q ||
+            !mix_k)
+            return ATTN_ERR_NULL;
+        if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(gq) ||
+            !aligned16(gk) || !aligned16(gv) || !aligned16(q) || !aligned16(k) ||
+            !aligned16(mix_q) || !aligned16(mix_k) || ((uintptr_t)conv_q & 1u) ||
+            ((uintptr_t)conv_k & 1u) || ((uintptr_t)pos_offset & 3u))
+            return ATTN_ERR_ALIGN;
+        if (!workspace ||
+            workspace_bytes < attn::cca_bwd_workspace_bytes(B, Hq, Hkv, S, D, conv_width))
+            return ATTN_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+    }
+    // with no token the weight gradients are zero (written by the reduce over
+    // no partial sums); the input gradients are empty
+    return hip_status(attn::launch_cca_bwd(dq, dk, dv, dconv_q, dconv_k, dmix_q, dmix_k, gq, gk,
+                                           gv, q, k, B, Hq, Hkv, S, D, conv_q, conv_k, conv_width,
+                                           mix_q, mix_k, pos_offset, rope_theta, workspace,
+                                           (hipStream_t)stream));
+}
+
 ATTN_API int attn_cca_mix_decode(void* q_out, void* k_out, void* v_out, const void* q,
                                  const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
                                  int D, const void* conv_q, const void* conv_k, int conv_width,

@@ -94,4 +94,15 @@ hipError_t launch_cca_decode(void* q_out, void* k_out, void* v_out, const void* 
                              void* q_state, void* k_state, void* v_state, const int32_t* tok,
                              const int32_t* pos_offset, double rope_theta, hipStream_t st);
 
+// Backward of the CCA pre-attention operations (bf16 in, bf16 input gradients,
+// fp32 weight gradients); workspace of cca_bwd_workspace_bytes bytes.
+int cca_bwd_max_width();
+size_t cca_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int W);
+hipError_t launch_cca_bwd(void* dq, void* dk, void* dv, float* dconv_q, float* dconv_k,
+                          float* dmix_q, float* dmix_k, const void* gq, const void* gk,
+                          const void* gv, const void* q, const void* k, int B, int Hq, int Hkv,
+                          int S, int D, const void* conv_q, const void* conv_k, int W,
+                          const void* mix_q, const void* mix_k, const int32_t* pos_offset,
+                          double rope_theta, void* workspace, hipStream_t st);
+
 }  // namespace attn

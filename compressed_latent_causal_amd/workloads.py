@@ -143,6 +143,16 @@ def make_cca(w: Workload, seed: int = 0, width: int = CCA_CONV_WIDTH):
     return q, k, v, conv_q, conv_k, mix_q, mix_k
 
 
+def make_cca_grads(w: Workload, seed: int = 0):
+    """Gradients for the CCA backward (CPU, dtype of the workload): gq
+    [B,Hq,S,D], gk, gv [B,Hkv,S,D] ~ N(0, 1), standing in for what the
+    attention backward returns for the mixed q, k, v."""
+    g = torch.Generator().manual_seed(seed)
+    return (_randn(g, (w.B, w.Hq, w.S, w.D), w.torch_dtype),
+            _randn(g, (w.B, w.Hkv, w.S, w.D), w.torch_dtype),
+            _randn(g, (w.B, w.Hkv, w.S, w.D), w.torch_dtype))
+
+
 def poison_cache_tail(cache: torch.Tensor, lens: torch.Tensor) -> None:
     """Write NaN into cache[b, :, t, :] for every t >= lens[b] (in place)."""
     for b in range(cache.shape[0]):

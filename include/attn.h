@@ -351,6 +351,48 @@ int attn_cca_mix_decode(void *q_out, void *k_out, void *v_out, const void *q, co
                         const int32_t *t, const int32_t *pos_offset, double rope_theta,
                         void *stream);
 
+/*
+ * Bytes of device workspace attn_cca_mix_backward needs (0 on invalid sizes):
+ * the mean's fp32 gradient [B, Hkv, S, D] and fp32 partial weight gradients
+ * per (sequence, 256-token chunk, head).
+ */
+size_t attn_cca_mix_backward_workspace_size(int B, int Hq, int Hkv, int S, int D, int conv_width);
+
+/*
+ * Backward pass of attn_cca_mix ("Compressed Convolutional Attention"
+ * summary, "Resultaten" 2 reports a backward pass for CCA; the formulas are
+ * the chain rule through the operations of "Methodologie" items 2 to 4, taken
+ * in reverse order).  Given gq, gk, gv, the gradients of a loss with respect
+ * to attn_cca_mix's outputs q, k (as rotated) and v, and the latent q~, k~ and
+ * weights of that call, it returns the gradients with respect to q~, k~, v~
+ * and the weights:
+ *   a = R_t^T g (the transposed rotation at pos_offset[b] + t; a = g when
+ *     rope_theta == 0);  dm[t,j] = sum_{h in group j} a_q[t,h] + a_k[t,j];
+ *   ds[t] = M^T a[t];  dq~[t,h] = sum_{i < W, t+i < S} w_i (.) ds[t+i] + dm[t,j]/(2G),
+ *     dk~[t,j] likewise with dm[t,j]/2;
+ *   dmix[h] = sum_{b,t} a[t] s[t]^T (s the forward's convolution output);
+ *   dconv[h,i] = sum_{b, t >= i} ds[t] (.) x~[t-i];
+ *   dv~[t,c] = gv[t,c] for c < D/2, gv[t+1,c] for c >= D/2 (0 at t = S-1).
+ * gq, dq: [B, Hq, S, D];  gk, gv, k~, dk, dv: [B, Hkv, S, D], bf16;  dconv_q
+ * [Hq, W, D], dconv_k [Hkv, W, D], dmix_q [Hq, D, D], dmix_k [Hkv, D, D]:
+ * fp32 device arrays (4-byte aligned), written (not accumulated into); with
+ * B == 0 or S == 0 they are set to zero and nothing else is touched.  Other
+ * arguments as for attn_cca_mix (W in 1..8).  Arithmetic is fp32; dq, dk, dv
+ * are rounded once to bf16.  workspace: at least
+ * attn_cca_mix_backward_workspace_size(B, Hq, Hkv, S, D, conv_width) bytes,
+ * 16-byte aligned, contents on entry irrelevant, not shared by calls that may
+ * overlap (ATTN_ERR_WORKSPACE otherwise).  Outputs must not overlap inputs.
+ * Three kernels are enqueued (the mean's gradient and dv, the per-head pass,
+ * the reduction of the weight gradients).
+ */
+int attn_cca_mix_backward(void *dq, void *dk, void *dv, float *dconv_q, float *dconv_k,
+                          float *dmix_q, float *dmix_k, const void *gq, const void *gk,
+                          const void *gv, const void *q, const void *k, int dtype, int B, int Hq,
+                          int Hkv, int S, int D, const void *conv_q, const void *conv_k,
+                          int conv_width, const void *mix_q, const void *mix_k,
+                          const int32_t *pos_offset, double rope_theta, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *attn_status_string(int status);
 

@@ -373,3 +373,37 @@ def test_cca_mix_validation(L):
     assert d(*args(pos=FAKE + 2)) == EALIGN
     assert d(*args(S=0, qo=None, ko=None, vo=None, q=None, k=None, v=None)) == OK
     assert d(*args(B=0, qo=None)) == OK
+
+
+def test_cca_mix_backward_workspace_and_validation(L):
+    ws = L.attn_cca_mix_backward_workspace_size
+    # the mean's fp32 gradient, then fp32 partial dM (D D) and taps (W D) per
+    # (sequence, 256-token chunk, head)
+    assert ws(2, 8, 2, 300, 64, 4) == 4 * (2 * 2 * 300 * 64 + 2 * 2 * 10 * (64 * 64 + 4 * 64))
+    assert ws(1, 4, 4, 1, 128, 1) == 4 * (4 * 128 + 1 * 8 * (128 * 128 + 128))
+    assert ws(0, 8, 2, 300, 64, 4) == 0 and ws(1, 8, 3, 16, 64, 4) == 0
+    assert ws(1, 8, 2, 16, 96, 4) == 0 and ws(1, 8, 2, 16, 64, 9) == 0 and ws(1, 8, 2, 0, 64, 4) == 0
+    need = ws(2, 8, 2, 100, 64, 4)
+    d = lambda *a: L.attn_cca_mix_backward(*a)
+    names = ["dq", "dk", "dv", "dcq", "dck", "dmq", "dmk", "gq", "gk", "gv", "q", "k"]
+    args = lambda **kw: [kw.get(n, FAKE) for n in names] + [
+        kw.get("dt", BF16), kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 2), kw.get("S", 100),
+        kw.get("D", 64), kw.get("cq", FAKE), kw.get("ck", FAKE), kw.get("W", 4), kw.get("mq", FAKE),
+        kw.get("mk", FAKE), kw.get("pos", None), kw.get("theta", 1e4), kw.get("ws", FAKE),
+        kw.get("wsb", need), None]
+    assert d(*args(Hkv=3)) == ESHAPE
+    assert d(*args(S=-1)) == ESHAPE
+    assert d(*args(dt=F32)) == EUNSUP
+    assert d(*args(D=32)) == EUNSUP
+    assert d(*args(W=0)) == EUNSUP and d(*args(W=9)) == EUNSUP
+    assert d(*args(theta=float("nan"))) == EUNSUP and d(*args(theta=-1.0)) == EUNSUP
+    for name in names + ["cq", "ck", "mq", "mk"]:
+        assert d(*args(**{name: None})) == ENULL, name
+    assert d(*args(dcq=FAKE + 2)) == EALIGN
+    assert d(*args(gq=FAKE + 8)) == EALIGN
+    assert d(*args(mq=FAKE + 8)) == EALIGN
+    assert d(*args(cq=FAKE + 1)) == EALIGN
+    assert d(*args(pos=FAKE + 2)) == EALIGN
+    assert d(*args(wsb=need - 1)) == EWS
+    assert d(*args(ws=None)) == EWS
+    assert d(*args(ws=FAKE + 8)) == EALIGN

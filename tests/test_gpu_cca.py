@@ -297,3 +297,108 @@ def test_cca_mix_decode_negative_index_is_taken_as_zero():
         assert torch.equal(qs[:, :, 0], q[:, :, 0]) and torch.equal(vs, v[:, :, 0])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Backward (attn_cca_mix_backward).  dv~ only moves bf16 values: bit for bit.
+# dq~ and dk~ are fp32 sums (the transposed mix over D terms, W taps, the
+# mean's share) rounded once to bf16: RNE of the oracle's exact value except
+# within 2^-16 of the sum of absolute terms of a rounding midpoint.  The
+# weight gradients are fp32 sums over every token (sequential within a chunk
+# of 256 tokens, then over the chunks): within 2^-13 of their sum of absolute
+# terms, a few times the worst accumulation error.  The sums of absolute
+# terms come from the oracle fed absolute values, each gradient channel pair
+# summed (the transposed rotation mixes the two channels of a pair).
+# ---------------------------------------------------------------------------
+def _pair_abs(x):
+    a = np.abs(oracle.widen(x))
+    return np.repeat(a[..., 0::2] + a[..., 1::2], 2, axis=-1)
+
+
+def _check_backward(w, width, theta, seed, pos=None):
+    q, k, v, cq, ck, mq, mk = wl.make_cca(w, seed=seed, width=width)
+    gq, gk, gv = wl.make_cca_grads(w, seed=seed + 1)
+    say(f"cca_mix_backward B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.S} D={w.D} W={width} theta={theta} pos={pos}")
+    pd = None if pos is None else torch.tensor(pos, dtype=torch.int32, device=DEV)
+    (dq, dk, dv), wg = attn.cca_mix_backward(
+        *(t.to(DEV) for t in (gq, gk, gv, q, k, cq, ck, mq, mk)), rope_theta=theta, pos_offset=pd)
+    torch.cuda.synchronize()
+    ins = [bits(t) for t in (gq, gk, gv, q, k, cq, ck, mq, mk)]
+    ref = oracle.cca_mix_backward(*ins, pos_offset=pos, theta=theta)
+    absins = [_pair_abs(ins[0]), _pair_abs(ins[1]), np.abs(oracle.widen(ins[2]))] + \
+             [np.abs(oracle.widen(x)) for x in ins[3:]]
+    bnd = oracle.cca_mix_backward(*absins)
+    assert np.array_equal(bits(dv), oracle.round_bf16(ref[2])), "value gradient must be exact"
+    assert_rounded(bits(dq), ref[0], 2.0 ** -16 * bnd[0], "dq~")
+    assert_rounded(bits(dk), ref[1], 2.0 ** -16 * bnd[1], "dk~")
+    for got, r, b, name in zip(wg, ref[3:], bnd[3:], ["dconv_q", "dconv_k", "dmix_q", "dmix_k"]):
+        err = np.abs(got.cpu().double().numpy() - r)
+        worst = float((err / (b + 1e-300)).max())
+        say(f"{name}: worst error {worst:.2e} of its sum of absolute terms")
+        assert np.isfinite(err).all() and (err <= 2.0 ** -13 * b).all(), name
+
+
+BWD_CASES = [  # B, Hq, Hkv, S, D, width, theta, pos_offset
+    (1, 8, 2, 200, 64, 4, 1e4, None),
+    (2, 8, 2, 130, 128, 4, 5e5, [0, 777]),
+    (1, 4, 4, 64, 128, 1, 0.0, None),       # MHA, single tap
+    (1, 4, 4, 65, 64, 8, 1e4, None),        # widest convolution, a block plus one token
+    (1, 16, 1, 97, 64, 3, 1e4, [5]),        # MQA, G = 16
+    (2, 6, 2, 17, 128, 2, 0.0, None),       # G = 3, shorter than one block
+    (1, 8, 2, 1, 64, 4, 1e4, None),         # one token
+    (1, 10, 2, 300, 64, 3, 1e4, None),      # two chunks, the second ragged
+    (1, 2, 1, 600, 128, 5, 5e5, [131000]),  # three chunks at D = 128, large positions
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+def test_cca_mix_backward_matches_oracle(case):
+    B, Hq, Hkv, S, D, width, theta, pos = case
+    _check_backward(wl.custom("prefill", "bf16", B, Hq, Hkv, D, S), width, theta, 200 + S, pos)
+
+
+def test_cca_mix_backward_full_size():
+    """ccgqa_prefill's shape (2 x 8/2 heads x 16384 x 64, W = 4, RoPE), every
+    gradient checked."""
+    w = wl.WORKLOADS["ccgqa_prefill"]
+    _check_backward(w, wl.CCA_CONV_WIDTH, w.theta, 3)
+
+
+def test_cca_mix_backward_without_tokens_zeroes_the_weight_gradients():
+    w = wl.custom("prefill", "bf16", 1, 8, 2, 64, 16)
+    q, k, v, cq, ck, mq, mk = (t.to(DEV) for t in wl.make_cca(w, seed=1))
+    say("cca_mix_backward with S = 0")
+    e = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device=DEV)
+    (dq, dk, dv), wg = attn.cca_mix_backward(e(1, 8, 0, 64), e(1, 2, 0, 64), e(1, 2, 0, 64),
+                                             e(1, 8, 0, 64), e(1, 2, 0, 64), cq, ck, mq, mk)
+    for t in wg:
+        t.fill_(float("nan"))
+    (dq, dk, dv), wg = attn.cca_mix_backward(e(1, 8, 0, 64), e(1, 2, 0, 64), e(1, 2, 0, 64),
+                                             e(1, 8, 0, 64), e(1, 2, 0, 64), cq, ck, mq, mk)
+    torch.cuda.synchronize()
+    for t in wg:
+        assert not t.abs().any()
+
+
+def test_cca_mix_backward_rejects_bad_arguments():
+    w = wl.custom("prefill", "bf16", 1, 8, 2, 64, 16)
+    q, k, v, cq, ck, mq, mk = (t.to(DEV) for t in wl.make_cca(w, seed=1))
+    gq, gk, gv = (t.to(DEV) for t in wl.make_cca_grads(w, seed=2))
+    L = attn.lib()
+    say("cca_mix_backward argument checks")
+    f32 = lambda *s: torch.empty(*s, dtype=torch.float32, device=DEV)
+    outs = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(k), f32(8, 4, 64),
+            f32(2, 4, 64), f32(8, 64, 64), f32(2, 64, 64)]
+    n = L.attn_cca_mix_backward_workspace_size(1, 8, 2, 16, 64, 4)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+
+    def call(W=4, D=64, theta=0.0, wsb=n, dt=1, Hkv=2):
+        return L.attn_cca_mix_backward(*(t.data_ptr() for t in outs), gq.data_ptr(), gk.data_ptr(),
+                                       gv.data_ptr(), q.data_ptr(), k.data_ptr(), dt, 1, 8, Hkv, 16,
+                                       D, cq.data_ptr(), ck.data_ptr(), W, mq.data_ptr(),
+                                       mk.data_ptr(), None, theta, ws.data_ptr(), wsb, None)
+    assert call() == 0
+    assert call(W=9) == 3 and call(W=0) == 3 and call(D=96) == 3 and call(theta=-1.0) == 3
+    assert call(dt=0) == 3 and call(Hkv=3) == 2
+    assert call(wsb=n - 1) == 5
+    torch.cuda.synchronize()
