@@ -15,11 +15,13 @@
 // again here.  Input gradients are rounded once to bf16; the weight gradients
 // are fp32 sums over the batch and every token.
 //
-// Three kernels, all fp32 vector arithmetic (the pass moves a few bytes per
-// flop; its products are small D x D maps per token):
+// Three kernels; the two D x D products per token and head (ds and dM) run on
+// the matrix cores with fp32 values split into bf16 high and low parts, the
+// rest is fp32 vector arithmetic:
 //  * cca_bwd_mean_kernel: per token and KV group, the rotated-back gradients
 //    of the group's query heads and key head summed into dm (fp32, in the
-//    workspace), and the value shift's gradient;
+//    workspace), the value shift's gradient, and the rotation's (cos, sin)
+//    per (sequence, token, channel pair) into the workspace for the next pass;
 //  * cca_bwd_head_kernel: one workgroup per (sequence, head, chunk of 256
 //    tokens), walking the chunk in blocks of 32 tokens.  Per block the
 //    rotated-back gradient rows (the block and the W - 1 tokens after it) and
@@ -43,79 +45,109 @@ constexpr int CB_THREADS = 256;
 
 __device__ inline float bf16_at(const uint16_t* p, size_t i) { return __uint_as_float((unsigned)p[i] << 16); }
 
-// a = R^T g for the channel pair (2i, 2i + 1) of one row at position p
-__device__ inline void rope_back(float g0, float g1, long long p, double freq, int rope, float& a0, float& a1) {
-    if (!rope) {
-        a0 = g0;
-        a1 = g1;
-        return;
-    }
-    float cs, sn;
-    rope_cos_sin(p, freq, cs, sn);
-    rope_rotate(g0, g1, cs, -sn, a0, a1);
-}
-
-// dm[b, j, t, :] and the value gradient, one thread per (row, channel pair)
+// dm[b, j, t, :] and the value gradient, one thread per (row, 8 channels)
 template <int D>
 __global__ __launch_bounds__(CB_THREADS) void cca_bwd_mean_kernel(
-    float* __restrict__ dm, uint16_t* __restrict__ dv, const uint16_t* __restrict__ gq,
+    float* __restrict__ dm, float* __restrict__ tab, uint16_t* __restrict__ dv, const uint16_t* __restrict__ gq,
     const uint16_t* __restrict__ gk, const uint16_t* __restrict__ gv, int B, int Hq, int Hkv, int S,
     const int32_t* __restrict__ pos_offset, int rope, RopeFreqs fr) {
-    constexpr int P = D / 2;
+    constexpr int C8 = D / 8;
     const long long rows = (long long)B * Hkv * S;
     const long long idx = (long long)blockIdx.x * CB_THREADS + threadIdx.x;
-    if (idx >= rows * P) return;
-    const long long row = idx / P;  // (b, j, t)
-    const int i = (int)(idx % P);
+    if (idx >= rows * C8) return;
+    const long long row = idx / C8;  // (b, j, t)
+    const int c0 = 8 * (int)(idx % C8);
     const int t = (int)(row % S);
     const int j = (int)((row / S) % Hkv);
     const int b = (int)(row / ((long long)S * Hkv));
     const int G = Hq / Hkv;
     const long long p = (pos_offset ? (long long)pos_offset[b] : 0) + t;
-    float s0 = 0.f, s1 = 0.f;
-    for (int r = 0; r < G; ++r) {
-        const size_t at = (((size_t)b * Hq + (size_t)j * G + r) * S + t) * D + 2 * i;
-        float a0, a1;
-        rope_back(bf16_at(gq, at), bf16_at(gq, at + 1), p, fr.f[i], rope, a0, a1);
-        s0 += a0;
-        s1 += a1;
+    float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
+    if (rope) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rope_cos_sin(p, fr.f[c0 / 2 + e], cs[e], sn[e]);
+        if (j == 0) {  // the (cos, sin) table of the per-head pass: [b, t, pair]
+            float* const tp = tab + (((size_t)b * S + t) * (D / 2) + c0 / 2) * 2;
+            *(f32x4_t*)tp = f32x4_t{cs[0], sn[0], cs[1], sn[1]};
+            *(f32x4_t*)(tp + 4) = f32x4_t{cs[2], sn[2], cs[3], sn[3]};
+        }
     }
-    const size_t at = (size_t)row * D + 2 * i;
-    float a0, a1;
-    rope_back(bf16_at(gk, at), bf16_at(gk, at + 1), p, fr.f[i], rope, a0, a1);
-    dm[at] = s0 + a0;
-    dm[at + 1] = s1 + a1;
+    const size_t at = (size_t)row * D + c0;
+    const u32x4_t kw = *(const u32x4_t*)(gk + at);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rope_rotate(bf16_lo(kw[e]), bf16_hi(kw[e]), cs[e], -sn[e], acc[2 * e], acc[2 * e + 1]);
+    for (int r = 0; r < G; ++r) {
+        const u32x4_t qw = *(const u32x4_t*)(gq + (((size_t)b * Hq + (size_t)j * G + r) * S + t) * D + c0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float a0, a1;
+            rope_rotate(bf16_lo(qw[e]), bf16_hi(qw[e]), cs[e], -sn[e], a0, a1);
+            acc[2 * e] += a0;
+            acc[2 * e + 1] += a1;
+        }
+    }
+    *(f32x4_t*)(dm + at) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4_t*)(dm + at + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
     // value shift: first half in place, second half from the next token
-    unsigned w;
-    if (2 * i < D / 2) w = *(const unsigned*)(gv + at);
-    else w = t + 1 < S ? *(const unsigned*)(gv + at + D) : 0u;
-    *(unsigned*)(dv + at) = w;
+    u32x4_t vw = {0, 0, 0, 0};
+    if (c0 < D / 2) vw = *(const u32x4_t*)(gv + at);
+    else if (t + 1 < S) vw = *(const u32x4_t*)(gv + at + D);
+    *(u32x4_t*)(dv + at) = vw;
 }
 
-// One workgroup per (chunk, head n of the Hq + Hkv, sequence b).
+// Eight fp32 values as a bf16 high part (truncated) and the bf16 rounding of
+// the remainder: hi + lo carries about 16 bits of each value, so a product
+// taken as hi x b + lo x b is fp32-accurate for an exact bf16 b.
+__device__ inline void split8(const float* p, bf16x8_t& hi, bf16x8_t& lo) {
+    const f32x4_t u = *(const f32x4_t*)p, v = *(const f32x4_t*)(p + 4);
+    const float x[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+    u32x4_t h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const unsigned b0 = __float_as_uint(x[2 * e]) & 0xffff0000u;
+        const unsigned b1 = __float_as_uint(x[2 * e + 1]) & 0xffff0000u;
+        h[e] = (b0 >> 16) | b1;
+        l[e] = pack_bf16x2(x[2 * e] - __uint_as_float(b0), x[2 * e + 1] - __uint_as_float(b1));
+    }
+    hi = __builtin_bit_cast(bf16x8_t, h);
+    lo = __builtin_bit_cast(bf16x8_t, l);
+}
+
+// One workgroup per (chunk, head n of the Hq + Hkv, sequence b).  The two D x D
+// products run on the matrix cores (v_mfma_f32_16x16x32_bf16): ds = M^T a with
+// a split into bf16 high and low parts and M exact; dM += a s^T over the
+// block's 32 tokens with both split (hi hi + hi lo + lo hi).
 template <int D>
 __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
     uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, float* __restrict__ part_mix,
-    float* __restrict__ part_conv, const float* __restrict__ dm, const uint16_t* __restrict__ gq,
-    const uint16_t* __restrict__ gk, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ conv_q, const uint16_t* __restrict__ conv_k,
-    const uint16_t* __restrict__ mix_q, const uint16_t* __restrict__ mix_k, int B, int Hq, int Hkv,
-    int S, int W, const int32_t* __restrict__ pos_offset, int rope, RopeFreqs fr) {
-    constexpr int CG = D / 4;                  // 4-column groups
-    constexpr int RG = CB_THREADS / CG;        // row groups of the ds product
-    constexpr int RPT = (CB_R + RG - 1) / RG;  // ds rows per thread
-    constexpr int MB = D == 64 ? 4 : 8;        // dM block per thread: MB x MB
-    constexpr int MG = D / MB;                 // dM column groups
-    static_assert(MG * MG == CB_THREADS, "dM split");
+    float* __restrict__ part_conv, const float* __restrict__ dm, const float* __restrict__ tab,
+    const uint16_t* __restrict__ gq, const uint16_t* __restrict__ gk, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ conv_q,
+    const uint16_t* __restrict__ conv_k, const uint16_t* __restrict__ mix_q,
+    const uint16_t* __restrict__ mix_k, int B, int Hq, int Hkv, int S, int W, int rope) {
+    constexpr int NT = D / 16;      // 16-wide tiles of a D-long dimension
+    constexpr int KS = D / 32;      // 32-deep k-steps over D
+    constexpr int RM = 48;          // staged gradient rows, padded to 3 tiles of 16
+    static_assert(RM >= CB_R, "row tiles");
+    constexpr int DSN = 3 * NT;     // ds tiles
+    constexpr int DMN = NT * NT;    // dM tiles
+    constexpr int DMW = DMN / 4;    // dM tiles per wave
 
-    __shared__ __attribute__((aligned(16))) float a_s[CB_R][D];   // a rows t0 .. t0 + T + W - 2
-    __shared__ __attribute__((aligned(16))) float ds_s[CB_R][D];  // M^T a of the same rows
-    __shared__ __attribute__((aligned(16))) float x_s[CB_R][D];   // x rows t0 - W + 1 .. t0 + T - 1
-    __shared__ __attribute__((aligned(16))) float s_s[CB_T][D];   // the forward's s of the block
+    // Rows are padded by 16 bytes (4 floats, 8 bf16) so that the reads of 16
+    // rows at one column (the matrix-core operands, the convolution over
+    // tokens) and the writes of the products' results fall in distinct banks.
+    constexpr int DP = D + 4, TP = CB_T + 4, MP = D + 8;
+    __shared__ __attribute__((aligned(16))) float a_s[RM][DP];       // a rows t0 .. t0 + RA - 1, zeros after
+    __shared__ __attribute__((aligned(16))) float at_s[D][TP];       // a of the block, transposed
+    __shared__ __attribute__((aligned(16))) float st_s[D][TP];       // s of the block, transposed
+    __shared__ __attribute__((aligned(16))) float ds_s[RM][DP];      // M^T a of the staged rows
+    __shared__ __attribute__((aligned(16))) float x_s[CB_R][DP];     // x rows t0 - W + 1 .. t0 + T - 1
     __shared__ __attribute__((aligned(16))) float w_s[CB_MAXW][D];
-    __shared__ __attribute__((aligned(16))) uint16_t m_s[D * D];  // mix, row c = output channel
+    __shared__ __attribute__((aligned(16))) uint16_t mt_s[D * MP];   // M^T: mt_s[c' MP + c] = M[c][c']
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
     const int nchunk = (S + CB_CHUNK - 1) / CB_CHUNK;
     const int chunk = (int)blockIdx.x % nchunk;
     const int n = (int)blockIdx.x / nchunk % (Hq + Hkv);
@@ -131,112 +163,163 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
     uint16_t* const dx = isq ? dq : dk;
     const size_t row0 = ((size_t)b * H + h) * S;     // this head's first row
     const size_t mrow0 = ((size_t)b * Hkv + j) * S;  // its group's first dm row
-    const long long pbase = pos_offset ? (long long)pos_offset[b] : 0;
+    const float* const tab_b = tab + (size_t)b * S * D;  // (cos, sin) of the sequence's rows
 
-    // weights of the head
-    for (int e = tid; e < D * D / 8; e += CB_THREADS)
-        *(u32x4_t*)(m_s + 8 * e) = *(const u32x4_t*)((isq ? mix_q : mix_k) + (size_t)h * D * D + 8 * e);
+    // weights of the head: M transposed into LDS, the taps in fp32
+    {
+        const uint16_t* const mw = (isq ? mix_q : mix_k) + (size_t)h * D * D;
+        for (int e = tid; e < D * D; e += CB_THREADS) {
+            const int c = e / D, c2 = e % D;  // coalesced read of row c
+            mt_s[c2 * MP + c] = mw[e];
+        }
+    }
     for (int e = tid; e < W * D; e += CB_THREADS)
         w_s[e / D][e % D] = bf16_at(isq ? conv_q : conv_k, (size_t)h * W * D + e);
 
-    // running sums of the weight gradients
-    float mix_acc[MB][MB];
+    // running sums of the weight gradients: the wave's dM tiles, and thread
+    // tid's taps e = tid + 256 q4 (W D <= 1024)
+    f32x4_t dmacc[DMW];
 #pragma unroll
-    for (int r = 0; r < MB; ++r)
-#pragma unroll
-        for (int c = 0; c < MB; ++c) mix_acc[r][c] = 0.f;
-    // tap gradients: thread tid sums taps e = tid + 256 q4 (W D <= 1024)
+    for (int u = 0; u < DMW; ++u) dmacc[u] = f32x4_t{0, 0, 0, 0};
     float conv_acc[4] = {0.f, 0.f, 0.f, 0.f};
 
     const int c_begin = chunk * CB_CHUNK, c_end = min(S, c_begin + CB_CHUNK);
-    for (int t0 = c_begin; t0 < c_end; t0 += CB_T) {
-        const int T = min(CB_T, c_end - t0);  // block tokens
-        const int RA = min(T + W - 1, S - t0);  // gradient rows staged (tokens t0 .. t0 + RA - 1)
-        const int RX = T + W - 1;               // latent rows staged (tokens t0 - W + 1 ..)
-        __syncthreads();  // the previous block's reads are done
-        for (int e = tid; e < RA * (D / 2); e += CB_THREADS) {
-            const int r = e / (D / 2), i = e % (D / 2);
-            const size_t at = (row0 + t0 + r) * D + 2 * i;
-            float a0, a1;
-            rope_back(bf16_at(g, at), bf16_at(g, at + 1), pbase + t0 + r, fr.f[i], rope, a0, a1);
-            a_s[r][2 * i] = a0;
-            a_s[r][2 * i + 1] = a1;
-        }
-        for (int e = tid; e < RX * D; e += CB_THREADS) {
-            const int r = e / D, c = e % D;
-            const int tok = t0 - (W - 1) + r;
-            x_s[r][c] = tok >= 0 ? bf16_at(x, (row0 + tok) * D + c) : 0.f;
-        }
-        __syncthreads();
-        // ds = M^T a: thread (column group cg, row group rg) forms rows rg + RG m, columns 4cg .. +3
-        {
-            const int cg = tid % CG, rg = tid / CG;
-            float acc[RPT][4];
+    // A block's global loads (gradient rows, 8 channels per item; latent rows;
+    // the mean's gradient) are issued while the previous block is computed.
+    constexpr int AI = (RM * (D / 8) + CB_THREADS - 1) / CB_THREADS;
+    constexpr int XI = (CB_R * (D / 8) + CB_THREADS - 1) / CB_THREADS;
+    constexpr int DI = (CB_T * (D / 8) + CB_THREADS - 1) / CB_THREADS;
+    u32x4_t gw[AI], xw[XI];
+    f32x4_t tlo[AI], thi[AI];  // (cos, sin) of the 4 pairs of a gradient item
+    f32x4_t mlo[DI], mhi[DI];
+    auto load_block = [&](int tb) __attribute__((always_inline)) {
+        const int Tb = min(CB_T, c_end - tb);
+        const int RAb = min(Tb + W - 1, S - tb), RXb = Tb + W - 1;
 #pragma unroll
-            for (int m = 0; m < RPT; ++m)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) acc[m][u] = 0.f;
-            for (int c = 0; c < D; ++c) {
-                const u32x2_t mw = *(const u32x2_t*)(m_s + c * D + 4 * cg);
-                const float m0 = bf16_lo(mw[0]), m1 = bf16_hi(mw[0]), m2 = bf16_lo(mw[1]), m3 = bf16_hi(mw[1]);
-#pragma unroll
-                for (int m = 0; m < RPT; ++m) {
-                    const int r = rg + RG * m;
-                    if (r < RA) {
-                        const float av = a_s[r][c];
-                        acc[m][0] = fmaf(m0, av, acc[m][0]);
-                        acc[m][1] = fmaf(m1, av, acc[m][1]);
-                        acc[m][2] = fmaf(m2, av, acc[m][2]);
-                        acc[m][3] = fmaf(m3, av, acc[m][3]);
-                    }
+        for (int u = 0; u < AI; ++u) {
+            const int e = tid + u * CB_THREADS, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            gw[u] = u32x4_t{0, 0, 0, 0};
+            tlo[u] = thi[u] = f32x4_t{1, 0, 1, 0};
+            if (r < RAb) {
+                gw[u] = *(const u32x4_t*)(g + (row0 + tb + r) * D + c0);
+                if (rope) {
+                    tlo[u] = *(const f32x4_t*)(tab_b + (size_t)(tb + r) * D + c0);
+                    thi[u] = *(const f32x4_t*)(tab_b + (size_t)(tb + r) * D + c0 + 4);
                 }
             }
+        }
 #pragma unroll
-            for (int m = 0; m < RPT; ++m) {
-                const int r = rg + RG * m;
-                if (r < RA) *(f32x4_t*)&ds_s[r][4 * cg] = f32x4_t{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+        for (int u = 0; u < XI; ++u) {
+            const int e = tid + u * CB_THREADS, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int tok = tb - (W - 1) + r;
+            xw[u] = u32x4_t{0, 0, 0, 0};
+            if (r < RXb && tok >= 0) xw[u] = *(const u32x4_t*)(x + (row0 + tok) * D + c0);
+        }
+#pragma unroll
+        for (int u = 0; u < DI; ++u) {
+            const int e = tid + u * CB_THREADS, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            mlo[u] = mhi[u] = f32x4_t{0, 0, 0, 0};
+            if (r < Tb) {
+                mlo[u] = *(const f32x4_t*)(dm + (mrow0 + tb + r) * D + c0);
+                mhi[u] = *(const f32x4_t*)(dm + (mrow0 + tb + r) * D + c0 + 4);
             }
         }
-        // s of the block (the forward's convolution output)
-        for (int e = tid; e < T * D; e += CB_THREADS) {
-            const int r = e / D, c = e % D;
+    };
+    load_block(c_begin);
+    for (int t0 = c_begin; t0 < c_end; t0 += CB_T) {
+        const int T = min(CB_T, c_end - t0);    // block tokens
+        const int RA = min(T + W - 1, S - t0);  // gradient rows (tokens t0 .. t0 + RA - 1)
+        const int RX = T + W - 1;               // latent rows (tokens t0 - W + 1 ..)
+        __syncthreads();  // the previous block's reads are done
+#pragma unroll
+        for (int u = 0; u < AI; ++u) {
+            const int e = tid + u * CB_THREADS, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            if (r < RM) {
+                float a[8];
+                const float cs[4] = {tlo[u][0], tlo[u][2], thi[u][0], thi[u][2]};
+                const float sn[4] = {tlo[u][1], tlo[u][3], thi[u][1], thi[u][3]};
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2)  // a = R^T g (cos 1, sin 0 without RoPE)
+                    rope_rotate(bf16_lo(gw[u][q2]), bf16_hi(gw[u][q2]), cs[q2], -sn[q2], a[2 * q2],
+                                a[2 * q2 + 1]);
+                *(f32x4_t*)&a_s[r][c0] = f32x4_t{a[0], a[1], a[2], a[3]};
+                *(f32x4_t*)&a_s[r][c0 + 4] = f32x4_t{a[4], a[5], a[6], a[7]};
+                if (r < CB_T) {  // the block's tokens only (zeros past T)
+                    const bool in = r < T;
+#pragma unroll
+                    for (int z = 0; z < 8; ++z) at_s[c0 + z][r] = in ? a[z] : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < XI; ++u) {
+            const int e = tid + u * CB_THREADS, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            if (r < RX) {
+                const u32x4_t v = xw[u];
+                *(f32x4_t*)&x_s[r][c0] = f32x4_t{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
+                *(f32x4_t*)&x_s[r][c0 + 4] = f32x4_t{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
+            }
+        }
+        f32x4_t cur_lo[DI], cur_hi[DI];  // this block's mean gradient
+#pragma unroll
+        for (int u = 0; u < DI; ++u) {
+            cur_lo[u] = mlo[u];
+            cur_hi[u] = mhi[u];
+        }
+        if (t0 + CB_T < c_end) load_block(t0 + CB_T);
+        __syncthreads();
+        // s of the block (the forward's convolution output), transposed
+        for (int e = tid; e < CB_T * D; e += CB_THREADS) {
+            const int c = e / CB_T, r = e % CB_T;
             float acc = 0.f;
-            for (int i = 0; i < W; ++i) acc = fmaf(w_s[i][c], x_s[r + W - 1 - i][c], acc);
-            s_s[r][c] = acc;
+            if (r < T)
+                for (int i = 0; i < W; ++i) acc = fmaf(w_s[i][c], x_s[r + W - 1 - i][c], acc);
+            st_s[c][r] = acc;
+        }
+        // ds = M^T a: tile (mt, nt) gives rows 16 mt + 4 lg + i, column 16 nt + lr
+        for (int tt = w; tt < DSN; tt += 4) {
+            const int mt = tt / NT, nt = tt % NT;
+            f32x4_t acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8_t ahi, alo;
+                split8(&a_s[16 * mt + lr][32 * ks + 8 * lg], ahi, alo);
+                const bf16x8_t bm = *(const bf16x8_t*)(mt_s + (16 * nt + lr) * MP + 32 * ks + 8 * lg);
+                acc = mfma16(ahi, bm, acc);
+                acc = mfma16(alo, bm, acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ds_s[16 * mt + 4 * lg + i][16 * nt + lr] = acc[i];
         }
         __syncthreads();
-        // dx of the block's tokens: the taps forward in time, plus the mean's share
-        for (int e = tid; e < T * (D / 2); e += CB_THREADS) {
-            const int r = e / (D / 2), c = 2 * (e % (D / 2));
-            float v0 = 0.f, v1 = 0.f;
-            for (int i = 0; i < W && r + i < RA; ++i) {
-                v0 = fmaf(w_s[i][c], ds_s[r + i][c], v0);
-                v1 = fmaf(w_s[i][c + 1], ds_s[r + i][c + 1], v1);
-            }
-            const float2 mm = *(const float2*)(dm + (mrow0 + t0 + r) * D + c);
-            v0 = fmaf(mean_w, mm.x, v0);
-            v1 = fmaf(mean_w, mm.y, v1);
-            *(unsigned*)(dx + (row0 + t0 + r) * D + c) = pack_bf16x2(v0, v1);
-        }
-        // dM += a s^T over the block: thread owns rows MB (tid / MG) .., columns MB (tid % MG) ..
+        // dx of the block's tokens: the taps forward in time, plus the mean's
+        // share; 8 channels per item
         {
-            const int mr = MB * (tid / MG), mc = MB * (tid % MG);
-            for (int r = 0; r < T; ++r) {
-                float av[MB], sv[MB];
 #pragma unroll
-                for (int u = 0; u < MB; u += 4) {
-                    const f32x4_t a4 = *(const f32x4_t*)&a_s[r][mr + u];
-                    const f32x4_t s4 = *(const f32x4_t*)&s_s[r][mc + u];
+            for (int u = 0; u < DI; ++u) {
+                const int e = tid + u * CB_THREADS, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                if (r < T) {
+                    float v[8];
 #pragma unroll
                     for (int z = 0; z < 4; ++z) {
-                        av[u + z] = a4[z];
-                        sv[u + z] = s4[z];
+                        v[z] = mean_w * cur_lo[u][z];
+                        v[z + 4] = mean_w * cur_hi[u][z];
                     }
+                    for (int i = 0; i < W && r + i < RA; ++i) {
+                        const f32x4_t d0 = *(const f32x4_t*)&ds_s[r + i][c0];
+                        const f32x4_t d1 = *(const f32x4_t*)&ds_s[r + i][c0 + 4];
+                        const f32x4_t w0 = *(const f32x4_t*)&w_s[i][c0];
+                        const f32x4_t w1 = *(const f32x4_t*)&w_s[i][c0 + 4];
+#pragma unroll
+                        for (int z = 0; z < 4; ++z) {
+                            v[z] = fmaf(w0[z], d0[z], v[z]);
+                            v[z + 4] = fmaf(w1[z], d1[z], v[z + 4]);
+                        }
+                    }
+                    *(u32x4_t*)(dx + (row0 + t0 + r) * D + c0) =
+                        u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
                 }
-#pragma unroll
-                for (int u = 0; u < MB; ++u)
-#pragma unroll
-                    for (int z = 0; z < MB; ++z) mix_acc[u][z] = fmaf(av[u], sv[z], mix_acc[u][z]);
             }
         }
         // tap gradient: dw_i[c] += sum over the block of ds[t] x[t - i]
@@ -250,18 +333,28 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
                 conv_acc[q4] += acc;
             }
         }
+        // dM += a s^T over the block: tile (mt, nt) of (c, c'), k = the 32 tokens
+#pragma unroll
+        for (int u = 0; u < DMW; ++u) {
+            const int tt = w + 4 * u, mt = tt / NT, nt = tt % NT;
+            bf16x8_t ahi, alo, shi, slo;
+            split8(&at_s[16 * mt + lr][8 * lg], ahi, alo);
+            split8(&st_s[16 * nt + lr][8 * lg], shi, slo);
+            dmacc[u] = mfma16(ahi, shi, dmacc[u]);
+            dmacc[u] = mfma16(ahi, slo, dmacc[u]);
+            dmacc[u] = mfma16(alo, shi, dmacc[u]);
+        }
     }
     // this chunk's partial sums: part[(b, chunk)][n][...]
     const size_t pidx = ((size_t)b * nchunk + chunk) * (Hq + Hkv) + n;
     {
-        const int mr = MB * (tid / MG), mc = MB * (tid % MG);
         float* const pm = part_mix + pidx * D * D;
 #pragma unroll
-        for (int u = 0; u < MB; ++u)
+        for (int u = 0; u < DMW; ++u) {
+            const int tt = w + 4 * u, mt = tt / NT, nt = tt % NT;
 #pragma unroll
-            for (int z = 0; z < MB; z += 4)
-                *(f32x4_t*)(pm + (size_t)(mr + u) * D + mc + z) =
-                    f32x4_t{mix_acc[u][z], mix_acc[u][z + 1], mix_acc[u][z + 2], mix_acc[u][z + 3]};
+            for (int i = 0; i < 4; ++i) pm[(size_t)(16 * mt + 4 * lg + i) * D + 16 * nt + lr] = dmacc[u][i];
+        }
     }
     {
         float* const pc = part_conv + pidx * (size_t)W * D;
@@ -286,7 +379,18 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_reduce_kernel(
     const int NH = Hq + Hkv;
     float acc = 0.f;
     if (e < D * D) {
-        for (int p = 0; p < P; ++p) acc += part_mix[((size_t)p * NH + n) * D * D + e];
+        int p = 0;
+        for (; p + 4 <= P; p += 4) {
+            const float v0 = part_mix[((size_t)p * NH + n) * D * D + e];
+            const float v1 = part_mix[((size_t)(p + 1) * NH + n) * D * D + e];
+            const float v2 = part_mix[((size_t)(p + 2) * NH + n) * D * D + e];
+            const float v3 = part_mix[((size_t)(p + 3) * NH + n) * D * D + e];
+            acc += v0;
+            acc += v1;
+            acc += v2;
+            acc += v3;
+        }
+        for (; p < P; ++p) acc += part_mix[((size_t)p * NH + n) * D * D + e];
         if (n < Hq) dmix_q[(size_t)n * D * D + e] = acc;
         else dmix_k[(size_t)(n - Hq) * D * D + e] = acc;
     } else {
@@ -309,19 +413,20 @@ hipError_t launch_cca_bwd_d(void* dq, void* dk, void* dv, float* dconv_q, float*
     const int nchunk = (S + CB_CHUNK - 1) / CB_CHUNK;
     const int P = B * nchunk;
     float* const dm = (float*)workspace;
-    float* const part_mix = dm + (size_t)B * Hkv * S * D;
+    float* const tab = dm + (size_t)B * Hkv * S * D;  // [B, S, D / 2] (cos, sin)
+    float* const part_mix = tab + (size_t)B * S * D;
     float* const part_conv = part_mix + (size_t)P * (Hq + Hkv) * D * D;
     if ((long long)B * S > 0) {
-        const long long items = (long long)B * Hkv * S * (D / 2);
+        const long long items = (long long)B * Hkv * S * (D / 8);
         hipLaunchKernelGGL(cca_bwd_mean_kernel<D>, dim3((unsigned)((items + CB_THREADS - 1) / CB_THREADS)),
-                           dim3(CB_THREADS), 0, st, dm, (uint16_t*)dv, (const uint16_t*)gq,
+                           dim3(CB_THREADS), 0, st, dm, tab, (uint16_t*)dv, (const uint16_t*)gq,
                            (const uint16_t*)gk, (const uint16_t*)gv, B, Hq, Hkv, S, pos_offset, rope, fr);
         hipLaunchKernelGGL(cca_bwd_head_kernel<D>, dim3((unsigned)((long long)B * (Hq + Hkv) * nchunk)),
                            dim3(CB_THREADS), 0, st, (uint16_t*)dq, (uint16_t*)dk, part_mix, part_conv,
-                           (const float*)dm, (const uint16_t*)gq, (const uint16_t*)gk,
-                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)conv_q,
-                           (const uint16_t*)conv_k, (const uint16_t*)mix_q, (const uint16_t*)mix_k,
-                           B, Hq, Hkv, S, W, pos_offset, rope, fr);
+                           (const float*)dm, (const float*)tab, (const uint16_t*)gq,
+                           (const uint16_t*)gk, (const uint16_t*)q, (const uint16_t*)k,
+                           (const uint16_t*)conv_q, (const uint16_t*)conv_k,
+                           (const uint16_t*)mix_q, (const uint16_t*)mix_k, B, Hq, Hkv, S, W, rope);
     }
     {
         const long long items = (long long)(Hq + Hkv) * (D * D + W * D);
@@ -337,7 +442,8 @@ hipError_t launch_cca_bwd_d(void* dq, void* dk, void* dv, float* dconv_q, float*
 size_t cca_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int W) {
     const size_t nchunk = ((size_t)S + CB_CHUNK - 1) / CB_CHUNK;
     const size_t P = (size_t)B * nchunk;
-    return sizeof(float) * ((size_t)B * Hkv * S * D + P * (Hq + Hkv) * ((size_t)D * D + (size_t)W * D));
+    return sizeof(float) * ((size_t)B * Hkv * S * D + (size_t)B * S * D +
+                            P * (Hq + Hkv) * ((size_t)D * D + (size_t)W * D));
 }
 
 int cca_bwd_max_width() { return CB_MAXW; }

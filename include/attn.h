@@ -353,8 +353,9 @@ int attn_cca_mix_decode(void *q_out, void *k_out, void *v_out, const void *q, co
 
 /*
  * Bytes of device workspace attn_cca_mix_backward needs (0 on invalid sizes):
- * the mean's fp32 gradient [B, Hkv, S, D] and fp32 partial weight gradients
- * per (sequence, 256-token chunk, head).
+ * the mean's fp32 gradient [B, Hkv, S, D], the rotation's fp32 (cos, sin) per
+ * (sequence, token, channel pair), and fp32 partial weight gradients per
+ * (sequence, 256-token chunk, head).
  */
 size_t attn_cca_mix_backward_workspace_size(int B, int Hq, int Hkv, int S, int D, int conv_width);
 

@@ -377,10 +377,12 @@ def test_cca_mix_validation(L):
 
 def test_cca_mix_backward_workspace_and_validation(L):
     ws = L.attn_cca_mix_backward_workspace_size
-    # the mean's fp32 gradient, then fp32 partial dM (D D) and taps (W D) per
-    # (sequence, 256-token chunk, head)
-    assert ws(2, 8, 2, 300, 64, 4) == 4 * (2 * 2 * 300 * 64 + 2 * 2 * 10 * (64 * 64 + 4 * 64))
-    assert ws(1, 4, 4, 1, 128, 1) == 4 * (4 * 128 + 1 * 8 * (128 * 128 + 128))
+    # the mean's fp32 gradient, the rotation's (cos, sin) per (sequence, token,
+    # pair), then fp32 partial dM (D D) and taps (W D) per (sequence, 256-token
+    # chunk, head)
+    assert ws(2, 8, 2, 300, 64, 4) == 4 * (2 * 2 * 300 * 64 + 2 * 300 * 64 +
+                                           2 * 2 * 10 * (64 * 64 + 4 * 64))
+    assert ws(1, 4, 4, 1, 128, 1) == 4 * (4 * 128 + 128 + 1 * 8 * (128 * 128 + 128))
     assert ws(0, 8, 2, 300, 64, 4) == 0 and ws(1, 8, 3, 16, 64, 4) == 0
     assert ws(1, 8, 2, 16, 96, 4) == 0 and ws(1, 8, 2, 16, 64, 9) == 0 and ws(1, 8, 2, 0, 64, 4) == 0
     need = ws(2, 8, 2, 100, 64, 4)
