@@ -96,28 +96,31 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_mean_kernel(
     *(u32x4_t*)(dv + at) = vw;
 }
 
-// Eight fp32 values as a bf16 high part (truncated) and the bf16 rounding of
-// the remainder: hi + lo carries about 16 bits of each value, so a product
-// taken as hi x b + lo x b is fp32-accurate for an exact bf16 b.
-__device__ inline void split8(const float* p, bf16x8_t& hi, bf16x8_t& lo) {
-    const f32x4_t u = *(const f32x4_t*)p, v = *(const f32x4_t*)(p + 4);
-    const float x[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
-    u32x4_t h, l;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const unsigned b0 = __float_as_uint(x[2 * e]) & 0xffff0000u;
-        const unsigned b1 = __float_as_uint(x[2 * e + 1]) & 0xffff0000u;
-        h[e] = (b0 >> 16) | b1;
-        l[e] = pack_bf16x2(x[2 * e] - __uint_as_float(b0), x[2 * e + 1] - __uint_as_float(b1));
-    }
-    hi = __builtin_bit_cast(bf16x8_t, h);
-    lo = __builtin_bit_cast(bf16x8_t, l);
+// fp32 x as a bf16 high part (truncated) and the bf16 rounding of the rest:
+// hi + lo carries about 16 bits of x, so products taken part by part with an
+// exact bf16 (or a split) operand are fp32-accurate.
+__device__ inline void split1(float x, unsigned& hi, unsigned& lo) {
+    const unsigned b = __float_as_uint(x) & 0xffff0000u;
+    hi = b >> 16;
+    lo = pack_bf16x2(x - __uint_as_float(b), 0.f) & 0xffffu;
+}
+
+// 8 bf16 of column c0 + (lane % 16) of rows r0 .. r0 + 7 of a row-major bf16
+// tile with rows of `ld` elements (two transpose reads of 4 rows each): the
+// matrix-core operand whose k runs along the rows.
+__device__ inline bf16x8_t col8(const uint16_t* tile, int ld, int r0, int c0, int lane) {
+    const int L = lane & 15;
+    const uint16_t* const p = tile + (r0 + L / 4) * ld + c0 + 4 * (L % 4);
+    const bf16x4_t lo = lds_read_tr(p), hi = lds_read_tr(p + 4 * ld);
+    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{l2.x, l2.y, h2.x, h2.y});
 }
 
 // One workgroup per (chunk, head n of the Hq + Hkv, sequence b).  The two D x D
-// products run on the matrix cores (v_mfma_f32_16x16x32_bf16): ds = M^T a with
-// a split into bf16 high and low parts and M exact; dM += a s^T over the
-// block's 32 tokens with both split (hi hi + hi lo + lo hi).
+// products run on the matrix cores (v_mfma_f32_16x16x32_bf16) on operands
+// stored in LDS as bf16 high and low parts: ds = M^T a (a split, M exact),
+// read row-wise; dM += a s^T over the block's 32 tokens (hi hi + hi lo +
+// lo hi), with a and s read down their token columns by transpose reads.
 template <int D>
 __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
     uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, float* __restrict__ part_mix,
@@ -137,10 +140,11 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
     // Rows are padded by 16 bytes (4 floats, 8 bf16) so that the reads of 16
     // rows at one column (the matrix-core operands, the convolution over
     // tokens) and the writes of the products' results fall in distinct banks.
-    constexpr int DP = D + 4, TP = CB_T + 4, MP = D + 8;
-    __shared__ __attribute__((aligned(16))) float a_s[RM][DP];       // a rows t0 .. t0 + RA - 1, zeros after
-    __shared__ __attribute__((aligned(16))) float at_s[D][TP];       // a of the block, transposed
-    __shared__ __attribute__((aligned(16))) float st_s[D][TP];       // s of the block, transposed
+    constexpr int DP = D + 4, AP = D + 8, MP = D + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t ah_s[RM * AP];  // a rows t0 .., bf16 high part, zeros after RA
+    __shared__ __attribute__((aligned(16))) uint16_t al_s[RM * AP];  // low part
+    __shared__ __attribute__((aligned(16))) uint16_t sh_s[CB_T * AP];  // s of the block, high part, zeros after T
+    __shared__ __attribute__((aligned(16))) uint16_t sl_s[CB_T * AP];
     __shared__ __attribute__((aligned(16))) float ds_s[RM][DP];      // M^T a of the staged rows
     __shared__ __attribute__((aligned(16))) float x_s[CB_R][DP];     // x rows t0 - W + 1 .. t0 + T - 1
     __shared__ __attribute__((aligned(16))) float w_s[CB_MAXW][D];
@@ -235,20 +239,21 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
         for (int u = 0; u < AI; ++u) {
             const int e = tid + u * CB_THREADS, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             if (r < RM) {
-                float a[8];
                 const float cs[4] = {tlo[u][0], tlo[u][2], thi[u][0], thi[u][2]};
                 const float sn[4] = {tlo[u][1], tlo[u][3], thi[u][1], thi[u][3]};
+                u32x4_t hw, lw;
 #pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2)  // a = R^T g (cos 1, sin 0 without RoPE)
-                    rope_rotate(bf16_lo(gw[u][q2]), bf16_hi(gw[u][q2]), cs[q2], -sn[q2], a[2 * q2],
-                                a[2 * q2 + 1]);
-                *(f32x4_t*)&a_s[r][c0] = f32x4_t{a[0], a[1], a[2], a[3]};
-                *(f32x4_t*)&a_s[r][c0 + 4] = f32x4_t{a[4], a[5], a[6], a[7]};
-                if (r < CB_T) {  // the block's tokens only (zeros past T)
-                    const bool in = r < T;
-#pragma unroll
-                    for (int z = 0; z < 8; ++z) at_s[c0 + z][r] = in ? a[z] : 0.f;
+                for (int q2 = 0; q2 < 4; ++q2) {  // a = R^T g (cos 1, sin 0 without RoPE)
+                    float a0, a1;
+                    rope_rotate(bf16_lo(gw[u][q2]), bf16_hi(gw[u][q2]), cs[q2], -sn[q2], a0, a1);
+                    unsigned h0, l0, h1, l1;
+                    split1(a0, h0, l0);
+                    split1(a1, h1, l1);
+                    hw[q2] = h0 | (h1 << 16);
+                    lw[q2] = l0 | (l1 << 16);
                 }
+                *(u32x4_t*)(ah_s + r * AP + c0) = hw;
+                *(u32x4_t*)(al_s + r * AP + c0) = lw;
             }
         }
 #pragma unroll
@@ -268,13 +273,23 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
         }
         if (t0 + CB_T < c_end) load_block(t0 + CB_T);
         __syncthreads();
-        // s of the block (the forward's convolution output), transposed
-        for (int e = tid; e < CB_T * D; e += CB_THREADS) {
-            const int c = e / CB_T, r = e % CB_T;
-            float acc = 0.f;
+        // s of the block (the forward's convolution output) as bf16 parts, two
+        // channels per item
+        for (int e = tid; e < CB_T * (D / 2); e += CB_THREADS) {
+            const int r = e / (D / 2), c = 2 * (e % (D / 2));
+            float s0 = 0.f, s1 = 0.f;
             if (r < T)
-                for (int i = 0; i < W; ++i) acc = fmaf(w_s[i][c], x_s[r + W - 1 - i][c], acc);
-            st_s[c][r] = acc;
+                for (int i = 0; i < W; ++i) {
+                    const float2 xv = *(const float2*)&x_s[r + W - 1 - i][c];
+                    const float2 wv = *(const float2*)&w_s[i][c];
+                    s0 = fmaf(wv.x, xv.x, s0);
+                    s1 = fmaf(wv.y, xv.y, s1);
+                }
+            unsigned h0, l0, h1, l1;
+            split1(s0, h0, l0);
+            split1(s1, h1, l1);
+            *(unsigned*)(sh_s + r * AP + c) = h0 | (h1 << 16);
+            *(unsigned*)(sl_s + r * AP + c) = l0 | (l1 << 16);
         }
         // ds = M^T a: tile (mt, nt) gives rows 16 mt + 4 lg + i, column 16 nt + lr
         for (int tt = w; tt < DSN; tt += 4) {
@@ -282,8 +297,8 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
             f32x4_t acc = {0, 0, 0, 0};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                bf16x8_t ahi, alo;
-                split8(&a_s[16 * mt + lr][32 * ks + 8 * lg], ahi, alo);
+                const int ao = (16 * mt + lr) * AP + 32 * ks + 8 * lg;
+                const bf16x8_t ahi = *(const bf16x8_t*)(ah_s + ao), alo = *(const bf16x8_t*)(al_s + ao);
                 const bf16x8_t bm = *(const bf16x8_t*)(mt_s + (16 * nt + lr) * MP + 32 * ks + 8 * lg);
                 acc = mfma16(ahi, bm, acc);
                 acc = mfma16(alo, bm, acc);
@@ -337,9 +352,10 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
 #pragma unroll
         for (int u = 0; u < DMW; ++u) {
             const int tt = w + 4 * u, mt = tt / NT, nt = tt % NT;
-            bf16x8_t ahi, alo, shi, slo;
-            split8(&at_s[16 * mt + lr][8 * lg], ahi, alo);
-            split8(&st_s[16 * nt + lr][8 * lg], shi, slo);
+            // A[m = c][k = t] = a[t][c] and B[k = t][n = c'] = s[t][c']: token
+            // columns of the row-major parts (rows 8 lg .. 8 lg + 7)
+            const bf16x8_t ahi = col8(ah_s, AP, 8 * lg, 16 * mt, lane), alo = col8(al_s, AP, 8 * lg, 16 * mt, lane);
+            const bf16x8_t shi = col8(sh_s, AP, 8 * lg, 16 * nt, lane), slo = col8(sl_s, AP, 8 * lg, 16 * nt, lane);
             dmacc[u] = mfma16(ahi, shi, dmacc[u]);
             dmacc[u] = mfma16(ahi, slo, dmacc[u]);
             dmacc[u] = mfma16(alo, shi, dmacc[u]);
