@@ -383,37 +383,50 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
 }
 
 // Weight gradients: the sum of the P = B * nchunk partials of every weight
-// element; element e of head n runs over dM (D D) then the taps (W D).
+// element; element e of head n runs over dM (D D) then the taps (W D).  A
+// workgroup takes 64 consecutive elements; its 4 waves each sum a quarter of
+// the partials (8 loads in flight per lane), then the quarters are added
+// through LDS, so the result does not depend on the launch.
 __global__ __launch_bounds__(CB_THREADS) void cca_bwd_reduce_kernel(
     float* __restrict__ dconv_q, float* __restrict__ dconv_k, float* __restrict__ dmix_q,
     float* __restrict__ dmix_k, const float* __restrict__ part_mix, const float* __restrict__ part_conv,
     int Hq, int Hkv, int D, int W, int P) {
+    __shared__ float red[4][64];
     const int per = D * D + W * D;
-    const long long idx = (long long)blockIdx.x * CB_THREADS + threadIdx.x;
-    if (idx >= (long long)(Hq + Hkv) * per) return;
-    const int n = (int)(idx / per), e = (int)(idx % per);
     const int NH = Hq + Hkv;
+    const int lane = threadIdx.x & 63, qw = threadIdx.x >> 6;
+    const long long idx = (long long)blockIdx.x * 64 + lane;
+    const bool ok = idx < (long long)NH * per;
+    const int n = ok ? (int)(idx / per) : 0, e = ok ? (int)(idx % per) : 0;
+    const bool mix = e < D * D;
+    const float* const base = mix ? part_mix + (size_t)n * D * D + e
+                                  : part_conv + (size_t)n * W * D + (e - D * D);
+    const size_t stride = mix ? (size_t)NH * D * D : (size_t)NH * W * D;
+    const int p0 = qw * ((P + 3) / 4), p1 = min(P, p0 + (P + 3) / 4);
     float acc = 0.f;
-    if (e < D * D) {
-        int p = 0;
-        for (; p + 4 <= P; p += 4) {
-            const float v0 = part_mix[((size_t)p * NH + n) * D * D + e];
-            const float v1 = part_mix[((size_t)(p + 1) * NH + n) * D * D + e];
-            const float v2 = part_mix[((size_t)(p + 2) * NH + n) * D * D + e];
-            const float v3 = part_mix[((size_t)(p + 3) * NH + n) * D * D + e];
-            acc += v0;
-            acc += v1;
-            acc += v2;
-            acc += v3;
+    if (ok) {
+        int p = p0;
+        for (; p + 8 <= p1; p += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = base[(size_t)(p + u) * stride];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += v[u];
         }
-        for (; p < P; ++p) acc += part_mix[((size_t)p * NH + n) * D * D + e];
-        if (n < Hq) dmix_q[(size_t)n * D * D + e] = acc;
-        else dmix_k[(size_t)(n - Hq) * D * D + e] = acc;
-    } else {
-        const int f = e - D * D;
-        for (int p = 0; p < P; ++p) acc += part_conv[((size_t)p * NH + n) * W * D + f];
-        if (n < Hq) dconv_q[(size_t)n * W * D + f] = acc;
-        else dconv_k[(size_t)(n - Hq) * W * D + f] = acc;
+        for (; p < p1; ++p) acc += base[(size_t)p * stride];
+    }
+    red[qw][lane] = acc;
+    __syncthreads();
+    if (qw == 0 && ok) {
+        const float sum = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+        if (mix) {
+            if (n < Hq) dmix_q[(size_t)n * D * D + e] = sum;
+            else dmix_k[(size_t)(n - Hq) * D * D + e] = sum;
+        } else {
+            const int f = e - D * D;
+            if (n < Hq) dconv_q[(size_t)n * W * D + f] = sum;
+            else dconv_k[(size_t)(n - Hq) * W * D + f] = sum;
+        }
     }
 }
 
@@ -446,7 +459,7 @@ hipError_t launch_cca_bwd_d(void* dq, void* dk, void* dv, float* dconv_q, float*
     }
     {
         const long long items = (long long)(Hq + Hkv) * (D * D + W * D);
-        hipLaunchKernelGGL(cca_bwd_reduce_kernel, dim3((unsigned)((items + CB_THREADS - 1) / CB_THREADS)),
+        hipLaunchKernelGGL(cca_bwd_reduce_kernel, dim3((unsigned)((items + 63) / 64)),
                            dim3(CB_THREADS), 0, st, dconv_q, dconv_k, dmix_q, dmix_k,
                            (const float*)part_mix, (const float*)part_conv, Hq, Hkv, D, W, P);
     }
