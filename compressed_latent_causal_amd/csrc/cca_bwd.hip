@@ -146,7 +146,7 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sh_s[CB_T * AP];  // s of the block, high part, zeros after T
     __shared__ __attribute__((aligned(16))) uint16_t sl_s[CB_T * AP];
     __shared__ __attribute__((aligned(16))) float ds_s[RM][DP];      // M^T a of the staged rows
-    __shared__ __attribute__((aligned(16))) float x_s[CB_R][DP];     // x rows t0 - W + 1 .. t0 + T - 1
+    __shared__ __attribute__((aligned(16))) uint16_t x_s[CB_R * AP];  // x rows t0 - W + 1 .. t0 + T - 1 (bf16)
     __shared__ __attribute__((aligned(16))) float w_s[CB_MAXW][D];
     __shared__ __attribute__((aligned(16))) uint16_t mt_s[D * MP];   // M^T: mt_s[c' MP + c] = M[c][c']
 
@@ -261,8 +261,7 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
             const int e = tid + u * CB_THREADS, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             if (r < RX) {
                 const u32x4_t v = xw[u];
-                *(f32x4_t*)&x_s[r][c0] = f32x4_t{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
-                *(f32x4_t*)&x_s[r][c0 + 4] = f32x4_t{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
+                *(u32x4_t*)(x_s + r * AP + c0) = v;
             }
         }
         f32x4_t cur_lo[DI], cur_hi[DI];  // this block's mean gradient
@@ -280,10 +279,10 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
             float s0 = 0.f, s1 = 0.f;
             if (r < T)
                 for (int i = 0; i < W; ++i) {
-                    const float2 xv = *(const float2*)&x_s[r + W - 1 - i][c];
+                    const unsigned xv = *(const unsigned*)(x_s + (r + W - 1 - i) * AP + c);
                     const float2 wv = *(const float2*)&w_s[i][c];
-                    s0 = fmaf(wv.x, xv.x, s0);
-                    s1 = fmaf(wv.y, xv.y, s1);
+                    s0 = fmaf(wv.x, bf16_lo(xv), s0);
+                    s1 = fmaf(wv.y, bf16_hi(xv), s1);
                 }
             unsigned h0, l0, h1, l1;
             split1(s0, h0, l0);
@@ -344,7 +343,8 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
             if (e < W * D) {
                 const int i = e / D, c = e % D;
                 float acc = 0.f;
-                for (int r = 0; r < T; ++r) acc = fmaf(ds_s[r][c], x_s[r + W - 1 - i][c], acc);
+                for (int r = 0; r < T; ++r)
+                    acc = fmaf(ds_s[r][c], __uint_as_float((unsigned)x_s[(r + W - 1 - i) * AP + c] << 16), acc);
                 conv_acc[q4] += acc;
             }
         }
