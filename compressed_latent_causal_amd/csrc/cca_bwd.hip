@@ -30,6 +30,8 @@
 //    workgroup's running sums of dM and of the tap gradient, which it writes
 //    once per chunk into the workspace;
 //  * cca_bwd_reduce_kernel: the per-chunk partial sums added up per weight.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -121,14 +123,15 @@ __device__ inline bf16x8_t col8(const uint16_t* tile, int ld, int r0, int c0, in
 // stored in LDS as bf16 high and low parts: ds = M^T a (a split, M exact),
 // read row-wise; dM += a s^T over the block's 32 tokens (hi hi + hi lo +
 // lo hi), with a and s read down their token columns by transpose reads.
-template <int D>
-__global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
+template <int D, int W>
+__global__ __launch_bounds__(CB_THREADS, D == 64 ? 3 : 1) void cca_bwd_head_kernel(
     uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, float* __restrict__ part_mix,
     float* __restrict__ part_conv, const float* __restrict__ dm, const float* __restrict__ tab,
     const uint16_t* __restrict__ gq, const uint16_t* __restrict__ gk, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ conv_q,
     const uint16_t* __restrict__ conv_k, const uint16_t* __restrict__ mix_q,
-    const uint16_t* __restrict__ mix_k, int B, int Hq, int Hkv, int S, int W, int rope) {
+    const uint16_t* __restrict__ mix_k, int B, int Hq, int Hkv, int S, int rope) {
+    static_assert(W >= 1 && W <= CB_MAXW, "convolution width");
     constexpr int NT = D / 16;      // 16-wide tiles of a D-long dimension
     constexpr int KS = D / 32;      // 32-deep k-steps over D
     constexpr int RM = 48;          // staged gradient rows, padded to 3 tiles of 16
@@ -180,12 +183,32 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
     for (int e = tid; e < W * D; e += CB_THREADS)
         w_s[e / D][e % D] = bf16_at(isq ? conv_q : conv_k, (size_t)h * W * D + e);
 
-    // running sums of the weight gradients: the wave's dM tiles, and thread
-    // tid's taps e = tid + 256 q4 (W D <= 1024)
+    // The convolution over tokens (s, formed again) and the tap gradient:
+    // thread tid takes channel cc and the TPG consecutive tokens r0 .. of its
+    // group, with the latent rows they reach held in registers (a sliding
+    // window), so each staged value is read once per block.  Tap i meets the
+    // row W - 1 - i after the token's own first reach; in the window that is
+    // offset j = W - 1 - i, and the taps are kept in that order (wj[j] = w_i).
+    constexpr int NG = CB_THREADS / D;        // token groups: 4 at D = 64, 2 at D = 128
+    constexpr int TPG = CB_T / NG;            // tokens per group
+    constexpr int XW = TPG + W - 1;           // window rows
+    const int cc = tid % D, r0 = (tid / D) * TPG;
+
+    // running sums of the weight gradients: the wave's dM tiles, and the
+    // thread's tap sums (window offset j) over its groups' tokens
     f32x4_t dmacc[DMW];
 #pragma unroll
     for (int u = 0; u < DMW; ++u) dmacc[u] = f32x4_t{0, 0, 0, 0};
-    float conv_acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float conv_acc[W];
+#pragma unroll
+    for (int jj = 0; jj < W; ++jj) conv_acc[jj] = 0.f;
+    // window rows r0 .. r0 + TPG + W - 2 of the staged latent rows (x_s row m
+    // holds token t0 - W + 1 + m); rows past the staged ones are only reached
+    // by tokens past the block
+    auto load_window = [&](float (&xv)[XW]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < XW; ++m) xv[m] = __uint_as_float((unsigned)x_s[(r0 + m) * AP + cc] << 16);
+    };
 
     const int c_begin = chunk * CB_CHUNK, c_end = min(S, c_begin + CB_CHUNK);
     // A block's global loads (gradient rows, 8 channels per item; latent rows;
@@ -233,7 +256,6 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
     for (int t0 = c_begin; t0 < c_end; t0 += CB_T) {
         const int T = min(CB_T, c_end - t0);    // block tokens
         const int RA = min(T + W - 1, S - t0);  // gradient rows (tokens t0 .. t0 + RA - 1)
-        const int RX = T + W - 1;               // latent rows (tokens t0 - W + 1 ..)
         __syncthreads();  // the previous block's reads are done
 #pragma unroll
         for (int u = 0; u < AI; ++u) {
@@ -259,10 +281,9 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
 #pragma unroll
         for (int u = 0; u < XI; ++u) {
             const int e = tid + u * CB_THREADS, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            if (r < RX) {
-                const u32x4_t v = xw[u];
-                *(u32x4_t*)(x_s + r * AP + c0) = v;
-            }
+            // every staged row is written, zeros past the T + W - 1 the
+            // block has (the windows of tokens past the block reach them)
+            if (r < CB_R) *(u32x4_t*)(x_s + r * AP + c0) = xw[u];
         }
         f32x4_t cur_lo[DI], cur_hi[DI];  // this block's mean gradient
 #pragma unroll
@@ -272,23 +293,24 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
         }
         if (t0 + CB_T < c_end) load_block(t0 + CB_T);
         __syncthreads();
-        // s of the block (the forward's convolution output) as bf16 parts, two
-        // channels per item
-        for (int e = tid; e < CB_T * (D / 2); e += CB_THREADS) {
-            const int r = e / (D / 2), c = 2 * (e % (D / 2));
-            float s0 = 0.f, s1 = 0.f;
-            if (r < T)
-                for (int i = 0; i < W; ++i) {
-                    const unsigned xv = *(const unsigned*)(x_s + (r + W - 1 - i) * AP + c);
-                    const float2 wv = *(const float2*)&w_s[i][c];
-                    s0 = fmaf(wv.x, bf16_lo(xv), s0);
-                    s1 = fmaf(wv.y, bf16_hi(xv), s1);
-                }
-            unsigned h0, l0, h1, l1;
-            split1(s0, h0, l0);
-            split1(s1, h1, l1);
-            *(unsigned*)(sh_s + r * AP + c) = h0 | (h1 << 16);
-            *(unsigned*)(sl_s + r * AP + c) = l0 | (l1 << 16);
+        // s of the block (the forward's convolution output) as bf16 parts,
+        // zero past the block's tokens
+        {
+            float xv[XW], wj[W];
+            load_window(xv);
+#pragma unroll
+            for (int jj = 0; jj < W; ++jj) wj[jj] = w_s[W - 1 - jj][cc];
+#pragma unroll
+            for (int kq = 0; kq < TPG; ++kq) {
+                float sv = 0.f;
+#pragma unroll
+                for (int jj = W - 1; jj >= 0; --jj) sv = fmaf(wj[jj], xv[kq + jj], sv);  // taps i = 0 .. W - 1
+                if (r0 + kq >= T) sv = 0.f;
+                unsigned hs, ls;
+                split1(sv, hs, ls);
+                sh_s[(r0 + kq) * AP + cc] = (uint16_t)hs;
+                sl_s[(r0 + kq) * AP + cc] = (uint16_t)ls;
+            }
         }
         // ds = M^T a: tile (mt, nt) gives rows 16 mt + 4 lg + i, column 16 nt + lr
         for (int tt = w; tt < DSN; tt += 4) {
@@ -336,17 +358,21 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
                 }
             }
         }
-        // tap gradient: dw_i[c] += sum over the block of ds[t] x[t - i]
+        // tap gradient: dw_i[c] += sum over the block's tokens of ds[t] x[t - i]
+        {
+            float xv[XW];
+            load_window(xv);
+            float tacc[W];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int e = tid + q4 * CB_THREADS;
-            if (e < W * D) {
-                const int i = e / D, c = e % D;
-                float acc = 0.f;
-                for (int r = 0; r < T; ++r)
-                    acc = fmaf(ds_s[r][c], __uint_as_float((unsigned)x_s[(r + W - 1 - i) * AP + c] << 16), acc);
-                conv_acc[q4] += acc;
+            for (int jj = 0; jj < W; ++jj) tacc[jj] = 0.f;
+#pragma unroll
+            for (int kq = 0; kq < TPG; ++kq) {
+                const float d = r0 + kq < T ? ds_s[r0 + kq][cc] : 0.f;
+#pragma unroll
+                for (int jj = 0; jj < W; ++jj) tacc[jj] = fmaf(d, xv[kq + jj], tacc[jj]);
             }
+#pragma unroll
+            for (int jj = 0; jj < W; ++jj) conv_acc[jj] += tacc[jj];
         }
         // dM += a s^T over the block: tile (mt, nt) of (c, c'), k = the 32 tokens
 #pragma unroll
@@ -373,11 +399,20 @@ __global__ __launch_bounds__(CB_THREADS) void cca_bwd_head_kernel(
         }
     }
     {
-        float* const pc = part_conv + pidx * (size_t)W * D;
+        // the token groups' tap sums added in group order through LDS (the
+        // ds rows are free after the last block): row NG jj + group
+        static_assert(NG * CB_MAXW <= RM, "tap-sum rows");
+        __syncthreads();
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int e = tid + q4 * CB_THREADS;
-            if (e < W * D) pc[e] = conv_acc[q4];
+        for (int jj = 0; jj < W; ++jj) ds_s[NG * jj + tid / D][cc] = conv_acc[jj];
+        __syncthreads();
+        float* const pc = part_conv + pidx * (size_t)W * D;
+        for (int e = tid; e < W * D; e += CB_THREADS) {
+            const int i = e / D, c = e % D, jj = W - 1 - i;
+            float sum = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) sum += ds_s[NG * jj + gg][c];
+            pc[e] = sum;
         }
     }
 }
@@ -450,12 +485,26 @@ hipError_t launch_cca_bwd_d(void* dq, void* dk, void* dv, float* dconv_q, float*
         hipLaunchKernelGGL(cca_bwd_mean_kernel<D>, dim3((unsigned)((items + CB_THREADS - 1) / CB_THREADS)),
                            dim3(CB_THREADS), 0, st, dm, tab, (uint16_t*)dv, (const uint16_t*)gq,
                            (const uint16_t*)gk, (const uint16_t*)gv, B, Hq, Hkv, S, pos_offset, rope, fr);
-        hipLaunchKernelGGL(cca_bwd_head_kernel<D>, dim3((unsigned)((long long)B * (Hq + Hkv) * nchunk)),
-                           dim3(CB_THREADS), 0, st, (uint16_t*)dq, (uint16_t*)dk, part_mix, part_conv,
-                           (const float*)dm, (const float*)tab, (const uint16_t*)gq,
-                           (const uint16_t*)gk, (const uint16_t*)q, (const uint16_t*)k,
-                           (const uint16_t*)conv_q, (const uint16_t*)conv_k,
-                           (const uint16_t*)mix_q, (const uint16_t*)mix_k, B, Hq, Hkv, S, W, rope);
+        auto head = [&](auto w_c) {
+            hipLaunchKernelGGL((cca_bwd_head_kernel<D, decltype(w_c)::value>),
+                               dim3((unsigned)((long long)B * (Hq + Hkv) * nchunk)), dim3(CB_THREADS), 0, st,
+                               (uint16_t*)dq, (uint16_t*)dk, part_mix, part_conv, (const float*)dm,
+                               (const float*)tab, (const uint16_t*)gq, (const uint16_t*)gk,
+                               (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)conv_q,
+                               (const uint16_t*)conv_k, (const uint16_t*)mix_q, (const uint16_t*)mix_k, B,
+                               Hq, Hkv, S, rope);
+        };
+        static_assert(CB_MAXW == 8, "one instance per width");
+        switch (W) {  // the width is checked (1 .. CB_MAXW) before the launch
+            case 1: head(std::integral_constant<int, 1>{}); break;
+            case 2: head(std::integral_constant<int, 2>{}); break;
+            case 3: head(std::integral_constant<int, 3>{}); break;
+            case 4: head(std::integral_constant<int, 4>{}); break;
+            case 5: head(std::integral_constant<int, 5>{}); break;
+            case 6: head(std::integral_constant<int, 6>{}); break;
+            case 7: head(std::integral_constant<int, 7>{}); break;
+            default: head(std::integral_constant<int, 8>{}); break;
+        }
     }
     {
         const long long items = (long long)(Hq + Hkv) * (D * D + W * D);
