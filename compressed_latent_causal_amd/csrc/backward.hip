@@ -36,7 +36,6 @@
 // S and dP are formed in both the dK/dV and the dQ kernel (seven products per
 // score tile instead of five): the price of writing every gradient once
 // without atomics or an fp32 dQ buffer.
-#include <atomic>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -599,21 +598,6 @@ int pow2_divisor(int g, int cap) {
 #ifndef BW_NW
 #define BW_NW 4
 #endif
-
-// Compute units of the current device (cached per device).
-int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    const int slot = dev & 63;
-    int n = cache[slot].load(std::memory_order_relaxed);
-    if (n < 1) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-            n = 256;
-        cache[slot].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
 
 template <int D, int NK>
 int dkdv_blocks_per_cu() {

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace attn {
 
 // ---------------------------------------------------------------- types
@@ -170,6 +172,21 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __attribute__((always_inline)) inline void dma16(__amdgpu_buffer_rsrc_t rs, char* lds,
                                                             int voff, int soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+
+// Compute units of the current device (cached per device; 256 if the query
+// fails).  Launch planning sizes grids and splits from it.
+inline int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 }  // namespace attn

@@ -54,7 +54,6 @@
 // the keys before it; the split counts only the sub-tiles a query sees.  The
 // contiguous instantiation compiles all of this out.
 #include <algorithm>
-#include <atomic>
 #include <chrono>
 
 #include "../../include/attn.h"
@@ -738,20 +737,6 @@ __global__ __launch_bounds__(DC_NW * 64, 2) void decode_split_kernel(
         wv[1] = pack_bf16x2(acc[it][2] * inv, acc[it][3] * inv);
         *(u32x2_t*)(o + (size_t)(b * Hq + h0 + hd) * D + d) = wv;
     }
-}
-
-// Compute units of the current device (cached per device).
-int device_cus() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-            n = 256;
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
 }
 
 // Workgroup budget of a launch over `groups` (sequence, KV head, head slice)
