@@ -364,6 +364,71 @@ def test_cca_mix_backward_full_size():
     _check_backward(w, wl.CCA_CONV_WIDTH, w.theta, 3)
 
 
+E2E_TRAIN_CASES = [  # B, Hq, Hkv, S, D, width, theta
+    (1, 8, 2, 200, 64, 4, 1e4),
+    (2, 4, 1, 130, 128, 3, 5e5),   # MQA at D = 128
+]
+
+
+@pytest.mark.parametrize("case", E2E_TRAIN_CASES)
+def test_ccgqa_training_step_end_to_end(case):
+    """One training step of a CCGQA attention block through the C ABI: the CCA
+    pass, the prefill with its log-normaliser, the prefill backward on a loss
+    gradient dout, then the CCA backward on the gradients it returns; against
+    the oracle's chain (its pass rounded to bf16, its prefill backward rounded
+    to bf16, then its CCA backward).  The CCA backward is linear in its
+    incoming gradients g, so the two chains differ by L(e) plus the CCA
+    backward's own error, where e = (GPU g) - (oracle g, rounded) is measured
+    here (and held to the prefill backward's mean bar) and |L|(|e|) is the
+    oracle's backward fed absolute values (gradient channel pairs summed, as
+    the rotation mixes them).  The CCA backward's own error is that of
+    _check_backward: 2^-16 of the sum of absolute terms plus the final bf16
+    rounding (half an ulp, at most 2^-8 of the value) for dq~ and dk~, none for
+    dv~, 2^-13 of the sum of absolute terms for the weight gradients."""
+    B, Hq, Hkv, S, D, width, theta = case
+    w = wl.custom("prefill", "bf16", B, Hq, Hkv, D, S, theta=theta)
+    q, k, v, cq, ck, mq, mk = wl.make_cca(w, seed=31, width=width)
+    dout = wl.make_cca_grads(w, seed=32)[0]
+    say(f"ccgqa training step {case}")
+    qd, kd, vd, cqd, ckd, mqd, mkd, gd = (t.to(DEV) for t in (q, k, v, cq, ck, mq, mk, dout))
+    qo, ko, vo = attn.cca_mix(qd, kd, vd, cqd, ckd, mqd, mkd, rope_theta=theta)
+    o, lse = attn.prefill_lse(qo, ko, vo, scale=w.scale)
+    gq, gk, gv = attn.prefill_backward(qo, ko, vo, o, gd, lse, scale=w.scale)
+    (dq, dk, dv), wg = attn.cca_mix_backward(gq, gk, gv, qd, kd, cqd, ckd, mqd, mkd, rope_theta=theta)
+    torch.cuda.synchronize()
+
+    lat = [bits(t) for t in (q, k, cq, ck, mq, mk)]
+    rq, rk, rv = oracle.cca_mix(bits(q), bits(k), bits(v), *lat[2:], theta=theta)
+    og = oracle.prefill_backward(*(oracle.round_bf16(x) for x in (rq, rk, rv)), bits(dout), scale=w.scale)
+    og = [oracle.round_bf16(x) for x in og]
+    ref = oracle.cca_mix_backward(*og, *lat, theta=theta)
+
+    gg = [bits(t) for t in (gq, gk, gv)]
+    err_in = [oracle.widen(a) - oracle.widen(b) for a, b in zip(gg, og)]
+    for e, r, name in zip(err_in, og, ["g_q", "g_k", "g_v"]):
+        rms = float(np.sqrt(np.mean(oracle.widen(r) ** 2)))
+        say(f"incoming {name}: mean error {np.abs(e).mean() / rms:.2e} of its rms")
+        assert np.abs(e).mean() <= 2.0 ** -7 * rms, name
+    absw = [np.abs(oracle.widen(x)) for x in lat]
+    prop = oracle.cca_mix_backward(_pair_abs(err_in[0]), _pair_abs(err_in[1]), np.abs(err_in[2]), *absw)
+    own = oracle.cca_mix_backward(_pair_abs(gg[0]), _pair_abs(gg[1]), np.abs(oracle.widen(gg[2])), *absw)
+    gots = [oracle.widen(bits(t)) for t in (dq, dk, dv)] + [t.cpu().double().numpy() for t in wg]
+    names = ["dq~", "dk~", "dv~", "dconv_q", "dconv_k", "dmix_q", "dmix_k"]
+    for i, (got, r, pr, b, name) in enumerate(zip(gots, ref, prop, own, names)):
+        if i < 2:
+            own_err = 2.0 ** -16 * b + 2.0 ** -8 * np.abs(got)
+        elif i == 2:
+            own_err = 0.0
+        else:
+            own_err = 2.0 ** -13 * b
+        bound = (1 + 2.0 ** -10) * pr + own_err
+        err = np.abs(got - r)
+        rms = float(np.sqrt(np.mean(r ** 2)))
+        say(f"{name}: worst error {float((err / (bound + 1e-300)).max()):.3f} of its bound, "
+            f"mean error {err.mean() / rms:.2e} of its rms")
+        assert np.isfinite(got).all() and (err <= bound).all(), name
+
+
 def test_cca_mix_backward_without_tokens_zeroes_the_weight_gradients():
     w = wl.custom("prefill", "bf16", 1, 8, 2, 64, 16)
     q, k, v, cq, ck, mq, mk = (t.to(DEV) for t in wl.make_cca(w, seed=1))
