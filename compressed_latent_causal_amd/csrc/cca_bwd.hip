@@ -22,13 +22,16 @@
 //    of the group's query heads and key head summed into dm (fp32, in the
 //    workspace), the value shift's gradient, and the rotation's (cos, sin)
 //    per (sequence, token, channel pair) into the workspace for the next pass;
-//  * cca_bwd_head_kernel: one workgroup per (sequence, head, chunk of 256
-//    tokens), walking the chunk in blocks of 32 tokens.  Per block the
+//  * cca_bwd_head_kernel<D, W>: one workgroup per (sequence, head, chunk of
+//    256 tokens), walking the chunk in blocks of 32 tokens.  Per block the
 //    rotated-back gradient rows (the block and the W - 1 tokens after it) and
-//    the latent rows (the block and the W - 1 before it) are staged in LDS,
-//    ds = M^T a is formed for every staged gradient row, then dx, s, and the
-//    workgroup's running sums of dM and of the tap gradient, which it writes
-//    once per chunk into the workspace;
+//    the latent rows (the block and the W - 1 before it) are staged in LDS;
+//    s is formed again, ds = M^T a for every staged gradient row, then dx,
+//    and the workgroup's running sums of dM and of the tap gradient, which it
+//    writes once per chunk into the workspace.  s and the tap gradient go
+//    per channel over a run of consecutive tokens, the latent rows they reach
+//    held in registers as a sliding window (W, the tap count, is a template
+//    parameter so the window has fixed indices);
 //  * cca_bwd_reduce_kernel: the per-chunk partial sums added up per weight.
 #include <type_traits>
 
