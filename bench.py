@@ -401,6 +401,36 @@ def bench_cca_step(w, steps, warmup):
     torch.cuda.synchronize()
     bwd_ms = sum(a.elapsed_time(b) for a, b in bevs) / steps
     bwd_gbs = cca_backward_bytes(w) / (bwd_ms * 1e-3) / 1e9
+
+    # a whole training step of the attention block: the pass and the prefill
+    # with its log-normaliser, then the prefill backward on a loss gradient
+    # (N(0, 1), like the pass's output gradients above) and the pass's
+    # backward on the gradients it returns
+    dout = grads[0]
+    lse = torch.empty(w.B, w.Hq, w.S, dtype=torch.float32, device="cuda")
+    gqo, gko, gvo = torch.empty_like(qo), torch.empty_like(ko), torch.empty_like(vo)
+    pws = torch.empty(max(1, attn.prefill_backward_workspace_size(w.B, w.Hq, w.Hkv, w.S, w.D)),
+                      dtype=torch.uint8, device="cuda")
+
+    def tstep():
+        attn.cca_mix(*ins, rope_theta=w.theta, q_out=qo, k_out=ko, v_out=vo)
+        attn.prefill_lse(qo, ko, vo, w.scale, out=o, lse=lse)
+        attn.prefill_backward(qo, ko, vo, o, dout, lse, w.scale, dq=gqo, dk=gko, dv=gvo, workspace=pws)
+        attn.cca_mix_backward(gqo, gko, gvo, ins[0], ins[1], *ins[3:], rope_theta=w.theta, workspace=bws)
+
+    for _ in range(warmup + 2):
+        tstep()
+    torch.cuda.synchronize()
+    tevs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(steps)]
+    for i in range(steps):
+        tevs[i][0].record(stream)
+        tstep()
+        tevs[i][1].record(stream)
+    torch.cuda.synchronize()
+    train_ms = sum(a.elapsed_time(b) for a, b in tevs) / steps
+    # products of the step: QK^T and PV forward, five in the backward (S, dP,
+    # dV, dK, dQ), each 2 D flop per unmasked pair
+    train_flops = prefill_flops(w.B, w.Hq, w.S, w.D) * 7 / 2
     return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
             "head_dim": w.D, "seq_len": w.S, "rope_theta": w.theta,
             "conv_width": wl.CCA_CONV_WIDTH,
@@ -416,6 +446,10 @@ def bench_cca_step(w, steps, warmup):
             "cca_backward_GB_per_s": round(bwd_gbs, 1),
             "cca_backward": "attn_cca_mix_backward: input gradients (bf16) and weight gradients "
                             "(fp32, summed over the batch and tokens) of the pass, three kernels",
+            "train_step_ms_mean": round(train_ms, 5),
+            "train_step_TFLOP_per_s": round(train_flops / (train_ms * 1e-3) / 1e12, 1),
+            "train_step": "attn_cca_mix, attn_prefill_lse, attn_prefill_backward, attn_cca_mix_backward "
+                          "(TFLOP/s of the 2 forward and 5 backward attention products)",
             "cca_decode_step_us": round(dec_us, 2),
             "cca_decode_step": f"attn_cca_mix_decode: one new token for each of {Bd} sequences "
                                f"(token indices 1024..8192), 100 steps replayed from a HIP graph"}
@@ -576,7 +610,8 @@ def main():
     log(f"ccgqa with the CCA pass: mix {ca['cca_mix_ms_mean']:.4f} ms ({ca['cca_mix_GB_per_s']:.0f} GB/s), "
         f"prefill {ca['prefill_ms_mean']:.4f} ms, step {ca['ms_per_step']:.4f} ms; "
         f"decode step {ca['cca_decode_step_us']:.1f} us; backward {ca['cca_backward_ms_mean']:.4f} ms "
-        f"({ca['cca_backward_GB_per_s']:.0f} GB/s)")
+        f"({ca['cca_backward_GB_per_s']:.0f} GB/s); training step {ca['train_step_ms_mean']:.4f} ms "
+        f"({ca['train_step_TFLOP_per_s']:.0f} TFLOP/s)")
     result["ccgqa_cca_step"] = ca
     if not args.no_decode:
         dec = {}
