@@ -348,6 +348,8 @@ BWD_CASES = [  # B, Hq, Hkv, S, D, width, theta, pos_offset
     (1, 8, 2, 1, 64, 4, 1e4, None),         # one token
     (1, 10, 2, 300, 64, 3, 1e4, None),      # two chunks, the second ragged
     (1, 2, 1, 600, 128, 5, 5e5, [131000]),  # three chunks at D = 128, large positions
+    (1, 8, 2, 4096, 128, 4, 5e5, None),     # sixteen chunks at D = 128
+    (1, 4, 1, 1000, 128, 8, 1e4, [7]),      # the widest convolution at D = 128, ragged last chunk
 ]
 
 
