@@ -14,7 +14,7 @@ GB/s of the two decode workloads (one decode step over several layers' caches
 back to back, caches evicted before each timed step), the `backward` object the
 training backward pass of both prefill workloads, and `cpu_baseline` times
 the fp64 CPU oracle on a bounded sample of the same prefill workload (and on
-the gqa_decode batch).  `prefill_ccgqa` times the compressed-latent prefill
+the gqa_decode batch, and the CCA pass and its backward on ccgqa_prefill).  `prefill_ccgqa` times the compressed-latent prefill
 (batch 2, 8 query heads, 2 KV heads, head dim 64, 16384 tokens) the same way
 as the headline step, and `ccgqa_cca_step` the same layer with the CCA
 pre-attention pass (convolutions, QK-mean, RoPE, value shift) before it.  Prints one JSON line on stdout.
@@ -484,6 +484,26 @@ def cpu_baseline_decode(w):
                       f"{el:.2f} s wall"}
 
 
+def cpu_baseline_cca(w):
+    """The oracle's CCA pre-attention pass and its backward (fp64 C, OpenMP
+    over heads) on the whole workload, in GB/s of the same algorithmic bytes
+    the GPU lines count."""
+    import oracle
+    from compressed_latent_causal_amd import workloads as wl
+
+    ins = [wl.to_numpy_bits(t) for t in wl.make_cca(w, seed=0)]
+    grads = [wl.to_numpy_bits(t) for t in wl.make_cca_grads(w, seed=1)]
+    t0 = time.perf_counter()
+    oracle.cca_mix(*ins, theta=w.theta)
+    t1 = time.perf_counter()
+    oracle.cca_mix_backward(*grads, ins[0], ins[1], *ins[3:], theta=w.theta)
+    t2 = time.perf_counter()
+    return {"pass": {"value": cca_bytes(w) / (t1 - t0) / 1e9, "unit": "GB/s"},
+            "backward": {"value": cca_backward_bytes(w) / (t2 - t1) / 1e9, "unit": "GB/s"},
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the whole {w.name} workload, {t1 - t0:.2f} s and {t2 - t1:.2f} s wall"}
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The oracle (fp64 C, OpenMP) on a random sample of output rows of the
     same prefill workload: RoPE of all keys and of the sampled queries, then
@@ -631,6 +651,7 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
         if not args.no_decode:
             result["cpu_baseline"]["decode"] = cpu_baseline_decode(wl.WORKLOADS["gqa_decode"])
+        result["cpu_baseline"]["cca"] = cpu_baseline_cca(wl.WORKLOADS["ccgqa_prefill"])
         log(f"cpu baseline: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
 
